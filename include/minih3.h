@@ -1,0 +1,195 @@
+/*
+ * minih3.h: C ABI of libminih3.so, the MI355X (gfx950) forward pass of a
+ * MiniMax-H3-style diffusion-transformer block over one packed 1-D sequence.
+ *
+ * Source of what is computed: the diffusers documentation page
+ * "MiniMaxH3Transformer3DModel" (class description, Parameters, `forward`).
+ * One block stack runs over one packed sequence of text, conditioning,
+ * audio and target-video rows; each row carries a modality tag that selects
+ * its AdaLN modulation, a timestep index and a (t, h, w) rotary position;
+ * padding rows (tag -1) form their own attention document.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *    owned by the caller. The library never allocates or frees device
+ *    memory; scratch space comes from a caller-provided workspace.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously on it; nothing synchronises unless a
+ *    flag below says so.
+ *  - Tensors are dense, row-major, with the shapes given per argument.
+ *    "act" tensors have the dtype `minih3_config.act_dtype` (bfloat16 or
+ *    float32); bfloat16 values are stored as IEEE bf16 bit patterns.
+ *  - Every call returns an int status (minih3_status) and never aborts.
+ *    Argument errors are found on the host before anything is enqueued.
+ *    Layout errors are found only under MINIH3_VALIDATE, which costs one
+ *    stream synchronisation. Without it an invalid layout gives unspecified
+ *    numbers, but every index the kernels use is clamped into range, so no
+ *    access leaves its buffer.
+ */
+#ifndef MINIH3_H
+#define MINIH3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MINIH3_OK = 0,
+  MINIH3_E_ARG = -1,           /* null pointer, bad size or unsupported dims   */
+  MINIH3_E_WORKSPACE = -2,     /* workspace null or smaller than required      */
+  MINIH3_E_UNSUPPORTED = -3,   /* a dims combination the kernels do not cover  */
+  MINIH3_E_LAYOUT_TAG = -10,   /* a tag outside {-1, 0 .. num_tags-1}          */
+  MINIH3_E_LAYOUT_TVAL = -11,  /* timestep index outside [0, num_tvals) on a non-padding row */
+  MINIH3_E_LAYOUT_INDEX = -12, /* index out of range, a row addressed twice, or a row of another modality */
+  MINIH3_E_LAYOUT_PAD = -13,   /* index addresses a padding row, or a non-padding row is unaddressed */
+  MINIH3_E_NEEDS_MASK = -14,   /* padding rows present under MINIH3_ASSUME_PADLESS */
+  MINIH3_E_HIP = -20           /* a HIP runtime call failed                    */
+} minih3_status;
+
+typedef enum { MINIH3_BF16 = 0, MINIH3_F32 = 1 } minih3_dtype;
+
+enum {
+  /* Validate the layout (tags, timestep indices, index tensors) on the
+   * device and synchronise the stream to report the first error by the
+   * precedence TAG, TVAL, INDEX, PAD, NEEDS_MASK. */
+  MINIH3_VALIDATE = 1u,
+  /* The caller promises a padless sequence (no tag -1 row): attention
+   * treats all rows as one document. With MINIH3_VALIDATE a -1 row gives
+   * MINIH3_E_NEEDS_MASK; without it, -1 rows are attended as ordinary rows. */
+  MINIH3_ASSUME_PADLESS = 2u,
+  /* Time every kernel of minih3_block_forward with HIP events on `stream`;
+   * read the totals with minih3_profile_collect. */
+  MINIH3_PROFILE = 4u
+};
+
+/* Model dimensions (page "MiniMaxH3Transformer3DModel", Parameters). */
+typedef struct {
+  int32_t hidden;        /* residual width D (5376); multiple of 256            */
+  int32_t num_heads;     /* H (56)                                              */
+  int32_t head_dim;      /* hd; must be 128                                      */
+  int32_t ffn_dim;       /* F, inner width of each SwiGLU half (14336); multiple of 128 */
+  int32_t rope_freq_dim; /* rotary frequencies per axis (16); 6*rope_freq_dim <= head_dim */
+  float rope_theta;      /* rotary base (1e4)                                    */
+  float norm_eps;        /* eps of the two AdaLN LayerNorms (1e-5)               */
+  float qk_norm_eps;     /* eps of the per-head q/k RMSNorms (1e-5)              */
+  int32_t num_tags;      /* modality tags that own an AdaLN table (3)            */
+  int32_t num_tvals;     /* timestep values per tag in the AdaLN table           */
+  int32_t tag_text, tag_video, tag_audio; /* tag value carried by each index tensor's rows */
+  int32_t act_dtype;     /* minih3_dtype of activations and weight matrices      */
+} minih3_config;
+
+/* One packed layout, shared by every batch item (the batch axis is a pure
+ * replication axis; each item is its own sequence). Page `forward`:
+ * timestep_indices, token_tags, position_ids, video/audio/text_indices. */
+typedef struct {
+  int32_t batch;                    /* B >= 1                                   */
+  int32_t seq_len;                  /* S >= 1                                   */
+  const int32_t* token_tags;        /* [S] modality tag, -1 = padding row        */
+  const int32_t* timestep_indices;  /* [S] index into the AdaLN table's timestep axis; ignored on padding rows */
+  const int32_t* position_ids;      /* [S, 3] (t, h, w) rotary coordinates       */
+  const int32_t* video_indices; int32_t num_video; /* rows of conditioning + target video */
+  const int32_t* audio_indices; int32_t num_audio;
+  const int32_t* text_indices;  int32_t num_text;  /* index tensors may be NULL when their count is 0;
+                                                      they are read only under MINIH3_VALIDATE */
+} minih3_layout;
+
+/* Weights of one block. Matrices are act_dtype, row-major [out, in]. */
+typedef struct {
+  const void* w_qkv;        /* [3W, D], W = H*hd: rows [0,W) q, [W,2W) k, [2W,3W) v; head h = rows [h*hd, (h+1)*hd) of each */
+  const void* w_out;        /* [D, W]                                        */
+  const void* w_gate_up;    /* [2F, D]: rows [0,F) gate, [F,2F) up            */
+  const void* w_down;       /* [D, F]                                        */
+  const float* q_norm;      /* [hd] RMSNorm weight shared by all query heads  */
+  const float* k_norm;      /* [hd] RMSNorm weight shared by all key heads    */
+  const float* adaln_table; /* [num_tags, num_tvals, 6, D] fp32: shift1, scale1, gate1 (attention),
+                               shift2, scale2, gate2 (FFN); padding rows use zeros */
+} minih3_block_weights;
+
+/* Optional copies of intermediates of the FIRST block (tests). Every field
+ * may be NULL. Shapes (S_pad = S rounded up to a multiple of 64):
+ *   adaln1, adaln2, x_mid, attn_proj, ffn_out : [B, S, D] act
+ *   q_rot, k_rot : [B, H, S_pad, hd] act (post RMSNorm + RoPE)
+ *   v_t          : [B, H, hd, S_pad] act (values, transposed)
+ *   attn_o       : [B, S, W] act;  ffn_h : [B, S, F] act
+ *   table_row    : [S] int32 tag*num_tvals + tidx, -1 on padding rows
+ *   doc_id       : [S] int32 attention document (1 = padding row)
+ *   tile_flags   : [ceil(S/64)] int32 bit0 = tile holds a non-padding row, bit1 = a padding row
+ *   num_pad      : [1] int32 */
+typedef struct {
+  void *adaln1, *q_rot, *k_rot, *v_t, *attn_o, *attn_proj, *x_mid, *adaln2, *ffn_h, *ffn_out;
+  int32_t *table_row, *doc_id, *tile_flags, *num_pad;
+} minih3_taps;
+
+/* Bytes of workspace minih3_block_forward needs for (batch, seq_len). */
+int minih3_workspace_bytes(const minih3_config* cfg, int32_t batch, int32_t seq_len, size_t* bytes);
+
+/* Forward pass of `num_blocks` consecutive blocks (page: num_layers blocks
+ * in one stack) over x_in [B, S, D] act -> x_out [B, S, D] act. Per block:
+ * AdaLN (LN + (1+scale)/shift chosen by tag and timestep index), QKV
+ * projection, per-head q/k RMSNorm, 3-D RoPE, attention within documents
+ * (padding rows alone), output projection with gated residual, AdaLN,
+ * SwiGLU FFN with gated residual. Padding rows leave the block unchanged.
+ * x_out must not alias x_in or the workspace. */
+int minih3_block_forward(const minih3_config* cfg, const minih3_layout* layout,
+                         const minih3_block_weights* blocks, int32_t num_blocks,
+                         const void* x_in, void* x_out, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, minih3_taps* taps, void* stream);
+
+/* Bytes of workspace minih3_attention_packed needs for seq_len S. */
+int minih3_attention_workspace_bytes(int32_t seq_len, size_t* bytes);
+
+/* Attention over the packed sequence (page: full self-attention; padding
+ * rows kept in their own document by a boolean mask):
+ *   out[b, i, h*hd:(h+1)*hd] = sum_j softmax_j(scale * q_i . k_j) v_j,
+ * over j < S with doc(j) == doc(i), doc = (tag == -1); under
+ * MINIH3_ASSUME_PADLESS every row is in one document.
+ * q, k : [B, H, seq_stride, hd] act;  v_t : [B, H, hd, seq_stride] act;
+ * out  : [B, S, H*hd] act. seq_stride >= S and a multiple of 64; rows
+ * and columns in [S, seq_stride) are never used in the result but must be
+ * readable. softmax_scale <= 0 selects 1/sqrt(hd). Only token_tags (and
+ * batch, seq_len) of the layout are read. */
+int minih3_attention_packed(const minih3_config* cfg, const minih3_layout* layout,
+                            const void* q, const void* k, const void* v_t, int32_t seq_stride,
+                            void* out, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            uint32_t flags, void* stream);
+
+/* One AdaLN modulation: y = LN(x) * (1 + scale) + shift per row, with
+ * (shift, scale) = adaln_table[tag, tidx, 3*which + {0, 1}] and zeros on
+ * padding rows. which = 0 before attention, 1 before the FFN.
+ * x, y : [B, S, D] act (may alias). */
+int minih3_adaln_modulate(const minih3_config* cfg, const minih3_layout* layout, const void* x,
+                          const float* adaln_table, int32_t which, void* y, uint32_t flags, void* stream);
+
+/* Per-head RMSNorm of q and k (weights q_norm, k_norm) followed by the
+ * 3-D rotary embedding on 6*rope_freq_dim channels: axis a (t, h, w) owns
+ * channels [2*fd*a, 2*fd*(a+1)), pair j = channels (2j, 2j+1) in it turns
+ * by position[a] * rope_theta^(-j/fd); other channels pass through.
+ * qkv   : [B, S, 3W] act (the QKV projection output)
+ * q_out, k_out : [B, H, seq_stride, hd] act;  v_t_out : [B, H, hd, seq_stride] act
+ * Rows [S, seq_stride) of the outputs are written as zeros. */
+int minih3_qk_norm_rope(const minih3_config* cfg, const minih3_layout* layout, const void* qkv,
+                        const float* q_norm, const float* k_norm, void* q_out, void* k_out,
+                        void* v_t_out, int32_t seq_stride, void* stream);
+
+/* Plain projection c[M, N] = a[M, K] . w[N, K]^T in `dtype`, fp32
+ * accumulation. Constraints: N % 256 == 0, K % 64 == 0, M >= 1. */
+int minih3_linear(int32_t dtype, const void* a, const void* w, void* c, int32_t M, int32_t N, int32_t K,
+                  void* stream);
+
+/* Kernel timing under MINIH3_PROFILE. Synchronises the recorded events,
+ * writes for each kernel id k < n the summed milliseconds and the number of
+ * launches since the last collect, then resets. Returns the number of
+ * kernel ids. */
+int minih3_profile_collect(double* total_ms, int32_t* launches, int32_t n);
+const char* minih3_kernel_name(int32_t id);
+
+const char* minih3_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MINIH3_H */

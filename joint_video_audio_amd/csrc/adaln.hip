@@ -1,0 +1,151 @@
+// Per-row AdaLN modulation: y = LN(x) * (1 + scale) + shift, with the
+// modulation vectors selected by the row's modality tag and timestep index.
+// Page "MiniMaxH3Transformer3DModel": the per-row tag selects the AdaLN
+// modulation parameters (class description); norm_eps is the eps of the
+// pre-attention and pre-feed-forward norms (Parameters). The LayerNorm
+// carries no affine part of its own; padding rows get zero shift/scale.
+//
+// HBM-bound: one workgroup per row, the row held in registers between the
+// mean, variance and output passes, 16-byte coalesced loads and stores,
+// fp32 statistics.
+#include "common.h"
+#include "kernels.h"
+
+namespace minih3 {
+
+template <typename T> struct Vec;
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(r[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(p) = r;
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    floatx4 r = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = r[i];
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i];
+    *reinterpret_cast<floatx4*>(p) = r;
+  }
+};
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();  // red[] reuse across calls
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) s += red[w];
+  return s;
+}
+
+template <typename T, int NT, int MAXV>
+__global__ void __launch_bounds__(NT) k_adaln(const T* x, T* y,  // x and y may alias: a row is read whole first
+                                              const float* __restrict__ table, const int32_t* __restrict__ tags,
+                                              const int32_t* __restrict__ tidx, int S, int D, int which, float eps,
+                                              int num_tags, int num_tvals) {
+  constexpr int VN = Vec<T>::N;
+  __shared__ float red[NT / 64];
+  const long row = blockIdx.x;
+  const int s = (int)(row % S);
+  const int nv = D / VN;
+  const T* xr = x + row * D;
+  T* yr = y + row * D;
+
+  float v[MAXV][VN];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = threadIdx.x + i * NT;
+    if (c < nv) {
+      Vec<T>::load(xr + c * VN, v[i]);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) sum += v[i][e];
+    }
+  }
+  const float mean = block_sum<NT>(sum, red) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = threadIdx.x + i * NT;
+    if (c < nv) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        float d = v[i][e] - mean;
+        sq += d * d;
+      }
+    }
+  }
+  const float var = block_sum<NT>(sq, red) / (float)D;
+  const float rstd = rsqrtf(var + eps);
+
+  const int tr = table_row_of(tags[s], tidx[s], num_tags, num_tvals);
+  const float* shift = tr >= 0 ? table + ((long)tr * 6 + 3 * which + 0) * D : nullptr;
+  const float* scale = tr >= 0 ? table + ((long)tr * 6 + 3 * which + 1) * D : nullptr;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = threadIdx.x + i * NT;
+    if (c < nv) {
+      float o[VN];
+      if (tr >= 0) {
+#pragma unroll
+        for (int e = 0; e < VN; e += 4) {
+          floatx4 sh = *reinterpret_cast<const floatx4*>(shift + c * VN + e);
+          floatx4 sc = *reinterpret_cast<const floatx4*>(scale + c * VN + e);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[e + u] = (v[i][e + u] - mean) * rstd * (1.f + sc[u]) + sh[u];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) o[e] = (v[i][e] - mean) * rstd;
+      }
+      Vec<T>::store(yr + c * VN, o);
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_adaln(const T* x, T* y, const float* table, const int32_t* tags, const int32_t* tidx, int B, int S,
+                        int D, int which, float eps, int num_tags, int num_tvals, hipStream_t st) {
+  constexpr int NT = 256;
+  const int nv = D / Vec<T>::N;
+  dim3 grid((unsigned)((long)B * S));
+  if (nv <= NT * 1)
+    k_adaln<T, NT, 1><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else if (nv <= NT * 2)
+    k_adaln<T, NT, 2><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else if (nv <= NT * 3)
+    k_adaln<T, NT, 3><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else if (nv <= NT * 4)
+    k_adaln<T, NT, 4><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template hipError_t launch_adaln<bf16_t>(const bf16_t*, bf16_t*, const float*, const int32_t*, const int32_t*, int,
+                                         int, int, int, float, int, int, hipStream_t);
+template hipError_t launch_adaln<float>(const float*, float*, const float*, const int32_t*, const int32_t*, int, int,
+                                        int, int, float, int, int, hipStream_t);
+
+}  // namespace minih3

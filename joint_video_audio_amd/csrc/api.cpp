@@ -1,0 +1,479 @@
+// C ABI of libminih3: argument checks, workspace carving, the launch
+// sequence of one block and of a chain of blocks, kernel timing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/minih3.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace minih3;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Kernel ids reported by minih3_profile_collect.
+enum KernelId {
+  kKLayout = 0, kKTiles, kKAdaLN1, kKQKV, kKQKNormRope, kKAttention, kKOutProj, kKAdaLN2, kKGateUp, kKDown,
+  kKNumIds
+};
+const char* kKernelNames[kKNumIds] = {"layout_validate", "attention_tiles", "adaln_pre_attention",
+                                      "qkv_projection", "qk_norm_rope", "attention",
+                                      "out_projection_gated_residual", "adaln_pre_ffn", "gate_up_swiglu",
+                                      "down_projection_gated_residual"};
+
+struct Profiler {
+  std::mutex mu;
+  struct Rec { int id; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler g_prof;
+
+// Records HIP events around the launches of one kernel when enabled.
+struct Timed {
+  bool on;
+  int id;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(bool on_, int id_, hipStream_t st_) : on(on_), id(id_), st(st_) {
+    if (!on) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    a = g_prof.get();
+    b = g_prof.get();
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~Timed() {
+    if (!on || !a || !b) return;
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.recs.push_back({id, a, b});
+  }
+};
+
+int act_size(int dtype) { return dtype == MINIH3_BF16 ? 2 : 4; }
+
+int check_config(const minih3_config* c) {
+  if (!c) return MINIH3_E_ARG;
+  if (c->act_dtype != MINIH3_BF16 && c->act_dtype != MINIH3_F32) return MINIH3_E_ARG;
+  if (c->head_dim != 128) return MINIH3_E_UNSUPPORTED;
+  if (c->num_heads < 1 || c->hidden < 256 || c->hidden % 256 != 0) return MINIH3_E_UNSUPPORTED;
+  if (c->ffn_dim < 128 || c->ffn_dim % 128 != 0) return MINIH3_E_UNSUPPORTED;
+  if ((3L * c->num_heads * c->head_dim) % 256 != 0) return MINIH3_E_UNSUPPORTED;
+  const int vec = c->act_dtype == MINIH3_BF16 ? 8 : 4;
+  if (c->hidden / vec > 1024) return MINIH3_E_UNSUPPORTED;
+  if (c->rope_freq_dim < 0 || 6 * c->rope_freq_dim > c->head_dim) return MINIH3_E_UNSUPPORTED;
+  if (!(c->rope_theta > 0.f) || !(c->norm_eps >= 0.f) || !(c->qk_norm_eps >= 0.f)) return MINIH3_E_ARG;
+  if (c->num_tags < 1 || c->num_tvals < 1) return MINIH3_E_ARG;
+  return MINIH3_OK;
+}
+
+int check_layout(const minih3_layout* L, bool need_indices) {
+  if (!L) return MINIH3_E_ARG;
+  if (L->batch < 1 || L->seq_len < 1) return MINIH3_E_ARG;
+  if ((long)L->batch * L->seq_len > (1L << 30)) return MINIH3_E_UNSUPPORTED;
+  if (!L->token_tags || !L->timestep_indices || !L->position_ids) return MINIH3_E_ARG;
+  if (L->num_video < 0 || L->num_audio < 0 || L->num_text < 0) return MINIH3_E_ARG;
+  if (need_indices) {
+    if ((L->num_video && !L->video_indices) || (L->num_audio && !L->audio_indices) ||
+        (L->num_text && !L->text_indices))
+      return MINIH3_E_ARG;
+  }
+  return MINIH3_OK;
+}
+
+struct Workspace {
+  void *a, *qkvh, *qn, *kn, *vt, *o, *xmid, *xping;
+  uint64_t* masks;
+  int32_t *list_real, *list_pad, *meta, *counts, *npad;
+  uint32_t* err;
+  size_t total;
+};
+
+size_t tiles_bytes(int S, int32_t** list_real, int32_t** list_pad, int32_t** meta, uint64_t** masks, char* base) {
+  const size_t nt = (size_t)(S + 63) / 64;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off += align_up(n);
+    return base ? base + o : nullptr;
+  };
+  char* p;
+  p = take(16 * nt);
+  if (masks) *masks = (uint64_t*)p;
+  p = take(4 * nt);
+  if (list_real) *list_real = (int32_t*)p;
+  p = take(4 * nt);
+  if (list_pad) *list_pad = (int32_t*)p;
+  p = take(16);
+  if (meta) *meta = (int32_t*)p;
+  return off;
+}
+
+Workspace carve(const minih3_config* c, int B, int S, char* base) {
+  Workspace w{};
+  const size_t e = act_size(c->act_dtype);
+  const size_t D = c->hidden, H = c->num_heads, hd = c->head_dim, F = c->ffn_dim;
+  const size_t Wd = H * hd;
+  const size_t M = (size_t)B * S;
+  const size_t Sp = (size_t)(S + 63) / 64 * 64;
+  size_t off = 0;
+  auto take = [&](size_t n) -> char* {
+    size_t o = off;
+    off += align_up(n);
+    return base ? base + o : nullptr;
+  };
+  w.a = take(M * D * e);
+  w.qkvh = take(M * (3 * Wd > F ? 3 * Wd : F) * e);
+  w.qn = take((size_t)B * H * Sp * hd * e);
+  w.kn = take((size_t)B * H * Sp * hd * e);
+  w.vt = take((size_t)B * H * Sp * hd * e);
+  w.o = take(M * Wd * e);
+  w.xmid = take(M * D * e);
+  w.xping = take(M * D * e);
+  char* tb = take(tiles_bytes(S, nullptr, nullptr, nullptr, nullptr, nullptr));
+  if (base) tiles_bytes(S, &w.list_real, &w.list_pad, &w.meta, &w.masks, tb);
+  w.counts = (int32_t*)take(4 * (size_t)S);
+  w.npad = (int32_t*)take(4);
+  w.err = (uint32_t*)take(4);
+  w.total = off;
+  return w;
+}
+
+int status_from_err(uint32_t err) {
+  if (err & kErrTag) return MINIH3_E_LAYOUT_TAG;
+  if (err & kErrTval) return MINIH3_E_LAYOUT_TVAL;
+  if (err & kErrIndex) return MINIH3_E_LAYOUT_INDEX;
+  if (err & kErrPad) return MINIH3_E_LAYOUT_PAD;
+  if (err & kErrNeedsMask) return MINIH3_E_NEEDS_MASK;
+  return MINIH3_OK;
+}
+
+#define HIPCHECK(x)                               \
+  do {                                            \
+    if ((x) != hipSuccess) return MINIH3_E_HIP;   \
+  } while (0)
+
+template <typename T>
+int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks, int nb,
+               const T* x_in, T* x_out, Workspace& w, uint32_t flags, minih3_taps* taps, hipStream_t st) {
+  const int B = L->batch, S = L->seq_len;
+  const int D = c->hidden, H = c->num_heads, hd = c->head_dim, F = c->ffn_dim;
+  const int Wd = H * hd;
+  const int M = B * S;
+  const int Sp = (S + 63) / 64 * 64;
+  const bool prof = flags & MINIH3_PROFILE;
+  const int padless = (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0;
+  const size_t e = sizeof(T);
+
+  {
+    Timed tm(prof, kKTiles, st);
+    HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, w.masks, w.list_real, w.list_pad, w.meta, st));
+  }
+
+  T* a = (T*)w.a;
+  T* qkv = (T*)w.qkvh;
+  T* hbuf = (T*)w.qkvh;  // the SwiGLU output reuses the QKV buffer
+  T *qn = (T*)w.qn, *kn = (T*)w.kn, *vt = (T*)w.vt, *o = (T*)w.o, *xmid = (T*)w.xmid, *ping = (T*)w.xping;
+  const float scale = 1.f / sqrtf((float)hd);
+
+  const T* src = x_in;
+  for (int i = 0; i < nb; ++i) {
+    const minih3_block_weights& bw = blocks[i];
+    T* dst = ((nb - 1 - i) % 2 == 0) ? x_out : ping;
+    const bool tap = taps && i == 0;
+    EpiArgs ea{};
+    ea.table = bw.adaln_table;
+    ea.tags = L->token_tags;
+    ea.tidx = L->timestep_indices;
+    ea.S = S;
+    ea.num_tags = c->num_tags;
+    ea.num_tvals = c->num_tvals;
+    ea.ffn_dim = F;
+
+    {
+      Timed tm(prof, kKAdaLN1, st);
+      HIPCHECK(launch_adaln<T>(src, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 0, c->norm_eps,
+                               c->num_tags, c->num_tvals, st));
+    }
+    if (tap && taps->adaln1) HIPCHECK(hipMemcpyAsync(taps->adaln1, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
+    {
+      Timed tm(prof, kKQKV, st);
+      HIPCHECK(launch_gemm<T>(kEpiStore, a, (const T*)bw.w_qkv, qkv, M, 3 * Wd, D, ea, st));
+    }
+    {
+      Timed tm(prof, kKQKNormRope, st);
+      HIPCHECK(launch_qk_norm_rope<T>(qkv, bw.q_norm, bw.k_norm, L->position_ids, qn, kn, vt, B, S, H, Sp,
+                                      c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st));
+    }
+    if (tap) {
+      const size_t hb = (size_t)B * H * Sp * hd * e;
+      if (taps->q_rot) HIPCHECK(hipMemcpyAsync(taps->q_rot, qn, hb, hipMemcpyDeviceToDevice, st));
+      if (taps->k_rot) HIPCHECK(hipMemcpyAsync(taps->k_rot, kn, hb, hipMemcpyDeviceToDevice, st));
+      if (taps->v_t) HIPCHECK(hipMemcpyAsync(taps->v_t, vt, hb, hipMemcpyDeviceToDevice, st));
+    }
+    {
+      Timed tm(prof, kKAttention, st);
+      HIPCHECK(launch_attention<T>(qn, kn, vt, o, L->token_tags, w.masks, w.list_real, w.list_pad, w.meta, B, S, H,
+                                   Sp, scale, padless, st));
+    }
+    if (tap && taps->attn_o) HIPCHECK(hipMemcpyAsync(taps->attn_o, o, (size_t)M * Wd * e, hipMemcpyDeviceToDevice, st));
+    if (tap && taps->attn_proj) HIPCHECK(launch_gemm<T>(kEpiStore, o, (const T*)bw.w_out, (T*)taps->attn_proj, M, D, Wd, ea, st));
+    {
+      Timed tm(prof, kKOutProj, st);
+      ea.resid = src;
+      ea.gate_slot = 2;
+      HIPCHECK(launch_gemm<T>(kEpiGatedResid, o, (const T*)bw.w_out, xmid, M, D, Wd, ea, st));
+    }
+    if (tap && taps->x_mid) HIPCHECK(hipMemcpyAsync(taps->x_mid, xmid, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
+    {
+      Timed tm(prof, kKAdaLN2, st);
+      HIPCHECK(launch_adaln<T>(xmid, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 1, c->norm_eps,
+                               c->num_tags, c->num_tvals, st));
+    }
+    if (tap && taps->adaln2) HIPCHECK(hipMemcpyAsync(taps->adaln2, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
+    {
+      Timed tm(prof, kKGateUp, st);
+      HIPCHECK(launch_gemm<T>(kEpiSwiGLU, a, (const T*)bw.w_gate_up, hbuf, M, 2 * F, D, ea, st));
+    }
+    if (tap && taps->ffn_h) HIPCHECK(hipMemcpyAsync(taps->ffn_h, hbuf, (size_t)M * F * e, hipMemcpyDeviceToDevice, st));
+    if (tap && taps->ffn_out) HIPCHECK(launch_gemm<T>(kEpiStore, hbuf, (const T*)bw.w_down, (T*)taps->ffn_out, M, D, F, ea, st));
+    {
+      Timed tm(prof, kKDown, st);
+      ea.resid = xmid;
+      ea.gate_slot = 5;
+      HIPCHECK(launch_gemm<T>(kEpiGatedResid, hbuf, (const T*)bw.w_down, dst, M, D, F, ea, st));
+    }
+    src = dst;
+  }
+  return MINIH3_OK;
+}
+
+LayoutDev make_layout_dev(const minih3_config* c, const minih3_layout* L) {
+  LayoutDev d{};
+  d.S = L->seq_len;
+  d.tags = L->token_tags;
+  d.tidx = L->timestep_indices;
+  d.pos = L->position_ids;
+  d.idx[0] = L->video_indices;
+  d.idx[1] = L->audio_indices;
+  d.idx[2] = L->text_indices;
+  d.n_idx[0] = L->num_video;
+  d.n_idx[1] = L->num_audio;
+  d.n_idx[2] = L->num_text;
+  d.want_tag[0] = c->tag_video;
+  d.want_tag[1] = c->tag_audio;
+  d.want_tag[2] = c->tag_text;
+  d.num_tags = c->num_tags;
+  d.num_tvals = c->num_tvals;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* minih3_status_string(int s) {
+  switch (s) {
+    case MINIH3_OK: return "ok";
+    case MINIH3_E_ARG: return "invalid argument";
+    case MINIH3_E_WORKSPACE: return "workspace missing or too small";
+    case MINIH3_E_UNSUPPORTED: return "unsupported dimensions";
+    case MINIH3_E_LAYOUT_TAG: return "layout: tag outside {-1, 0 .. num_tags-1}";
+    case MINIH3_E_LAYOUT_TVAL: return "layout: timestep index outside [0, num_tvals) on a non-padding row";
+    case MINIH3_E_LAYOUT_INDEX: return "layout: index out of range, duplicated, or addressing another modality";
+    case MINIH3_E_LAYOUT_PAD: return "layout: index addresses a padding row, or a non-padding row is unaddressed";
+    case MINIH3_E_NEEDS_MASK: return "layout: padding rows need the masked attention path";
+    case MINIH3_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* minih3_kernel_name(int32_t id) { return (id >= 0 && id < kKNumIds) ? kKernelNames[id] : nullptr; }
+
+int minih3_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_len, size_t* bytes) {
+  int s = check_config(c);
+  if (s) return s;
+  if (!bytes || batch < 1 || seq_len < 1) return MINIH3_E_ARG;
+  *bytes = carve(c, batch, seq_len, nullptr).total;
+  return MINIH3_OK;
+}
+
+int minih3_attention_workspace_bytes(int32_t seq_len, size_t* bytes) {
+  if (!bytes || seq_len < 1) return MINIH3_E_ARG;
+  *bytes = tiles_bytes(seq_len, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return MINIH3_OK;
+}
+
+int minih3_block_forward(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks,
+                         int32_t num_blocks, const void* x_in, void* x_out, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, minih3_taps* taps, void* stream) {
+  int s = check_config(c);
+  if (s) return s;
+  const bool validate = flags & MINIH3_VALIDATE;
+  s = check_layout(L, validate);
+  if (s) return s;
+  if (num_blocks < 1 || !blocks || !x_in || !x_out || x_in == x_out) return MINIH3_E_ARG;
+  for (int i = 0; i < num_blocks; ++i) {
+    const minih3_block_weights& b = blocks[i];
+    if (!b.w_qkv || !b.w_out || !b.w_gate_up || !b.w_down || !b.q_norm || !b.k_norm || !b.adaln_table)
+      return MINIH3_E_ARG;
+  }
+  Workspace w = carve(c, L->batch, L->seq_len, (char*)workspace);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const bool prof = flags & MINIH3_PROFILE;
+
+  const bool int_taps = taps && (taps->table_row || taps->doc_id || taps->tile_flags || taps->num_pad);
+  if (validate || int_taps) {
+    LayoutDev ld = make_layout_dev(c, L);
+    if (!validate) ld.n_idx[0] = ld.n_idx[1] = ld.n_idx[2] = 0;
+    {
+      Timed tm(prof, kKLayout, st);
+      if (launch_layout_validate(ld, (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0, w.counts, w.err, w.npad,
+                                 taps ? taps->table_row : nullptr, taps ? taps->doc_id : nullptr,
+                                 taps ? taps->tile_flags : nullptr, st) != hipSuccess)
+        return MINIH3_E_HIP;
+    }
+    if (taps && taps->num_pad)
+      HIPCHECK(hipMemcpyAsync(taps->num_pad, w.npad, 4, hipMemcpyDeviceToDevice, st));
+    if (validate) {
+      uint32_t err = 0;
+      HIPCHECK(hipMemcpyAsync(&err, w.err, 4, hipMemcpyDeviceToHost, st));
+      HIPCHECK(hipStreamSynchronize(st));
+      s = status_from_err(err);
+      if (s) return s;
+    }
+  }
+  if (c->act_dtype == MINIH3_BF16)
+    return run_blocks<bf16_t>(c, L, blocks, num_blocks, (const bf16_t*)x_in, (bf16_t*)x_out, w, flags, taps, st);
+  return run_blocks<float>(c, L, blocks, num_blocks, (const float*)x_in, (float*)x_out, w, flags, taps, st);
+}
+
+int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, const void* q, const void* k,
+                            const void* v_t, int32_t seq_stride, void* out, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, uint32_t flags, void* stream) {
+  int s = check_config(c);
+  if (s) return s;
+  if (!L || L->batch < 1 || L->seq_len < 1 || !L->token_tags) return MINIH3_E_ARG;
+  if (!q || !k || !v_t || !out) return MINIH3_E_ARG;
+  const int S = L->seq_len;
+  if (seq_stride < S || seq_stride % 64 != 0) return MINIH3_E_ARG;
+  if ((long)L->batch * c->num_heads * seq_stride > (1L << 31) - 1) return MINIH3_E_UNSUPPORTED;
+  int32_t *list_real, *list_pad, *meta;
+  uint64_t* masks;
+  const size_t need = tiles_bytes(S, &list_real, &list_pad, &meta, &masks, (char*)workspace);
+  if (!workspace || workspace_bytes < need) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int padless = (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0;
+  if ((flags & MINIH3_VALIDATE) && padless) {
+    HIPCHECK(launch_attn_tiles(L->token_tags, S, 0, masks, list_real, list_pad, meta, st));
+    int32_t m[2] = {0, 0};
+    HIPCHECK(hipMemcpyAsync(m, meta, 8, hipMemcpyDeviceToHost, st));
+    HIPCHECK(hipStreamSynchronize(st));
+    if (m[1] > 0) return MINIH3_E_NEEDS_MASK;
+  }
+  HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, masks, list_real, list_pad, meta, st));
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)c->head_dim);
+  if (c->act_dtype == MINIH3_BF16)
+    HIPCHECK(launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v_t, (bf16_t*)out,
+                                      L->token_tags, masks, list_real, list_pad, meta, L->batch, S, c->num_heads,
+                                      seq_stride, scale, padless, st));
+  else
+    HIPCHECK(launch_attention<float>((const float*)q, (const float*)k, (const float*)v_t, (float*)out, L->token_tags,
+                                     masks, list_real, list_pad, meta, L->batch, S, c->num_heads, seq_stride, scale,
+                                     padless, st));
+  return MINIH3_OK;
+}
+
+int minih3_adaln_modulate(const minih3_config* c, const minih3_layout* L, const void* x, const float* table,
+                          int32_t which, void* y, uint32_t flags, void* stream) {
+  (void)flags;
+  int s = check_config(c);
+  if (s) return s;
+  if (!L || L->batch < 1 || L->seq_len < 1 || !L->token_tags || !L->timestep_indices) return MINIH3_E_ARG;
+  if (!x || !table || !y || (which != 0 && which != 1)) return MINIH3_E_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (c->act_dtype == MINIH3_BF16)
+    HIPCHECK(launch_adaln<bf16_t>((const bf16_t*)x, (bf16_t*)y, table, L->token_tags, L->timestep_indices, L->batch,
+                                  L->seq_len, c->hidden, which, c->norm_eps, c->num_tags, c->num_tvals, st));
+  else
+    HIPCHECK(launch_adaln<float>((const float*)x, (float*)y, table, L->token_tags, L->timestep_indices, L->batch,
+                                 L->seq_len, c->hidden, which, c->norm_eps, c->num_tags, c->num_tvals, st));
+  return MINIH3_OK;
+}
+
+int minih3_qk_norm_rope(const minih3_config* c, const minih3_layout* L, const void* qkv, const float* q_norm,
+                        const float* k_norm, void* q_out, void* k_out, void* v_t_out, int32_t seq_stride,
+                        void* stream) {
+  int s = check_config(c);
+  if (s) return s;
+  if (!L || L->batch < 1 || L->seq_len < 1 || !L->position_ids) return MINIH3_E_ARG;
+  if (!qkv || !q_norm || !k_norm || !q_out || !k_out || !v_t_out) return MINIH3_E_ARG;
+  if (seq_stride < L->seq_len || seq_stride % 64 != 0) return MINIH3_E_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (c->act_dtype == MINIH3_BF16)
+    HIPCHECK(launch_qk_norm_rope<bf16_t>((const bf16_t*)qkv, q_norm, k_norm, L->position_ids, (bf16_t*)q_out,
+                                         (bf16_t*)k_out, (bf16_t*)v_t_out, L->batch, L->seq_len, c->num_heads,
+                                         seq_stride, c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st));
+  else
+    HIPCHECK(launch_qk_norm_rope<float>((const float*)qkv, q_norm, k_norm, L->position_ids, (float*)q_out,
+                                        (float*)k_out, (float*)v_t_out, L->batch, L->seq_len, c->num_heads,
+                                        seq_stride, c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st));
+  return MINIH3_OK;
+}
+
+int minih3_linear(int32_t dtype, const void* a, const void* w, void* c, int32_t M, int32_t N, int32_t K,
+                  void* stream) {
+  if (!a || !w || !c || M < 1 || N < 1 || K < 1) return MINIH3_E_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  EpiArgs ea{};
+  if (dtype == MINIH3_BF16) {
+    if (N % 256 != 0 || K % 64 != 0) return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)a, (const bf16_t*)w, (bf16_t*)c, M, N, K, ea, st));
+  } else if (dtype == MINIH3_F32) {
+    if (N % 64 != 0 || K % 16 != 0) return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_gemm<float>(kEpiStore, (const float*)a, (const float*)w, (float*)c, M, N, K, ea, st));
+  } else {
+    return MINIH3_E_ARG;
+  }
+  return MINIH3_OK;
+}
+
+int minih3_profile_collect(double* total_ms, int32_t* launches, int32_t n) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int i = 0; i < n; ++i) {
+    if (total_ms) total_ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (auto& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess && r.id < n) {
+      if (total_ms) total_ms[r.id] += ms;
+      if (launches) launches[r.id] += 1;
+    }
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  return kKNumIds;
+}
+
+}  // extern "C"

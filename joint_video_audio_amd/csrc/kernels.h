@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 kernels (internal to libminih3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace minih3 {
+
+enum ErrBits : uint32_t {
+  kErrTag = 1u, kErrTval = 2u, kErrIndex = 4u, kErrPad = 8u, kErrNeedsMask = 16u
+};
+
+struct LayoutDev {
+  int S;
+  const int32_t* tags;
+  const int32_t* tidx;
+  const int32_t* pos;
+  const int32_t* idx[3];  // video, audio, text
+  int n_idx[3];
+  int want_tag[3];
+  int num_tags, num_tvals;
+};
+
+// ---- layout (integer) ----
+// Scratch: counts[S] int32, err[1] u32, npad[1] int32. Writes the optional
+// per-row / per-tile outputs when non-null.
+hipError_t launch_layout_validate(const LayoutDev& L, int assume_padless, int32_t* counts, uint32_t* err,
+                                  int32_t* npad, int32_t* table_row, int32_t* doc_id, int32_t* tile_flags,
+                                  hipStream_t st);
+// Attention tile lists: for each 64-row tile the masks of its non-padding
+// and padding rows (u64 each), and the compacted lists of tiles holding
+// any non-padding / padding row. meta[0] = #real tiles, meta[1] = #pad tiles.
+hipError_t launch_attn_tiles(const int32_t* tags, int S, int assume_padless, uint64_t* masks, int32_t* list_real,
+                             int32_t* list_pad, int32_t* meta, hipStream_t st);
+
+// ---- AdaLN ----
+template <typename T>
+hipError_t launch_adaln(const T* x, T* y, const float* table, const int32_t* tags, const int32_t* tidx, int B, int S,
+                        int D, int which, float eps, int num_tags, int num_tvals, hipStream_t st);
+
+// ---- q/k RMSNorm + RoPE + V transpose ----
+template <typename T>
+hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, const int32_t* pos, T* qo, T* ko,
+                               T* vto, int B, int S, int H, int stride, int fd, float theta, float eps,
+                               hipStream_t st);
+
+// ---- GEMM: C[M,N] = A[M,K] . W[N,K]^T with fused epilogues ----
+enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2 };
+struct EpiArgs {
+  const void* resid;     // [M, ldc] act (gated residual)
+  const float* table;    // adaln table
+  const int32_t* tags;   // [S]
+  const int32_t* tidx;   // [S]
+  int S;                 // rows per batch item (row -> layout row = m % S)
+  int num_tags, num_tvals;
+  int gate_slot;         // 2 (attention gate) or 5 (FFN gate)
+  int ffn_dim;           // SwiGLU: F (W rows [0,F) gate, [F,2F) up)
+};
+template <typename T>
+hipError_t launch_gemm(int epi, const T* A, const T* W, T* C, int M, int N, int K, const EpiArgs& ea,
+                       hipStream_t st);
+
+// ---- attention ----
+template <typename T>
+hipError_t launch_attention(const T* q, const T* k, const T* vt, T* out, const int32_t* tags, const uint64_t* masks,
+                            const int32_t* list_real, const int32_t* list_pad, const int32_t* meta, int B, int S,
+                            int H, int stride, float scale, int assume_padless, hipStream_t st);
+
+}  // namespace minih3

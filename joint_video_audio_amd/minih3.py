@@ -1,0 +1,330 @@
+"""ctypes binding of libminih3.so (declared in include/minih3.h).
+
+Argument marshalling only: every step of the block runs in the library's
+HIP kernels. torch supplies device memory (``tensor.data_ptr()``) and the
+stream (``torch.cuda.current_stream().cuda_stream``). Importing this module
+loads nothing; the first call loads the library and raises
+``Minih3Error`` if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libminih3.so")
+
+BF16, F32 = 0, 1
+VALIDATE, ASSUME_PADLESS, PROFILE = 1, 2, 4
+
+OK = 0
+E_ARG, E_WORKSPACE, E_UNSUPPORTED = -1, -2, -3
+E_LAYOUT_TAG, E_LAYOUT_TVAL, E_LAYOUT_INDEX, E_LAYOUT_PAD, E_NEEDS_MASK = -10, -11, -12, -13, -14
+E_HIP = -20
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ffn_dim", ctypes.c_int32), ("rope_freq_dim", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("norm_eps", ctypes.c_float), ("qk_norm_eps", ctypes.c_float), ("num_tags", ctypes.c_int32),
+                ("num_tvals", ctypes.c_int32), ("tag_text", ctypes.c_int32), ("tag_video", ctypes.c_int32),
+                ("tag_audio", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("token_tags", _P),
+                ("timestep_indices", _P), ("position_ids", _P), ("video_indices", _P), ("num_video", ctypes.c_int32),
+                ("audio_indices", _P), ("num_audio", ctypes.c_int32), ("text_indices", _P),
+                ("num_text", ctypes.c_int32)]
+
+
+class _BlockWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", _P), ("w_out", _P), ("w_gate_up", _P), ("w_down", _P), ("q_norm", _P), ("k_norm", _P),
+                ("adaln_table", _P)]
+
+
+TAP_FLOAT = ("adaln1", "q_rot", "k_rot", "v_t", "attn_o", "attn_proj", "x_mid", "adaln2", "ffn_h", "ffn_out")
+TAP_INT = ("table_row", "doc_id", "tile_flags", "num_pad")
+
+
+class _Taps(ctypes.Structure):
+    _fields_ = [(n, _P) for n in TAP_FLOAT + TAP_INT]
+
+
+class Minih3Error(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = status_string(status) if _lib_loaded() else str(status)
+        super().__init__(f"{what}: {msg} ({status})" if what else f"{msg} ({status})")
+
+
+_LIB = None
+
+
+def _lib_loaded() -> bool:
+    return _LIB is not None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise Minih3Error(E_HIP, f"{LIB_PATH} is not built (python -m joint_video_audio_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.minih3_status_string.restype = ctypes.c_char_p
+        L.minih3_status_string.argtypes = [ctypes.c_int]
+        L.minih3_kernel_name.restype = ctypes.c_char_p
+        L.minih3_kernel_name.argtypes = [ctypes.c_int32]
+        L.minih3_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_attention_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_block_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
+                                           ctypes.POINTER(_BlockWeights), ctypes.c_int32, _P, _P, _P,
+                                           ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
+        L.minih3_attention_packed.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, _P,
+                                              ctypes.c_int32, _P, ctypes.c_float, _P, ctypes.c_size_t,
+                                              ctypes.c_uint32, _P]
+        L.minih3_adaln_modulate.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, ctypes.c_int32,
+                                            _P, ctypes.c_uint32, _P]
+        L.minih3_qk_norm_rope.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_int32, _P]
+        L.minih3_linear.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
+        L.minih3_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), _I32P, ctypes.c_int32]
+        for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
+                   "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
+                   "minih3_profile_collect"):
+            getattr(L, fn).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_workspace_bytes",
+            "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
+            "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string")
+
+
+def status_string(s: int) -> str:
+    return lib().minih3_status_string(int(s)).decode()
+
+
+def _check(s: int, what: str):
+    if s != OK:
+        raise Minih3Error(s, what)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _req(t: torch.Tensor, dtype: torch.dtype, name: str, numel: Optional[int] = None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def act_torch_dtype(cfg: Config) -> torch.dtype:
+    return torch.bfloat16 if cfg.act_dtype == BF16 else torch.float32
+
+
+# --------------------------------------------------------------------------
+# layout on the device
+
+class DeviceLayout:
+    """int32 device copies of one packed layout (shared by all batch items)."""
+
+    def __init__(self, batch: int, token_tags, timestep_indices, position_ids, video_indices, audio_indices,
+                 text_indices, device="cuda"):
+        def i32(a):
+            t = torch.as_tensor(a)
+            return t.to(device=device, dtype=torch.int32).contiguous()
+
+        self.batch = int(batch)
+        self.token_tags = i32(token_tags)
+        self.timestep_indices = i32(timestep_indices)
+        self.position_ids = i32(position_ids).reshape(-1, 3).contiguous()
+        self.video_indices = i32(video_indices)
+        self.audio_indices = i32(audio_indices)
+        self.text_indices = i32(text_indices)
+        self.seq_len = int(self.token_tags.numel())
+        if self.timestep_indices.numel() != self.seq_len or self.position_ids.shape[0] != self.seq_len:
+            raise ValueError("token_tags, timestep_indices and position_ids must describe the same rows")
+
+    @property
+    def seq_stride(self) -> int:
+        return (self.seq_len + 63) // 64 * 64
+
+    def c(self) -> _Layout:
+        def p(t):
+            return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+        return _Layout(self.batch, self.seq_len, p(self.token_tags), p(self.timestep_indices), p(self.position_ids),
+                       p(self.video_indices), self.video_indices.numel(), p(self.audio_indices),
+                       self.audio_indices.numel(), p(self.text_indices), self.text_indices.numel())
+
+
+class DeviceBlock:
+    """Device weights of one block (matrices in act dtype, norms/table fp32)."""
+
+    def __init__(self, w_qkv, w_out, w_gate_up, w_down, q_norm, k_norm, adaln_table):
+        self.w_qkv, self.w_out, self.w_gate_up, self.w_down = w_qkv, w_out, w_gate_up, w_down
+        self.q_norm, self.k_norm, self.adaln_table = q_norm, k_norm, adaln_table
+
+    def check(self, cfg: Config):
+        dt = act_torch_dtype(cfg)
+        D, W, F, hd = cfg.hidden, cfg.num_heads * cfg.head_dim, cfg.ffn_dim, cfg.head_dim
+        _req(self.w_qkv, dt, "w_qkv", 3 * W * D)
+        _req(self.w_out, dt, "w_out", D * W)
+        _req(self.w_gate_up, dt, "w_gate_up", 2 * F * D)
+        _req(self.w_down, dt, "w_down", D * F)
+        _req(self.q_norm, torch.float32, "q_norm", hd)
+        _req(self.k_norm, torch.float32, "k_norm", hd)
+        _req(self.adaln_table, torch.float32, "adaln_table", cfg.num_tags * cfg.num_tvals * 6 * D)
+
+    def c(self) -> _BlockWeights:
+        return _BlockWeights(*(ctypes.c_void_p(t.data_ptr()) for t in (
+            self.w_qkv, self.w_out, self.w_gate_up, self.w_down, self.q_norm, self.k_norm, self.adaln_table)))
+
+
+# --------------------------------------------------------------------------
+# entry points
+
+def workspace_bytes(cfg: Config, batch: int, seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().minih3_workspace_bytes(ctypes.byref(cfg), batch, seq_len, ctypes.byref(n)), "workspace_bytes")
+    return int(n.value)
+
+
+def attention_workspace_bytes(seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().minih3_attention_workspace_bytes(seq_len, ctypes.byref(n)), "attention_workspace_bytes")
+    return int(n.value)
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def block_forward(cfg: Config, layout: DeviceLayout, blocks: Sequence[DeviceBlock], x: torch.Tensor,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                  taps: Optional[dict] = None) -> torch.Tensor:
+    """x [B, S, D] -> out [B, S, D] through len(blocks) chained blocks."""
+    dt = act_torch_dtype(cfg)
+    B, S, D = layout.batch, layout.seq_len, cfg.hidden
+    _req(x, dt, "x", B * S * D)
+    for b in blocks:
+        b.check(cfg)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, dt, "out", B * S * D)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes(cfg, B, S), x.device)
+    arr = (_BlockWeights * len(blocks))(*[b.c() for b in blocks])
+    ct = None
+    if taps:
+        ct = _Taps(**{k: (ctypes.c_void_p(v.data_ptr()) if v is not None else None) for k, v in taps.items()})
+    L = layout.c()
+    s = lib().minih3_block_forward(ctypes.byref(cfg), ctypes.byref(L), arr, len(blocks), _ptr(x), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), flags,
+                                   ctypes.byref(ct) if ct is not None else None, _stream())
+    _check(s, "block_forward")
+    return out
+
+
+def attention_packed(cfg: Config, layout: DeviceLayout, q: torch.Tensor, k: torch.Tensor, v_t: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, flags: int = 0,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q, k [B, H, stride, hd], v_t [B, H, hd, stride] -> out [B, S, H*hd]."""
+    dt = act_torch_dtype(cfg)
+    B, H, hd, S = layout.batch, cfg.num_heads, cfg.head_dim, layout.seq_len
+    stride = q.shape[2]
+    for t, n in ((q, "q"), (k, "k"), (v_t, "v_t")):
+        _req(t, dt, n, B * H * stride * hd)
+    if out is None:
+        out = torch.empty(B, S, H * hd, dtype=dt, device=q.device)
+    _req(out, dt, "out", B * S * H * hd)
+    if workspace is None:
+        workspace = alloc_workspace(attention_workspace_bytes(S), q.device)
+    L = layout.c()
+    s = lib().minih3_attention_packed(ctypes.byref(cfg), ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v_t), stride,
+                                      _ptr(out), float(softmax_scale), _ptr(workspace), workspace.numel(), flags,
+                                      _stream())
+    _check(s, "attention_packed")
+    return out
+
+
+def adaln_modulate(cfg: Config, layout: DeviceLayout, x: torch.Tensor, adaln_table: torch.Tensor, which: int,
+                   y: Optional[torch.Tensor] = None, flags: int = 0) -> torch.Tensor:
+    dt = act_torch_dtype(cfg)
+    B, S, D = layout.batch, layout.seq_len, cfg.hidden
+    _req(x, dt, "x", B * S * D)
+    _req(adaln_table, torch.float32, "adaln_table", cfg.num_tags * cfg.num_tvals * 6 * D)
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, dt, "y", B * S * D)
+    L = layout.c()
+    _check(lib().minih3_adaln_modulate(ctypes.byref(cfg), ctypes.byref(L), _ptr(x), _ptr(adaln_table), which,
+                                       _ptr(y), flags, _stream()), "adaln_modulate")
+    return y
+
+
+def qk_norm_rope(cfg: Config, layout: DeviceLayout, qkv: torch.Tensor, q_norm: torch.Tensor, k_norm: torch.Tensor):
+    """qkv [B, S, 3W] -> (q, k [B, H, stride, hd], v_t [B, H, hd, stride])."""
+    dt = act_torch_dtype(cfg)
+    B, S, H, hd = layout.batch, layout.seq_len, cfg.num_heads, cfg.head_dim
+    _req(qkv, dt, "qkv", B * S * 3 * H * hd)
+    _req(q_norm, torch.float32, "q_norm", hd)
+    _req(k_norm, torch.float32, "k_norm", hd)
+    st = layout.seq_stride
+    q = torch.empty(B, H, st, hd, dtype=dt, device=qkv.device)
+    k = torch.empty_like(q)
+    vt = torch.empty(B, H, hd, st, dtype=dt, device=qkv.device)
+    L = layout.c()
+    _check(lib().minih3_qk_norm_rope(ctypes.byref(cfg), ctypes.byref(L), _ptr(qkv), _ptr(q_norm), _ptr(k_norm),
+                                     _ptr(q), _ptr(k), _ptr(vt), st, _stream()), "qk_norm_rope")
+    return q, k, vt
+
+
+def linear(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[M, N] = a[M, K] . w[N, K]^T (bf16 or fp32)."""
+    if a.dtype == torch.bfloat16:
+        dtc = BF16
+    elif a.dtype == torch.float32:
+        dtc = F32
+    else:
+        raise ValueError("a must be bf16 or fp32")
+    M, K = a.shape
+    N = w.shape[0]
+    _req(a, a.dtype, "a")
+    _req(w, a.dtype, "w", N * K)
+    if out is None:
+        out = torch.empty(M, N, dtype=a.dtype, device=a.device)
+    _req(out, a.dtype, "out", M * N)
+    _check(lib().minih3_linear(dtc, _ptr(a), _ptr(w), _ptr(out), M, N, K, _stream()), "linear")
+    return out
+
+
+def profile_collect() -> dict:
+    n = 16
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    k = lib().minih3_profile_collect(ms, cnt, n)
+    res = {}
+    for i in range(k):
+        name = lib().minih3_kernel_name(i).decode()
+        res[name] = (float(ms[i]), int(cnt[i]))
+    return res

@@ -1,0 +1,55 @@
+"""The C-ABI library loads and exports every symbol include/minih3.h declares
+(CPU only: host-side entry points that enqueue no GPU work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from joint_video_audio_amd import device as dv
+from joint_video_audio_amd import minih3 as m
+from joint_video_audio_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "minih3.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(minih3_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libminih3.so not built")
+    lib = ctypes.CDLL(m.LIB_PATH)
+    names = declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(m.EXPORTED)
+
+
+def test_host_side_queries_and_argument_errors():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libminih3.so not built")
+    assert m.status_string(m.E_NEEDS_MASK).startswith("layout")
+    cfg = dv.config_for(synth.workload_dims("clip32k"))
+    nbytes = m.workspace_bytes(cfg, 1, 32768)
+    # the workspace holds at least the qkv, q/k/v^T and attention buffers in bf16
+    assert nbytes > 32768 * (3 * 7168 + 3 * 7168 + 7168) * 2
+    assert m.attention_workspace_bytes(100) >= 16 * 2
+    lib = m.lib()
+    bad = m.Config(**{f: getattr(cfg, f) for f, _ in m.Config._fields_})
+    bad.head_dim = 64
+    n = ctypes.c_size_t(0)
+    assert lib.minih3_workspace_bytes(ctypes.byref(bad), 1, 10, ctypes.byref(n)) == m.E_UNSUPPORTED
+    assert lib.minih3_block_forward(None, None, None, 1, None, None, None, 0, 0, None, None) == m.E_ARG
+    # a valid call shape with a too-small workspace is refused before any GPU work
+    L = m._Layout(1, 8, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None, 0, None, 0, None, 0)
+    bw = (m._BlockWeights * 1)(m._BlockWeights(*[ctypes.c_void_p(16)] * 7))
+    s = lib.minih3_block_forward(ctypes.byref(cfg), ctypes.byref(L), bw, 1, ctypes.c_void_p(16),
+                                 ctypes.c_void_p(32), ctypes.c_void_p(64), 10, 0, None, None)
+    assert s == m.E_WORKSPACE
+    assert lib.minih3_linear(0, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 4, 100, 64,
+                             None) == m.E_UNSUPPORTED
