@@ -1,0 +1,175 @@
+"""Throughput of the packed DiT block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload clip32k]
+
+A step is one forward pass of the whole block (all kernels: AdaLN, QKV
+projection, q/k RMSNorm + RoPE, attention, output projection + gated
+residual, AdaLN, SwiGLU FFN, down projection + gated residual) over one
+packed sequence of synthetic inputs already resident in HBM. The default
+workload is the clip-scale block: hidden 5376, 56 x 128 heads, FFN 14336,
+32768 packed rows (1024 text, 1536 audio, 30208 video on a 16 x 32 x 59
+grid), bf16. Prints one JSON line.
+
+value = packed rows / s per block forward; TFLOP/s counts algorithmic work
+only (GEMMs on non-padding rows, attention on same-document pairs of
+non-padding rows). The dominant kernel's roofline uses its average launch
+time from HIP events recorded on the launch stream inside the timed region.
+cpu_baseline times the fp64 oracle on a bounded sample of the workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk (dense)
+HBM_PEAK_GBS = 8000.0
+
+
+def flop_counts(dims, layout):
+    """Algorithmic FLOP per block forward: (gemm, attention)."""
+    import numpy as np
+    D, W, F = dims.hidden, dims.num_heads * dims.head_dim, dims.ffn_dim
+    real = int((np.asarray(layout.token_tags) != -1).sum())
+    per_row = 2 * (D * 3 * W + W * D + D * 2 * F + F * D)
+    gemm = per_row * real
+    attn = 4 * dims.head_dim * dims.num_heads * real * real
+    return gemm, attn
+
+
+def cpu_baseline(wl, rows: int):
+    """The oracle (fp64 numpy) timed on the first `rows` packed rows of the
+    workload taken as their own sequence; scaled to rows/s of the full
+    workload by FLOP per row."""
+    import numpy as np
+    import oracle
+    from oracle import block as ob
+    from joint_video_audio_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    L = wl.layout
+    n = min(rows, L.seq_len)
+    sub = synth.Layout(L.token_tags[:n], L.timestep_indices[:n], L.position_ids[:n],
+                       L.video_indices[L.video_indices < n], L.audio_indices[L.audio_indices < n],
+                       L.text_indices[L.text_indices < n])
+    w = oracle.weights_f64(wl.blocks[0])
+    x = wl.x.values()[0][:n]
+    t0 = time.perf_counter()
+    ob.block_forward(x, sub, w, wl.dims)
+    t = time.perf_counter() - t0
+    g_s, a_s = flop_counts(wl.dims, sub)
+    g_f, a_f = flop_counts(wl.dims, L)
+    flops_per_s = (g_s + a_s) / t
+    rows_per_s = flops_per_s / ((g_f + a_f) / L.seq_len)
+    return dict(value=rows_per_s, unit="rows/s", cores=int(cores), kind="oracle",
+                sample=f"fp64 numpy oracle, full block on the first {n} packed rows of the workload as their own "
+                       f"sequence ({t:.1f} s, {flops_per_s / 1e9:.1f} GFLOP/s); scaled to the full workload's rows/s "
+                       f"by algorithmic FLOP per row")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="clip32k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the block is measured on a single "
+              f"MI355X and no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from joint_video_audio_amd import device as dv
+    from joint_video_audio_amd import minih3 as m
+    from joint_video_audio_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    m.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    t0 = time.time()
+    wl = synth.make_workload(a.workload, seed=a.seed)
+    cfg, lay, blocks, x = dv.upload(wl)
+    out = torch.empty_like(x)
+    ws = m.alloc_workspace(m.workspace_bytes(cfg, lay.batch, lay.seq_len))
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {a.workload} S={lay.seq_len} "
+          f"pads={wl.layout.num_pad} blocks={len(blocks)}", file=sys.stderr, flush=True)
+    nb = len(blocks)
+
+    for _ in range(a.warmup):
+        m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    m.profile_collect()  # drop anything recorded so far
+
+    st = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(st)
+    for _ in range(a.steps):
+        m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws, flags=m.PROFILE)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / a.steps
+    kern = m.profile_collect()
+
+    gemm, attn = flop_counts(wl.dims, wl.layout)
+    t_block = ms_step / 1e3 / nb
+    rows_s = lay.seq_len / t_block
+    tflops = (gemm + attn) / t_block / 1e12
+
+    att_ms, att_n = kern["attention"]
+    att_avg = att_ms / max(att_n, 1)
+    att_tflops = attn / (att_avg / 1e3) / 1e12
+    kernels = {k: round(v[0] / max(v[1], 1), 4) for k, v in kern.items() if v[1]}
+
+    res = {
+        "metric": "packed rows/s and TFLOP/s per block forward (hidden 5376, 56x128 heads) on 1 GPU",
+        "value": round(rows_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dims.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) latents, N(0,0.02) weights, random-init AdaLN tables)",
+        "config": {"workload": a.workload, "seq_len": lay.seq_len, "pad_rows": wl.layout.num_pad,
+                   "blocks_per_step": nb, "hidden": wl.dims.hidden, "heads": wl.dims.num_heads,
+                   "head_dim": wl.dims.head_dim, "ffn_dim": wl.dims.ffn_dim, "timestep_values": wl.dims.num_tvals,
+                   "seed": a.seed},
+        "tflops": round(tflops, 1),
+        "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "kernel_avg_ms": kernels,
+        "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(att_tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(att_avg, 4)},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

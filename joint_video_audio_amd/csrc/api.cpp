@@ -85,6 +85,14 @@ int check_config(const minih3_config* c) {
   return MINIH3_OK;
 }
 
+// Attention reads only head_dim, num_heads and act_dtype of the config.
+int check_config_attention(const minih3_config* c) {
+  if (!c) return MINIH3_E_ARG;
+  if (c->act_dtype != MINIH3_BF16 && c->act_dtype != MINIH3_F32) return MINIH3_E_ARG;
+  if (c->head_dim != 128 || c->num_heads < 1) return MINIH3_E_UNSUPPORTED;
+  return MINIH3_OK;
+}
+
 int check_layout(const minih3_layout* L, bool need_indices) {
   if (!L) return MINIH3_E_ARG;
   if (L->batch < 1 || L->seq_len < 1) return MINIH3_E_ARG;
@@ -370,7 +378,7 @@ int minih3_block_forward(const minih3_config* c, const minih3_layout* L, const m
 int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, const void* q, const void* k,
                             const void* v_t, int32_t seq_stride, void* out, float softmax_scale, void* workspace,
                             size_t workspace_bytes, uint32_t flags, void* stream) {
-  int s = check_config(c);
+  int s = check_config_attention(c);
   if (s) return s;
   if (!L || L->batch < 1 || L->seq_len < 1 || !L->token_tags) return MINIH3_E_ARG;
   if (!q || !k || !v_t || !out) return MINIH3_E_ARG;
