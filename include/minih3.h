@@ -138,8 +138,9 @@ int minih3_block_forward(const minih3_config* cfg, const minih3_layout* layout,
                          const void* x_in, void* x_out, void* workspace, size_t workspace_bytes,
                          uint32_t flags, minih3_taps* taps, void* stream);
 
-/* Bytes of workspace minih3_attention_packed needs for seq_len S. */
-int minih3_attention_workspace_bytes(int32_t seq_len, size_t* bytes);
+/* Bytes of workspace minih3_attention_packed needs for (batch, seq_len)
+ * with cfg->num_heads heads. */
+int minih3_attention_workspace_bytes(const minih3_config* cfg, int32_t batch, int32_t seq_len, size_t* bytes);
 
 /* Attention over the packed sequence (page: full self-attention; padding
  * rows kept in their own document by a boolean mask):

@@ -58,11 +58,11 @@ struct Timed {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     a = g_prof.get();
     b = g_prof.get();
-    if (a && b) hipEventRecord(a, st);
+    if (a && b) (void)hipEventRecord(a, st);
   }
   ~Timed() {
     if (!on || !a || !b) return;
-    hipEventRecord(b, st);
+    (void)hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.recs.push_back({id, a, b});
   }
@@ -110,12 +110,15 @@ int check_layout(const minih3_layout* L, bool need_indices) {
 struct Workspace {
   void *a, *qkvh, *qn, *kn, *vt, *o, *xmid, *xping;
   uint64_t* masks;
+  void* attn_scratch;
   int32_t *list_real, *list_pad, *meta, *counts, *npad;
   uint32_t* err;
   size_t total;
 };
 
-size_t tiles_bytes(int S, int32_t** list_real, int32_t** list_pad, int32_t** meta, uint64_t** masks, char* base) {
+// Attention scratch: tile masks and lists, then the kernels' own scratch.
+size_t tiles_bytes(int B, int S, int H, int32_t** list_real, int32_t** list_pad, int32_t** meta, uint64_t** masks,
+                   void** scratch, char* base) {
   const size_t nt = (size_t)(S + 63) / 64;
   size_t off = 0;
   auto take = [&](size_t n) {
@@ -132,6 +135,8 @@ size_t tiles_bytes(int S, int32_t** list_real, int32_t** list_pad, int32_t** met
   if (list_pad) *list_pad = (int32_t*)p;
   p = take(16);
   if (meta) *meta = (int32_t*)p;
+  p = take(attention_scratch_bytes(B, S, H));
+  if (scratch) *scratch = p;
   return off;
 }
 
@@ -156,8 +161,8 @@ Workspace carve(const minih3_config* c, int B, int S, char* base) {
   w.o = take(M * Wd * e);
   w.xmid = take(M * D * e);
   w.xping = take(M * D * e);
-  char* tb = take(tiles_bytes(S, nullptr, nullptr, nullptr, nullptr, nullptr));
-  if (base) tiles_bytes(S, &w.list_real, &w.list_pad, &w.meta, &w.masks, tb);
+  char* tb = take(tiles_bytes(B, S, (int)H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
+  if (base) tiles_bytes(B, S, (int)H, &w.list_real, &w.list_pad, &w.meta, &w.masks, &w.attn_scratch, tb);
   w.counts = (int32_t*)take(4 * (size_t)S);
   w.npad = (int32_t*)take(4);
   w.err = (uint32_t*)take(4);
@@ -239,8 +244,8 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
     }
     {
       Timed tm(prof, kKAttention, st);
-      HIPCHECK(launch_attention<T>(qn, kn, vt, o, L->token_tags, w.masks, w.list_real, w.list_pad, w.meta, B, S, H,
-                                   Sp, scale, padless, st));
+      HIPCHECK(launch_attention<T>(qn, kn, vt, o, w.masks, w.list_real, w.list_pad, w.meta, w.attn_scratch, B, S, H,
+                                   Sp, scale, st));
     }
     if (tap && taps->attn_o) HIPCHECK(hipMemcpyAsync(taps->attn_o, o, (size_t)M * Wd * e, hipMemcpyDeviceToDevice, st));
     if (tap && taps->attn_proj) HIPCHECK(launch_gemm<T>(kEpiStore, o, (const T*)bw.w_out, (T*)taps->attn_proj, M, D, Wd, ea, st));
@@ -324,9 +329,11 @@ int minih3_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_le
   return MINIH3_OK;
 }
 
-int minih3_attention_workspace_bytes(int32_t seq_len, size_t* bytes) {
-  if (!bytes || seq_len < 1) return MINIH3_E_ARG;
-  *bytes = tiles_bytes(seq_len, nullptr, nullptr, nullptr, nullptr, nullptr);
+int minih3_attention_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_len, size_t* bytes) {
+  int s = check_config_attention(c);
+  if (s) return s;
+  if (!bytes || seq_len < 1 || batch < 1) return MINIH3_E_ARG;
+  *bytes = tiles_bytes(batch, seq_len, c->num_heads, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
   return MINIH3_OK;
 }
 
@@ -387,7 +394,9 @@ int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, cons
   if ((long)L->batch * c->num_heads * seq_stride > (1L << 31) - 1) return MINIH3_E_UNSUPPORTED;
   int32_t *list_real, *list_pad, *meta;
   uint64_t* masks;
-  const size_t need = tiles_bytes(S, &list_real, &list_pad, &meta, &masks, (char*)workspace);
+  void* scratch;
+  const size_t need = tiles_bytes(L->batch, S, c->num_heads, &list_real, &list_pad, &meta, &masks, &scratch,
+                                  (char*)workspace);
   if (!workspace || workspace_bytes < need) return MINIH3_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int padless = (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0;
@@ -401,13 +410,13 @@ int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, cons
   HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, masks, list_real, list_pad, meta, st));
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)c->head_dim);
   if (c->act_dtype == MINIH3_BF16)
-    HIPCHECK(launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v_t, (bf16_t*)out,
-                                      L->token_tags, masks, list_real, list_pad, meta, L->batch, S, c->num_heads,
-                                      seq_stride, scale, padless, st));
+    HIPCHECK(launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v_t, (bf16_t*)out, masks,
+                                      list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, seq_stride, scale,
+                                      st));
   else
-    HIPCHECK(launch_attention<float>((const float*)q, (const float*)k, (const float*)v_t, (float*)out, L->token_tags,
-                                     masks, list_real, list_pad, meta, L->batch, S, c->num_heads, seq_stride, scale,
-                                     padless, st));
+    HIPCHECK(launch_attention<float>((const float*)q, (const float*)k, (const float*)v_t, (float*)out, masks,
+                                     list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, seq_stride, scale,
+                                     st));
   return MINIH3_OK;
 }
 

@@ -8,22 +8,33 @@
 // batch axis replicates the layout and each item is its own document.
 // Scale 1/sqrt(head_dim) unless the caller gives one (the page is silent).
 //
-// bf16 kernel (gfx950), flash-style with an fp32 online softmax:
-//   * workgroup = 4 waves x 64 queries of one head; q stays in registers;
+// bf16 kernels (gfx950), flash-style, fp32 softmax:
+//   * a workgroup is 8 waves x 32 queries of one head; q stays in registers;
 //   * K tiles [64 keys][128] and V^T tiles [128][64 keys] are staged in LDS
-//     (2 stages, XOR-swizzled 16-byte chunks), the next tile's global loads
-//     in flight while the current one is used;
-//   * scores are computed transposed, S^T = K Q^T with
-//     v_mfma_f32_32x32x16_bf16, so each lane owns one query column: the row
-//     max needs one exchange between the two 32-lane halves and the running
-//     max / sum / rescale are per-lane scalars. Key rows are fed to the MFMA
-//     in an order (bits 2 and 3 of the row swapped) that makes the score
-//     registers exactly the B operand of O^T += V^T P^T, so P never leaves
-//     registers;
-//   * exponentials in base 2 with scale*log2(e) folded into one FMA;
+//     (2 stages, XOR-swizzled 16-byte chunks); the next tile's global loads
+//     are in flight while the current one is used;
+//   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
+//     so each lane owns one query column and all per-query state is
+//     per-lane. Key rows enter the MFMA in an order (bits 2 and 3 of the row
+//     swapped) that makes the score registers exactly the B operand of
+//     O^T += V^T P^T: P never leaves registers;
+//   * fixed-reference softmax: for query i the exponent reference is
+//     m_i = |q_i| * max_j |k_j| over the keys of the query's document
+//     (scale * log2(e) folded into q), an upper bound of every score of the
+//     row (Cauchy-Schwarz). Probabilities
+//     exp2(s - m_i) are <= 1, so the row needs no running max and the O
+//     accumulators are never rescaled; the score accumulators start at -m_i
+//     so that exp2 reads the MFMA result directly. The bound is used only
+//     when m_i <= 55, so that every probability of the row that matters
+//     stays far above the fp32 / bf16 underflow (>= 2^-110); a workgroup
+//     holding a query with a larger bound leaves its tile to a second kernel
+//     with the classic running max (rescaled lazily, when the max grows by
+//     more than 2^8). After per-head q/k RMSNorm the bound is small, so the
+//     second kernel only exits early;
 //   * document masks per 64-key tile (non-padding / padding bit masks built
-//     once per call): tiles holding no key of a wave's documents are
-//     skipped, fully-matching tiles need no per-element mask.
+//     once per call): workgroups whose queries all sit in one document walk
+//     only the tiles holding keys of that document; fully-matching tiles
+//     need no per-element mask;
 //   * workgroups are ordered so that the workgroups of one head run on the
 //     same XCD and share its K/V stream in that XCD's L2.
 #include "common.h"
@@ -31,8 +42,12 @@
 
 namespace minih3 {
 
-constexpr int kAttnQ = 256;  // queries per workgroup
-constexpr int kKV = 64;      // keys per tile
+constexpr int kKV = 64;     // keys per tile
+constexpr int kNW = 8;      // waves per workgroup
+constexpr int kQG = kNW * 32;  // queries per workgroup
+constexpr int HD = 128;
+constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
+constexpr float kMaxRef = 55.f;  // largest fixed reference (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -42,111 +57,98 @@ __device__ __forceinline__ int key_of_reg(int r, int hi) {
   return 16 * (i >> 1) + 8 * hi + 4 * (i & 1) + j;
 }
 
-__global__ void __launch_bounds__(256, 1)
-    k_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
-                bf16_t* __restrict__ out, const uint64_t* __restrict__ masks, const int32_t* __restrict__ list_real,
-                const int32_t* __restrict__ list_pad, const int32_t* __restrict__ meta, int S, int H, int stride,
-                float c_log2, int n_qt, int total) {
-  constexpr int HD = 128;
-  constexpr int KT_BYTES = kKV * HD * 2;     // 16 KiB
-  constexpr int STAGE = 2 * KT_BYTES;        // K + V^T
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-
-  // ---- workgroup -> (query tile, head, batch); XCD-contiguous order
+// Workgroup -> (query tile, b*H + h) with XCD-contiguous ranges.
+struct WgPos {
+  int pid, qt, bh;
+};
+__device__ __forceinline__ WgPos wg_pos(int n_qt, int total) {
   const int bid = blockIdx.x;
   const int xcd = bid & 7, loc = bid >> 3;
   const int q8 = total >> 3, r8 = total & 7;
-  const int pid = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
-  const int qt = pid % n_qt;
-  const int bh = pid / n_qt;  // b * H + h
-  const int h = bh % H, b = bh / H;
-  const long head_row = (long)bh * stride;  // row offset of (b,h) in [B,H,stride,hd]
-  const int ntiles = stride / kKV;
-  const int nt_real = (S + kKV - 1) / kKV;
+  WgPos p;
+  p.pid = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+  p.qt = p.pid % n_qt;
+  p.bh = p.pid / n_qt;
+  return p;
+}
 
-  // ---- documents of this workgroup's and this wave's queries
-  const int qw0 = qt * kAttnQ + wid * 64;  // first query of the wave
-  bool wq_real = false, wq_pad = false;
-  if (qw0 < S) {
-    const int t = qw0 / kKV;
-    wq_real = masks[2 * t] != 0;
-    wq_pad = masks[2 * t + 1] != 0;
-  }
-  bool g_real = false, g_pad = false;
+// Shared pieces of the two bf16 kernels: documents, tile list, K/V^T tile
+// staging through LDS.
+struct TileWalk {
+  static constexpr int NT = kNW * 64;
+  static constexpr int KT_BYTES = kKV * HD * 2;  // 16 KiB
+  static constexpr int STAGE = 2 * KT_BYTES;     // K + V^T
+  static constexpr int CH = 1024 / NT;           // 16-byte chunks per thread per tile (K or V^T)
+
+  const int* list;
+  int n_iter;
+  bool wq_real, wq_pad;   // documents present among this wave's queries
+  int qdoc;               // this lane's query document
+  const bf16_t* kbase;
+  const bf16_t* vbase;
+  int k_st[CH], v_st[CH];
+  int vc, S, stride;
+  u32x4 rk[CH], rv[CH];
+
+  __device__ __forceinline__ void init(const bf16_t* k, const bf16_t* vt, const uint64_t* masks,
+                                       const int32_t* list_real, const int32_t* list_pad, const int32_t* meta,
+                                       int S_, int stride_, int qt, int bh, int qw0, int qr) {
+    S = S_;
+    stride = stride_;
+    const int tid = threadIdx.x;
+    const int nt_real = (S + kKV - 1) / kKV;
+    wq_real = wq_pad = false;
+    if (qw0 < S) {
+      wq_real = masks[2 * (qw0 / kKV)] != 0;
+      wq_pad = masks[2 * (qw0 / kKV) + 1] != 0;
+    }
+    bool g_real = false, g_pad = false;
+    for (int r = qt * kQG; r < qt * kQG + kQG && r < S; r += kKV) {
+      g_real |= masks[2 * (r / kKV)] != 0;
+      g_pad |= masks[2 * (r / kKV) + 1] != 0;
+    }
+    list = nullptr;
+    if (g_real && g_pad) {
+      n_iter = nt_real;  // every tile
+    } else if (g_pad) {
+      list = list_pad;
+      n_iter = meta[1];
+    } else {
+      list = list_real;
+      n_iter = meta[0];
+    }
+    qdoc = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
+
+    // K tile: 64 rows x 16 chunks; thread owns chunk (tid & 15) of rows (tid >> 4) + 32 i
+    // V^T tile: 128 rows x 8 chunks; thread owns chunk (tid & 7) of rows (tid >> 3) + 64 i
+    const long head_row = (long)bh * stride;
+    const int kc = tid & 15, kr0 = tid >> 4;
+    vc = tid & 7;
+    const int vr0 = tid >> 3;
+    kbase = k + (head_row + kr0) * HD + kc * 8;
+    vbase = vt + ((long)bh * HD + vr0) * stride + vc * 8;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int qq = qt * kAttnQ + w * 64;
-    if (qq < S) {
-      g_real |= masks[2 * (qq / kKV)] != 0;
-      g_pad |= masks[2 * (qq / kKV) + 1] != 0;
+    for (int i = 0; i < CH; ++i) {
+      const int kr = kr0 + (NT / 16) * i;
+      const int fk = (kr & 3) | (((kr >> 3) & 1) << 2);
+      k_st[i] = kr * 256 + ((kc ^ fk) << 4);
+      const int vr = vr0 + (NT / 8) * i;
+      v_st[i] = KT_BYTES + vr * 128 + ((vc ^ (vr & 7)) << 4);
     }
   }
-  const int* list = nullptr;
-  int n_iter;
-  if (g_real && g_pad) {
-    n_iter = nt_real;  // every tile
-  } else if (g_pad) {
-    list = list_pad;
-    n_iter = meta[1];
-  } else {
-    list = list_real;
-    n_iter = meta[0];
-  }
-
-  // per-lane query documents (1 = padding row) for the two 32-query blocks
-  int qdoc[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qr = qw0 + qb * 32 + l32;
-    qdoc[qb] = 0;
-    if (qr < S) qdoc[qb] = (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull);
-  }
-
-  // ---- Q fragments (B operand of S^T = K Q^T): query column l32, dims 16kk + 8hi .. +8
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    int qr = qw0 + qb * 32 + l32;
-    qr = qr < stride ? qr : stride - 1;
-    const bf16_t* src = q + (head_row + qr) * HD + 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[qb][kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
-  }
-
-  // ---- global -> LDS mapping
-  // K tile: 64 rows x 16 chunks; thread owns chunk (tid & 15) of rows (tid >> 4) + 16 i
-  // V^T tile: 128 rows x 8 chunks; thread owns chunk (tid & 7) of rows (tid >> 3) + 32 i
-  const int kc = tid & 15, kr0 = tid >> 4;
-  const int vc = tid & 7, vr0 = tid >> 3;
-  const bf16_t* kbase = k + head_row * HD + kr0 * HD + kc * 8;
-  const bf16_t* vbase = vt + ((long)bh * HD + vr0) * stride + vc * 8;
-  int k_st[4], v_st[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kr = kr0 + 16 * i;
-    const int fk = (kr & 3) | (((kr >> 3) & 1) << 2);
-    k_st[i] = kr * 256 + ((kc ^ fk) << 4);
-    const int vr = vr0 + 32 * i;
-    v_st[i] = KT_BYTES + vr * 128 + ((vc ^ (vr & 7)) << 4);
-  }
-
-  u32x4 rk[4], rv[4];
-  auto tile_of = [&](int it) { return list ? list[it] : it; };
-  auto gload = [&](int t) {
+  __device__ __forceinline__ int tile(int it) const { return list ? list[it] : it; }
+  __device__ __forceinline__ void gload(int t) {
     const long key0 = (long)t * kKV;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + 16 * i) * HD);
-      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (long)(32 * i) * stride + key0);
+    for (int i = 0; i < CH; ++i) {
+      rk[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + (NT / 16) * i) * HD);
+      rv[i] = *reinterpret_cast<const u32x4*>(vbase + (long)((NT / 8) * i) * stride + key0);
     }
     // values of keys >= S are zeroed so that masked keys contribute exactly 0
     if (key0 + kKV > S) {
       const int first = (int)(S - key0) - vc * 8;  // keys of this chunk below S
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < CH; ++i) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int e0 = 2 * w;
@@ -157,153 +159,322 @@ __global__ void __launch_bounds__(256, 1)
         }
       }
     }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* base = lds + stage * STAGE;
+  }
+  __device__ __forceinline__ void lstore(uint8_t* base) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CH; ++i) {
       *reinterpret_cast<u32x4*>(base + k_st[i]) = rk[i];
       *reinterpret_cast<u32x4*>(base + v_st[i]) = rv[i];
     }
-  };
+  }
+};
 
-  // fragment-read offsets
-  // K (A operand of S^T): key row kb*32 + sigma(l32), chunk 2kk + hi
-  const int krow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2 and 3 swapped
-  const int kfk = (krow & 3) | (((krow >> 3) & 1) << 2);
-  // V^T (A operand of O^T): row db*32 + l32, chunk kb*4 + cc*2 + hi
-  const int vsw = l32 & 7;
+// Fragment-read offsets inside a staged tile.
+//   K (A operand of S^T): key row kb*32 + sigma(l32), chunk 2kk + hi
+//   V^T (A operand of O^T): row db*32 + l32, chunk kb*4 + cc*2 + hi
+struct Frag {
+  int krow, kfk, vsw;
+  __device__ __forceinline__ Frag(int l32) {
+    krow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2 and 3 swapped
+    kfk = (krow & 3) | (((krow >> 3) & 1) << 2);
+    vsw = l32 & 7;
+  }
+  __device__ __forceinline__ bf16x8 k(const uint8_t* Ks, int kb, int kk, int hi) const {
+    return *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + krow) * 256 + (((2 * kk + hi) ^ kfk) << 4));
+  }
+  __device__ __forceinline__ bf16x8 v(const uint8_t* Vs, int db, int kb, int cc, int l32, int hi) const {
+    return *reinterpret_cast<const bf16x8*>(Vs + (db * 32 + l32) * 128 + (((kb * 4 + cc * 2 + hi) ^ vsw) << 4));
+  }
+};
 
-  floatx16 o[4][2];
+__device__ __forceinline__ void apply_doc_mask(floatx16 (&s)[2], uint64_t msel, int hi) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb * 32 + key_of_reg(r, hi);
+      if (!((msel >> key) & 1ull)) s[kb][r] = -INFINITY;
+    }
+}
+
+__device__ __forceinline__ void store_out(bf16_t* out, const floatx16 (&o)[4], float l_run, int S, int H, int b,
+                                          int h, int qr, int hi) {
+  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qr >= S) return;
+  bf16_t* dst = out + ((long)b * S + qr) * (H * HD) + h * HD + 4 * hi;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][qb][e] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
+      pk[1] = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+      *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * i) = pk;
+    }
+}
 
-  if (n_iter > 0) {
-    gload(tile_of(0));
-    lstore(0);
+// ---------------------------------------------------------------- key norms
+// kmax[2*(b*H + h) + d] = max over rows j < S of document d of |k_j| (fp32
+// from the stored values); one maximum per document, so that the rows of one
+// document never depend on the other's. kmax must be zero on entry.
+__global__ void __launch_bounds__(256) k_key_norm_max(const bf16_t* __restrict__ k, const uint64_t* __restrict__ masks,
+                                                      float* __restrict__ kmax, int S, int stride) {
+  __shared__ float red[2][4];
+  const int bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint64_t mpad = masks[2 * blockIdx.x + 1];
+  float mx[2] = {0.f, 0.f};
+  const int r_end = min(S, (int)(blockIdx.x + 1) * 64);
+  for (int r = blockIdx.x * 64 + wid; r < r_end; r += 4) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(k + ((long)bh * stride + r) * HD + 2 * lane);
+    const float a = __uint_as_float(u << 16), c = __uint_as_float(u & 0xffff0000u);
+    const float n2 = wave_sum(a * a + c * c);
+    const int d = (int)((mpad >> (r & 63)) & 1ull);
+    mx[d] = fmaxf(mx[d], n2);
+  }
+  if (lane == 0) {
+    red[0][wid] = mx[0];
+    red[1][wid] = mx[1];
   }
   __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    const int t = tile_of(it);
-    const int stage = it & 1;
-    if (it + 1 < n_iter) gload(tile_of(it + 1));
+  if (threadIdx.x < 2) {
+    const int d = threadIdx.x;
+    const float m = sqrtf(fmaxf(fmaxf(red[d][0], red[d][1]), fmaxf(red[d][2], red[d][3])));
+    atomicMax(reinterpret_cast<int*>(kmax + 2 * bh + d), __float_as_int(m));  // non-negative floats order as ints
+  }
+}
 
+__global__ void k_zero_f32(float* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------- fixed-reference kernel
+__global__ void __launch_bounds__(kNW * 64, 1)
+    k_attn_fixed(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
+                 bf16_t* __restrict__ out, const uint64_t* __restrict__ masks, const int32_t* __restrict__ list_real,
+                 const int32_t* __restrict__ list_pad, const int32_t* __restrict__ meta,
+                 const float* __restrict__ kmax, int32_t* __restrict__ wg_flag, int S, int H, int stride,
+                 float c_log2, int n_qt, int total) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TileWalk::STAGE];
+  __shared__ int s_big;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const WgPos wp = wg_pos(n_qt, total);
+  const int h = wp.bh % H, b = wp.bh / H;
+  const int qw0 = wp.qt * kQG + wid * 32;
+  const int qr = qw0 + l32;
+
+  // ---- q scaled by scale*log2(e), rounded to bf16; its norm gives the reference
+  bf16x8 qf[8];
+  float qsq = 0.f;
+  {
+    const int qc = qr < stride ? qr : stride - 1;
+    const bf16_t* src = q + ((long)wp.bh * stride + qc) * HD + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 16 * kk);
+      bf16x8 v;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const __bf16 a = (__bf16)(__uint_as_float(raw[w] << 16) * c_log2);
+        const __bf16 c = (__bf16)(__uint_as_float(raw[w] & 0xffff0000u) * c_log2);
+        v[2 * w] = a;
+        v[2 * w + 1] = c;
+        const float fa = (float)a, fc = (float)c;
+        qsq += fa * fa + fc * fc;
+      }
+      qf[kk] = v;
+    }
+  }
+  qsq += __shfl_xor(qsq, 32, 64);
+  const int qd = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
+  const float mref = sqrtf(qsq) * kmax[2 * wp.bh + qd] * 1.001f + 1e-6f;
+  if (tid == 0) s_big = 0;
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(qr < S && !(mref <= kMaxRef)) && lane == 0) atomicOr(&s_big, 1);
+  __syncthreads();
+  if (s_big) {
+    if (tid == 0) wg_flag[wp.pid] = 1;  // left to the running-max kernel
+    return;
+  }
+  if (tid == 0) wg_flag[wp.pid] = 0;
+
+  TileWalk tw;
+  tw.init(k, vt, masks, list_real, list_pad, meta, S, stride, wp.qt, wp.bh, qw0, qr);
+  const Frag fr(l32);
+
+  floatx16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float l_run = 0.f;
+
+  if (tw.n_iter > 0) {
+    tw.gload(tw.tile(0));
+    tw.lstore(lds);
+  }
+  __syncthreads();
+  for (int it = 0; it < tw.n_iter; ++it) {
+    const int t = tw.tile(it);
+    const uint8_t* Ks = lds + (it & 1) * TileWalk::STAGE;
+    const uint8_t* Vs = Ks + TileWalk::KT_BYTES;
+    if (it + 1 < tw.n_iter) tw.gload(tw.tile(it + 1));
+
+    // ---- S^T - m = K (c q)^T - m
+    floatx16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = -mref;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(Ks, kb, kk, hi), qf[kk], s[kb], 0, 0, 0);
+
+    // ---- document mask, unless the tile lies wholly in the wave's only document
     const uint64_t mreal = masks[2 * t], mpad = masks[2 * t + 1];
-    const bool need = (wq_real && mreal) || (wq_pad && mpad);
+    const bool clean = (tw.wq_real && !tw.wq_pad && mreal == ~0ull) || (tw.wq_pad && !tw.wq_real && mpad == ~0ull);
+    if (!clean) apply_doc_mask(s, tw.qdoc ? mpad : mreal, hi);
+
+    // ---- P = exp2(S - m) in bf16, row sums in fp32
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        bf16x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(s[kb][8 * cc + e]);
+          l_run += p;
+          pv[e] = (__bf16)p;
+        }
+        pf[kb][cc] = pv;
+      }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vs, db, kb, cc, l32, hi), pf[kb][cc], o[db], 0, 0, 0);
+
+    if (it + 1 < tw.n_iter) tw.lstore(lds + ((it + 1) & 1) * TileWalk::STAGE);
+    __syncthreads();
+  }
+  store_out(out, o, l_run, S, H, b, h, qr, hi);
+}
+
+// ---------------------------------------------------------------- running-max kernel
+// Handles the workgroups the fixed-reference kernel flagged (all of them
+// when wg_flag is null).
+__global__ void __launch_bounds__(kNW * 64, 1)
+    k_attn_running(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
+                   bf16_t* __restrict__ out, const uint64_t* __restrict__ masks,
+                   const int32_t* __restrict__ list_real, const int32_t* __restrict__ list_pad,
+                   const int32_t* __restrict__ meta, const int32_t* __restrict__ wg_flag, int S, int H, int stride,
+                   float c_log2, int n_qt, int total) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TileWalk::STAGE];
+  const WgPos wp = wg_pos(n_qt, total);
+  if (wg_flag && wg_flag[wp.pid] == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int h = wp.bh % H, b = wp.bh / H;
+  const int qw0 = wp.qt * kQG + wid * 32;
+  const int qr = qw0 + l32;
+
+  bf16x8 qf[8];
+  {
+    const int qc = qr < stride ? qr : stride - 1;
+    const bf16_t* src = q + ((long)wp.bh * stride + qc) * HD + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
+  }
+  TileWalk tw;
+  tw.init(k, vt, masks, list_real, list_pad, meta, S, stride, wp.qt, wp.bh, qw0, qr);
+  const Frag fr(l32);
+
+  floatx16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (tw.n_iter > 0) {
+    tw.gload(tw.tile(0));
+    tw.lstore(lds);
+  }
+  __syncthreads();
+  for (int it = 0; it < tw.n_iter; ++it) {
+    const int t = tw.tile(it);
+    const uint8_t* Ks = lds + (it & 1) * TileWalk::STAGE;
+    const uint8_t* Vs = Ks + TileWalk::KT_BYTES;
+    if (it + 1 < tw.n_iter) tw.gload(tw.tile(it + 1));
+    const uint64_t mreal = masks[2 * t], mpad = masks[2 * t + 1];
+    const bool need = (tw.wq_real && mreal) || (tw.wq_pad && mpad);
     if (need) {
-      const uint8_t* Ks = lds + stage * STAGE;
-      const uint8_t* Vs = Ks + KT_BYTES;
-      // ---- S^T = K Q^T
-      floatx16 s[2][2];
+      floatx16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + krow;
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + row * 256 + (((2 * kk + hi) ^ kfk) << 4));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][kk], s[kb][qb], 0, 0, 0);
-        }
-      }
-      // ---- document mask (skipped when the tile is entirely in the wave's only document)
-      const bool full_real = wq_real && !wq_pad && mreal == ~0ull;
-      const bool full_pad = wq_pad && !wq_real && mpad == ~0ull;
-      if (!(full_real || full_pad)) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const uint64_t msel = qdoc[qb] ? mpad : mreal;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kb * 32 + key_of_reg(r, hi);
-              if (!((msel >> key) & 1ull)) s[kb][qb][r] = -INFINITY;
-            }
-        }
-      }
-      // ---- online softmax (per lane = per query)
-      bf16x8 pf[2][2][2];  // [kb][qb][cc]
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = -INFINITY;
+      for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(Ks, kb, kk, hi), qf[kk], s[kb], 0, 0, 0);
+      const bool clean =
+          (tw.wq_real && !tw.wq_pad && mreal == ~0ull) || (tw.wq_pad && !tw.wq_real && mpad == ~0ull);
+      if (!clean) apply_doc_mask(s, tw.qdoc ? mpad : mreal, hi);
+      float mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[qb], mx * c_log2);
-        const float base = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[qb] - base);
-        float ls = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            bf16x8 pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float p = fast_exp2(fmaf(s[kb][qb][8 * cc + e], c_log2, -base));
-              ls += p;
-              pv[e] = (__bf16)p;
-            }
-            pf[kb][qb][cc] = pv;
-          }
-        l_run[qb] = l_run[qb] * alpha + ls;
-        m_run[qb] = m_new;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][qb][e] *= alpha;
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        m_run = m_new;
       }
-      // ---- O^T += V^T P^T
+      const float base = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = fast_exp2(fmaf(s[kb][8 * cc + e], c_log2, -base));
+            l_run += p;
+            pv[e] = (__bf16)p;
+          }
+          pf[kb][cc] = pv;
+        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int row = db * 32 + l32;
-            const int chunk = kb * 4 + cc * 2 + hi;
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + row * 128 + ((chunk ^ vsw) << 4));
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][qb][cc], o[db][qb], 0, 0, 0);
-          }
+          for (int db = 0; db < 4; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vs, db, kb, cc, l32, hi), pf[kb][cc], o[db], 0, 0, 0);
     }
-    if (it + 1 < n_iter) lstore(stage ^ 1);
+    if (it + 1 < tw.n_iter) tw.lstore(lds + ((it + 1) & 1) * TileWalk::STAGE);
     __syncthreads();
   }
-
-  // ---- normalise and store: lane holds query l32 of block qb, dims db*32 + 8i + 4hi + j
-  const int W = H * HD;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int qr = qw0 + qb * 32 + l32;
-    if (qr >= S) continue;
-    bf16_t* dst = out + ((long)b * S + qr) * W + h * HD + 4 * hi;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(o[db][qb][4 * i] * inv, o[db][qb][4 * i + 1] * inv);
-        pk[1] = pack_bf16x2(o[db][qb][4 * i + 2] * inv, o[db][qb][4 * i + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * i) = pk;
-      }
-  }
+  store_out(out, o, l_run, S, H, b, h, qr, hi);
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -313,7 +484,6 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float* __restrict__ q, co
                                                  const float* __restrict__ vt, float* __restrict__ out,
                                                  const uint64_t* __restrict__ masks, int S, int H, int stride,
                                                  float scale) {
-  constexpr int HD = 128;
   __shared__ float Ks[kKV][HD + 1];
   __shared__ float Vs[HD][kKV + 1];
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -358,31 +528,41 @@ __global__ void __launch_bounds__(64) k_attn_f32(const float* __restrict__ q, co
   }
 }
 
+// ---------------------------------------------------------------- launchers
+
+size_t attention_scratch_bytes(int B, int S, int H) {
+  const size_t n_qt = (size_t)(S + kQG - 1) / kQG;
+  return 8 * (size_t)B * H + 4 * n_qt * H * B;  // kmax per document + workgroup flags
+}
+
 template <>
 hipError_t launch_attention<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* out,
-                                    const int32_t* tags, const uint64_t* masks, const int32_t* list_real,
-                                    const int32_t* list_pad, const int32_t* meta, int B, int S, int H, int stride,
-                                    float scale, int assume_padless, hipStream_t st) {
-  (void)tags;
-  (void)assume_padless;
-  const int n_qt = (S + kAttnQ - 1) / kAttnQ;
+                                    const uint64_t* masks, const int32_t* list_real, const int32_t* list_pad,
+                                    const int32_t* meta, void* scratch, int B, int S, int H, int stride, float scale,
+                                    hipStream_t st) {
+  const int n_qt = (S + kQG - 1) / kQG;
   const int total = n_qt * H * B;
   const float c_log2 = scale * 1.4426950408889634f;
-  k_attn_bf16<<<total, 256, 0, st>>>(q, k, vt, out, masks, list_real, list_pad, meta, S, H, stride, c_log2, n_qt,
-                                      total);
+  float* kmax = reinterpret_cast<float*>(scratch);
+  int32_t* flags = reinterpret_cast<int32_t*>(kmax + 2 * B * H);
+  k_zero_f32<<<(2 * B * H + 255) / 256, 256, 0, st>>>(kmax, 2 * B * H);
+  k_key_norm_max<<<dim3((unsigned)((S + 63) / 64), (unsigned)(B * H)), 256, 0, st>>>(k, masks, kmax, S, stride);
+  k_attn_fixed<<<total, kNW * 64, 0, st>>>(q, k, vt, out, masks, list_real, list_pad, meta, kmax, flags, S, H,
+                                            stride, c_log2, n_qt, total);
+  k_attn_running<<<total, kNW * 64, 0, st>>>(q, k, vt, out, masks, list_real, list_pad, meta, flags, S, H, stride,
+                                              c_log2, n_qt, total);
   return hipGetLastError();
 }
 
 template <>
-hipError_t launch_attention<float>(const float* q, const float* k, const float* vt, float* out, const int32_t* tags,
+hipError_t launch_attention<float>(const float* q, const float* k, const float* vt, float* out,
                                    const uint64_t* masks, const int32_t* list_real, const int32_t* list_pad,
-                                   const int32_t* meta, int B, int S, int H, int stride, float scale,
-                                   int assume_padless, hipStream_t st) {
-  (void)tags;
+                                   const int32_t* meta, void* scratch, int B, int S, int H, int stride, float scale,
+                                   hipStream_t st) {
   (void)list_real;
   (void)list_pad;
   (void)meta;
-  (void)assume_padless;
+  (void)scratch;
   dim3 grid((unsigned)((S + 63) / 64), (unsigned)H, (unsigned)B);
   k_attn_f32<<<grid, 64, 0, st>>>(q, k, vt, out, masks, S, H, stride, scale);
   return hipGetLastError();

@@ -61,9 +61,12 @@ hipError_t launch_gemm(int epi, const T* A, const T* W, T* C, int M, int N, int 
                        hipStream_t st);
 
 // ---- attention ----
+// scratch: attention_scratch_bytes(B, S, H) bytes (per-head key-norm maxima
+// and per-workgroup flags).
+size_t attention_scratch_bytes(int B, int S, int H);
 template <typename T>
-hipError_t launch_attention(const T* q, const T* k, const T* vt, T* out, const int32_t* tags, const uint64_t* masks,
-                            const int32_t* list_real, const int32_t* list_pad, const int32_t* meta, int B, int S,
-                            int H, int stride, float scale, int assume_padless, hipStream_t st);
+hipError_t launch_attention(const T* q, const T* k, const T* vt, T* out, const uint64_t* masks,
+                            const int32_t* list_real, const int32_t* list_pad, const int32_t* meta, void* scratch,
+                            int B, int S, int H, int stride, float scale, hipStream_t st);
 
 }  // namespace minih3

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libminih3.so")
+LIB_PATH = os.environ.get("MINIH3_LIBRARY") or os.path.join(HERE, "libminih3.so")
 
 BF16, F32 = 0, 1
 VALIDATE, ASSUME_PADLESS, PROFILE = 1, 2, 4
@@ -83,7 +83,8 @@ def lib() -> ctypes.CDLL:
         L.minih3_kernel_name.argtypes = [ctypes.c_int32]
         L.minih3_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_size_t)]
-        L.minih3_attention_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_attention_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
         L.minih3_block_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
                                            ctypes.POINTER(_BlockWeights), ctypes.c_int32, _P, _P, _P,
                                            ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
@@ -209,9 +210,10 @@ def workspace_bytes(cfg: Config, batch: int, seq_len: int) -> int:
     return int(n.value)
 
 
-def attention_workspace_bytes(seq_len: int) -> int:
+def attention_workspace_bytes(cfg: Config, batch: int, seq_len: int) -> int:
     n = ctypes.c_size_t(0)
-    _check(lib().minih3_attention_workspace_bytes(seq_len, ctypes.byref(n)), "attention_workspace_bytes")
+    _check(lib().minih3_attention_workspace_bytes(ctypes.byref(cfg), batch, seq_len, ctypes.byref(n)),
+           "attention_workspace_bytes")
     return int(n.value)
 
 
@@ -258,7 +260,7 @@ def attention_packed(cfg: Config, layout: DeviceLayout, q: torch.Tensor, k: torc
         out = torch.empty(B, S, H * hd, dtype=dt, device=q.device)
     _req(out, dt, "out", B * S * H * hd)
     if workspace is None:
-        workspace = alloc_workspace(attention_workspace_bytes(S), q.device)
+        workspace = alloc_workspace(attention_workspace_bytes(cfg, B, S), q.device)
     L = layout.c()
     s = lib().minih3_attention_packed(ctypes.byref(cfg), ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v_t), stride,
                                       _ptr(out), float(softmax_scale), _ptr(workspace), workspace.numel(), flags,

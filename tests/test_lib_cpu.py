@@ -38,7 +38,7 @@ def test_host_side_queries_and_argument_errors():
     nbytes = m.workspace_bytes(cfg, 1, 32768)
     # the workspace holds at least the qkv, q/k/v^T and attention buffers in bf16
     assert nbytes > 32768 * (3 * 7168 + 3 * 7168 + 7168) * 2
-    assert m.attention_workspace_bytes(100) >= 16 * 2
+    assert m.attention_workspace_bytes(cfg, 1, 100) >= 16 * 2
     lib = m.lib()
     bad = m.Config(**{f: getattr(cfg, f) for f, _ in m.Config._fields_})
     bad.head_dim = 64
