@@ -18,19 +18,17 @@
 //     per-lane. Key rows enter the MFMA in an order (bits 2 and 3 of the row
 //     swapped) that makes the score registers exactly the B operand of
 //     O^T += V^T P^T: P never leaves registers;
-//   * fixed-reference softmax: for query i the exponent reference is
-//     m_i = |q_i| * max_j |k_j| over the keys of the query's document
-//     (scale * log2(e) folded into q), an upper bound of every score of the
-//     row (Cauchy-Schwarz). Probabilities
-//     exp2(s - m_i) are <= 1, so the row needs no running max and the O
-//     accumulators are never rescaled; the score accumulators start at -m_i
-//     so that exp2 reads the MFMA result directly. The bound is used only
-//     when m_i <= 55, so that every probability of the row that matters
-//     stays far above the fp32 / bf16 underflow (>= 2^-110); a workgroup
-//     holding a query with a larger bound leaves its tile to a second kernel
-//     with the classic running max (rescaled lazily, when the max grows by
-//     more than 2^8). After per-head q/k RMSNorm the bound is small, so the
-//     second kernel only exits early;
+//   * bounded-score softmax: with scale * log2(e) folded into q, every score
+//     s_ij of query i obeys |s_ij| <= B_i = |q_i| * max_j |k_j| over the keys
+//     of the query's document (Cauchy-Schwarz). When B_i <= 64, exp2(s_ij)
+//     lies in [2^-64, 2^64] and the row sums stay far below the fp32 / bf16
+//     overflow, so the probabilities need no reference at all: the common
+//     factor 2^-m of the usual max-shifted softmax cancels between O and the
+//     row sum. The row needs no running max and O is never rescaled. A
+//     workgroup holding a query with a larger bound leaves its tile to a
+//     second kernel with the classic running max (rescaled lazily, when the
+//     max grows by more than 2^8). After per-head q/k RMSNorm the bound is
+//     about 16, so the second kernel only exits early;
 //   * document masks per 64-key tile (non-padding / padding bit masks built
 //     once per call): workgroups whose queries all sit in one document walk
 //     only the tiles holding keys of that document; fully-matching tiles
@@ -47,15 +45,21 @@ constexpr int kNW = 8;      // waves per workgroup
 constexpr int kQG = kNW * 32;  // queries per workgroup
 constexpr int HD = 128;
 constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
-constexpr float kMaxRef = 55.f;  // largest fixed reference (log2 units)
+constexpr float kMaxRef = 64.f;  // largest score bound of the fixed-reference kernel (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// key index inside a 32-key block held by accumulator register r of lane half hi
-__device__ __forceinline__ int key_of_reg(int r, int hi) {
-  const int i = r >> 2, j = r & 3;
-  return 16 * (i >> 1) + 8 * hi + 4 * (i & 1) + j;
+// LDS swizzles. A ds_read_b128 is served 16 lanes at a time across 64
+// banks (256 bytes), so the 16 lanes that read together must hit 16
+// different 16-byte bank groups.
+//   K tile, 256-byte rows: lanes read rows sigma(0..15) at one logical chunk;
+//   the physical chunk is the logical one XOR (row with bits 2 and 3 swapped).
+//   V^T tile, 128-byte rows: lanes read 16 consecutive rows at one chunk;
+//   the physical chunk is the logical one XOR ((row >> 1) & 7).
+__device__ __forceinline__ int kswz(int row) {
+  return (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
 }
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
 
 // Workgroup -> (query tile, b*H + h) with XCD-contiguous ranges.
 struct WgPos {
@@ -130,10 +134,9 @@ struct TileWalk {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int kr = kr0 + (NT / 16) * i;
-      const int fk = (kr & 3) | (((kr >> 3) & 1) << 2);
-      k_st[i] = kr * 256 + ((kc ^ fk) << 4);
+      k_st[i] = kr * 256 + ((kc ^ kswz(kr)) << 4);
       const int vr = vr0 + (NT / 8) * i;
-      v_st[i] = KT_BYTES + vr * 128 + ((vc ^ (vr & 7)) << 4);
+      v_st[i] = KT_BYTES + vr * 128 + ((vc ^ vswz(vr)) << 4);
     }
   }
   __device__ __forceinline__ int tile(int it) const { return list ? list[it] : it; }
@@ -167,6 +170,40 @@ struct TileWalk {
       *reinterpret_cast<u32x4*>(base + v_st[i]) = rv[i];
     }
   }
+  // K and V^T staged separately (K one tile ahead of V): buffers of
+  // KT_BYTES each; the V^T offsets drop their KT_BYTES bias.
+  __device__ __forceinline__ void gload_k(int t) {
+    const long key0 = (long)t * kKV;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) rk[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + (NT / 16) * i) * HD);
+  }
+  __device__ __forceinline__ void gload_v(int t) {
+    const long key0 = (long)t * kKV;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) rv[i] = *reinterpret_cast<const u32x4*>(vbase + (long)((NT / 8) * i) * stride + key0);
+    if (key0 + kKV > S) {
+      const int first = (int)(S - key0) - vc * 8;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int e0 = 2 * w;
+          uint32_t x = rv[i][w];
+          if (e0 >= first) x &= 0xffff0000u;
+          if (e0 + 1 >= first) x &= 0x0000ffffu;
+          rv[i][w] = x;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void lstore_k(uint8_t* kbuf) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(kbuf + k_st[i]) = rk[i];
+  }
+  __device__ __forceinline__ void lstore_v(uint8_t* vbuf) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(vbuf + v_st[i] - KT_BYTES) = rv[i];
+  }
 };
 
 // Fragment-read offsets inside a staged tile.
@@ -176,8 +213,8 @@ struct Frag {
   int krow, kfk, vsw;
   __device__ __forceinline__ Frag(int l32) {
     krow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // bits 2 and 3 swapped
-    kfk = (krow & 3) | (((krow >> 3) & 1) << 2);
-    vsw = l32 & 7;
+    kfk = kswz(krow);
+    vsw = vswz(l32);
   }
   __device__ __forceinline__ bf16x8 k(const uint8_t* Ks, int kb, int kk, int hi) const {
     return *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + krow) * 256 + (((2 * kk + hi) ^ kfk) << 4));
@@ -187,14 +224,19 @@ struct Frag {
   }
 };
 
+// Sets the scores of keys outside the allowed set msel (bit j = key j of
+// the tile) to -inf. For block kb and lane half hi the 16 registers hold
+// keys kb*32 + 8hi + {0..7, 16..23}: register r < 8 is key bit r, r >= 8 is
+// bit r + 8 of msel >> (kb*32 + 8hi).
 __device__ __forceinline__ void apply_doc_mask(floatx16 (&s)[2], uint64_t msel, int hi) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    const uint32_t m32 = (uint32_t)(msel >> (kb * 32 + 8 * hi));
+    const uint32_t b16 = (m32 & 0xffu) | ((m32 >> 8) & 0xff00u);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb * 32 + key_of_reg(r, hi);
-      if (!((msel >> key) & 1ull)) s[kb][r] = -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r)
+      if (!((b16 >> r) & 1u)) s[kb][r] = -INFINITY;
+  }
 }
 
 __device__ __forceinline__ void store_out(bf16_t* out, const floatx16 (&o)[4], float l_run, int S, int H, int b,
@@ -251,13 +293,56 @@ __global__ void k_zero_f32(float* p, int n) {
 }
 
 // ---------------------------------------------------------------- fixed-reference kernel
+// Software-pipelined: while the VALU turns the scores of tile j into
+// probabilities, the MFMA unit already multiplies K of tile j+1. K is
+// staged in LDS one tile ahead of V^T (buffers K0, K1, V0, V1). Each step
+// runs in four quarters: four score MFMAs of tile j+1, the exponentials of
+// 16 keys of tile j, and the four O^T MFMAs that consume them.
+struct FixedCtx {
+  const Frag* fr;
+  const bf16x8* qf;
+  bf16x2 ones2;
+  int l32, hi;
+};
+
+__device__ __forceinline__ void scores_full(floatx16 (&s)[2], const uint8_t* Ks, const FixedCtx& c) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fr->k(Ks, kb, 0, c.hi), c.qf[0], floatx16{}, 0, 0, 0);
+#pragma unroll
+  for (int kk = 1; kk < 8; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fr->k(Ks, kb, kk, c.hi), c.qf[kk], s[kb], 0, 0, 0);
+}
+
+// probabilities of keys 16*qq .. 16*qq+15 of a tile (block kb = qq>>1, half cc = qq&1), then O^T += V^T P^T
+__device__ __forceinline__ void prob_quarter(const floatx16 (&cur)[2], int qq, floatx16 (&o)[4], float (&lsum)[4],
+                                             const uint8_t* Vs, const FixedCtx& c) {
+  const int kb = qq >> 1, cc = qq & 1;
+  bf16x8 pv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pv[e] = (__bf16)fast_exp2(cur[kb][8 * cc + e]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bf16x2 pair;
+    pair[0] = pv[2 * e];
+    pair[1] = pv[2 * e + 1];
+    lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, c.ones2, lsum[e], false);
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fr->v(Vs, db, kb, cc, c.l32, c.hi), pv, o[db], 0, 0, 0);
+}
+
 __global__ void __launch_bounds__(kNW * 64, 1)
     k_attn_fixed(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
                  bf16_t* __restrict__ out, const uint64_t* __restrict__ masks, const int32_t* __restrict__ list_real,
                  const int32_t* __restrict__ list_pad, const int32_t* __restrict__ meta,
                  const float* __restrict__ kmax, int32_t* __restrict__ wg_flag, int S, int H, int stride,
                  float c_log2, int n_qt, int total) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TileWalk::STAGE];
+  constexpr int KB = TileWalk::KT_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * KB];  // K0 K1 V0 V1
   __shared__ int s_big;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -290,10 +375,10 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   }
   qsq += __shfl_xor(qsq, 32, 64);
   const int qd = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
-  const float mref = sqrtf(qsq) * kmax[2 * wp.bh + qd] * 1.001f + 1e-6f;
+  const float bound = sqrtf(qsq) * kmax[2 * wp.bh + qd] * 1.001f + 1e-6f;
   if (tid == 0) s_big = 0;
   __syncthreads();
-  if (__builtin_amdgcn_ballot_w64(qr < S && !(mref <= kMaxRef)) && lane == 0) atomicOr(&s_big, 1);
+  if (__builtin_amdgcn_ballot_w64(qr < S && !(bound <= kMaxRef)) && lane == 0) atomicOr(&s_big, 1);
   __syncthreads();
   if (s_big) {
     if (tid == 0) wg_flag[wp.pid] = 1;  // left to the running-max kernel
@@ -304,70 +389,85 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   TileWalk tw;
   tw.init(k, vt, masks, list_real, list_pad, meta, S, stride, wp.qt, wp.bh, qw0, qr);
   const Frag fr(l32);
+  const int n = tw.n_iter;
+
+  FixedCtx c;
+  c.fr = &fr;
+  c.qf = qf;
+  c.ones2[0] = (__bf16)1.f;
+  c.ones2[1] = (__bf16)1.f;
+  c.l32 = l32;
+  c.hi = hi;
 
   floatx16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float l_run = 0.f;
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-  if (tw.n_iter > 0) {
-    tw.gload(tw.tile(0));
-    tw.lstore(lds);
-  }
-  __syncthreads();
-  for (int it = 0; it < tw.n_iter; ++it) {
-    const int t = tw.tile(it);
-    const uint8_t* Ks = lds + (it & 1) * TileWalk::STAGE;
-    const uint8_t* Vs = Ks + TileWalk::KT_BYTES;
-    if (it + 1 < tw.n_iter) tw.gload(tw.tile(it + 1));
-
-    // ---- S^T - m = K (c q)^T - m
-    floatx16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = -mref;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(Ks, kb, kk, hi), qf[kk], s[kb], 0, 0, 0);
-
-    // ---- document mask, unless the tile lies wholly in the wave's only document
+  auto mask_tile = [&](floatx16(&sc)[2], int t) {
     const uint64_t mreal = masks[2 * t], mpad = masks[2 * t + 1];
     const bool clean = (tw.wq_real && !tw.wq_pad && mreal == ~0ull) || (tw.wq_pad && !tw.wq_real && mpad == ~0ull);
-    if (!clean) apply_doc_mask(s, tw.qdoc ? mpad : mreal, hi);
-
-    // ---- P = exp2(S - m) in bf16, row sums in fp32
-    bf16x8 pf[2][2];
+    if (!clean) apply_doc_mask(sc, tw.qdoc ? mpad : mreal, hi);
+  };
+  // one pipelined step: scores of tile it+1 into nxt, probabilities and O^T of tile it from cur
+  auto step = [&](int it, floatx16(&cur)[2], floatx16(&nxt)[2]) {
+    const int t1 = tw.tile(it + 1);
+    tw.gload_k(tw.tile(it + 2 < n ? it + 2 : n - 1));  // the repeat at the end is never read
+    tw.gload_v(t1);
+    const uint8_t* Kn = lds + ((it + 1) & 1) * KB;
+    const uint8_t* Vc = lds + 2 * KB + (it & 1) * KB;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qq = 0; qq < 4; ++qq) {
+      const int kb = qq >> 1, k0 = (qq & 1) * 4;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        bf16x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(s[kb][8 * cc + e]);
-          l_run += p;
-          pv[e] = (__bf16)p;
-        }
-        pf[kb][cc] = pv;
+      for (int j = 0; j < 4; ++j) {
+        const int kk = k0 + j;
+        nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(Kn, kb, kk, hi), qf[kk], kk == 0 ? floatx16{} : nxt[kb],
+                                                          0, 0, 0);
       }
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vs, db, kb, cc, l32, hi), pf[kb][cc], o[db], 0, 0, 0);
-
-    if (it + 1 < tw.n_iter) tw.lstore(lds + ((it + 1) & 1) * TileWalk::STAGE);
+      prob_quarter(cur, qq, o, lsum, Vc, c);
+    }
+    mask_tile(nxt, t1);
+    tw.lstore_k(lds + (it & 1) * KB);
+    tw.lstore_v(lds + 2 * KB + ((it + 1) & 1) * KB);
     __syncthreads();
+  };
+  auto last = [&](int it, floatx16(&cur)[2]) {
+    const uint8_t* Vc = lds + 2 * KB + (it & 1) * KB;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) prob_quarter(cur, qq, o, lsum, Vc, c);
+  };
+
+  if (n > 0) {
+    // ---- prologue: K0 = K(0), V0 = V(0), K1 = K(1); scores of tile 0
+    const int t0 = tw.tile(0);
+    tw.gload_k(t0);
+    tw.gload_v(t0);
+    tw.lstore_k(lds);
+    tw.lstore_v(lds + 2 * KB);
+    if (n > 1) {
+      tw.gload_k(tw.tile(1));
+      tw.lstore_k(lds + KB);
+    }
+    __syncthreads();
+    floatx16 sa[2], sb[2];
+    scores_full(sa, lds, c);
+    mask_tile(sa, t0);
+    int it = 0;
+    for (; it + 2 < n; it += 2) {
+      step(it, sa, sb);
+      step(it + 1, sb, sa);
+    }
+    if (it + 1 < n) {
+      step(it, sa, sb);
+      last(it + 1, sb);
+    } else {
+      last(it, sa);
+    }
   }
-  store_out(out, o, l_run, S, H, b, h, qr, hi);
+  store_out(out, o, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]), S, H, b, h, qr, hi);
 }
 
 // ---------------------------------------------------------------- running-max kernel

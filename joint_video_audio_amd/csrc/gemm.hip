@@ -13,8 +13,10 @@
 //
 // bf16 kernel (gfx950): 256x256 output tile per workgroup of 4 waves, each
 // wave 128x128 as 4x4 v_mfma_f32_32x32x16_bf16 tiles; K step 64 staged in
-// LDS (2 stages, 128 KiB, XOR-swizzled 16-byte chunks so fragment reads and
-// tile stores are bank-conflict free); global loads of step k+1 are in
+// LDS (2 stages, 128 KiB). Rows are 128 bytes; the 16-byte chunk c of row r
+// sits at c ^ ((r >> 1) & 7), so the 16 lanes a ds_read_b128 serves together
+// (16 consecutive rows, one chunk) hit 16 different bank groups of the 64
+// banks, and so do tile stores (2 rows x 8 chunks); global loads of step k+1 are in
 // flight while step k is multiplied. Tiles are ordered so that the
 // workgroups an XCD runs together share A and W panels in its L2.
 #include "common.h"
@@ -107,7 +109,7 @@ __global__ void __launch_bounds__(256, 1)
   // ---- global -> LDS mapping: thread owns chunk column (tid & 7) of rows (tid >> 3) + 32 i
   const int ck = tid & 7;
   const int r0 = tid >> 3;
-  const int swz = ck ^ (r0 & 7);
+  const int swz = ck ^ ((r0 >> 1) & 7);  // rows r0 + 32 i share (row >> 1) & 7
   const bf16_t* a_src[8];
   const bf16_t* w_src[8];
 #pragma unroll
@@ -154,7 +156,7 @@ __global__ void __launch_bounds__(256, 1)
   };
 
   // fragment read offsets: row (lane & 31) of a 32-row block, chunk 2kk + (lane >> 5)
-  const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = lane & 7;
+  const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = (fr_row >> 1) & 7;
 
   const int KT = K / BK;
   gload(0);
