@@ -11,8 +11,8 @@
 //                    a padding row keeps resid unchanged)
 //   kEpiSwiGLU     : W rows [0,F) gate, [F,2F) up; C[:, f] = silu(g_f) * u_f
 //
-// bf16 kernel (gfx950): 256x256 output tile per workgroup of 4 waves, each
-// wave 128x128 as 4x4 v_mfma_f32_32x32x16_bf16 tiles; K step 64 staged in
+// bf16 kernel (gfx950): 256x256 output tile per workgroup of 8 waves (two per
+// SIMD), each wave 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 tiles; K step 64 staged in
 // LDS (2 stages, 128 KiB). Rows are 128 bytes; the 16-byte chunk c of row r
 // sits at c ^ ((r >> 1) & 7), so the 16 lanes a ds_read_b128 serves together
 // (16 consecutive rows, one chunk) hit 16 different bank groups of the 64
@@ -81,14 +81,20 @@ __device__ __forceinline__ void epi_gated(T* C, int ldc, int m, int n, const flo
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KiB
 
-template <int EPI>
-__global__ void __launch_bounds__(256, 1)
+// WGM x WGN waves; each wave owns a (256/WGM) x (256/WGN) block of the tile.
+template <int EPI, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1)
     k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, int M, int N,
                 int K, EpiArgs ea) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  constexpr int MI = WTM / 32, NI = WTN / 32;    // 32x32 MFMA blocks per wave
+  constexpr int LPT = BM * 8 / NT;               // 16-byte chunks per thread per operand and K step
+  constexpr int RSTEP = NT / 8;                  // row step between a thread's chunks
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid & 1, wn = wid >> 1;
+  const int wm = wid % WGM, wn = wid / WGM;
 
   // ---- tile order: XCD-contiguous ranges, then groups of 8 M-tiles
   const int MT = (M + BM - 1) / BM, NTL = N / BN;
@@ -106,41 +112,42 @@ __global__ void __launch_bounds__(256, 1)
   const int tn = (pid % npg) / gsz;
   const int m0 = tm * BM;
 
-  // ---- global -> LDS mapping: thread owns chunk column (tid & 7) of rows (tid >> 3) + 32 i
+  // ---- global -> LDS mapping: thread owns chunk column (tid & 7) of rows (tid >> 3) + RSTEP i
   const int ck = tid & 7;
   const int r0 = tid >> 3;
-  const int swz = ck ^ ((r0 >> 1) & 7);  // rows r0 + 32 i share (row >> 1) & 7
-  const bf16_t* a_src[8];
-  const bf16_t* w_src[8];
+  const int swz = ck ^ ((r0 >> 1) & 7);  // rows r0 + RSTEP i share (row >> 1) & 7
+  const bf16_t* a_src[LPT];
+  const bf16_t* w_src[LPT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int row = r0 + 32 * i;
+  for (int i = 0; i < LPT; ++i) {
+    const int row = r0 + RSTEP * i;
     int am = m0 + row;
     am = am < M ? am : M - 1;
     a_src[i] = A + (long)am * K + ck * 8;
     int wr;
     if (EPI == kEpiSwiGLU) {
-      const int half = row >> 7, sel = (row & 127) >> 6, o = row & 63;
-      wr = sel * ea.ffn_dim + 128 * tn + 64 * half + o;
+      // wave block of WTN rows: first half gate rows, second half the matching up rows
+      const int wblk = row / WTN, sel = (row % WTN) / (WTN / 2), o = row % (WTN / 2);
+      wr = sel * ea.ffn_dim + 128 * tn + (WTN / 2) * wblk + o;
     } else {
       wr = tn * BN + row;
     }
     w_src[i] = W + (long)wr * K + ck * 8;
   }
-  const int st_off = r0 * 128 + (swz << 4);  // + i * 32 * 128
+  const int st_off = r0 * 128 + (swz << 4);  // + i * RSTEP * 128
 
-  floatx16 acc[4][4];
+  floatx16 acc[MI][NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  u32x4 ra[8], rw[8];
+  u32x4 ra[LPT], rw[LPT];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < LPT; ++i) {
       ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK);
       rw[i] = *reinterpret_cast<const u32x4*>(w_src[i] + kt * BK);
     }
@@ -149,9 +156,9 @@ __global__ void __launch_bounds__(256, 1)
     uint8_t* As = lds + stage * kStageBytes;
     uint8_t* Ws = As + BM * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(As + st_off + i * 32 * 128) = ra[i];
-      *reinterpret_cast<u32x4*>(Ws + st_off + i * 32 * 128) = rw[i];
+    for (int i = 0; i < LPT; ++i) {
+      *reinterpret_cast<u32x4*>(As + st_off + i * RSTEP * 128) = ra[i];
+      *reinterpret_cast<u32x4*>(Ws + st_off + i * RSTEP * 128) = rw[i];
     }
   };
 
@@ -170,17 +177,17 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int chunk = ((2 * kk + fr_hi) ^ fr_sw) << 4;
-      bf16x8 wf[4], af[4];
+      bf16x8 wf[NI], af[MI];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        wf[ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 128 + ni * 32 + fr_row) * 128 + chunk);
+      for (int ni = 0; ni < NI; ++ni)
+        wf[ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * 128 + chunk);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + mi * 32 + fr_row) * 128 + chunk);
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * 128 + chunk);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ni], af[mi], acc[mi][ni], 0, 0, 0);
     }
     if (kt + 1 < KT) lstore(stage ^ 1);
@@ -189,27 +196,27 @@ __global__ void __launch_bounds__(256, 1)
 
   // ---- epilogue: lane holds row m = ... + (lane & 31), columns 8i + 4*(lane>>5) + j
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int m = m0 + wm * 128 + mi * 32 + fr_row;
+  for (int mi = 0; mi < MI; ++mi) {
+    const int m = m0 + wm * WTM + mi * 32 + fr_row;
     if (m >= M) continue;
     if (EPI == kEpiSwiGLU) {
       const int F = ea.ffn_dim;
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NI / 2; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = silu(acc[mi][ni][4 * i + j]) * acc[mi][ni + 2][4 * i + j];
-          const int f = 128 * tn + 64 * wn + ni * 32 + 8 * i + 4 * fr_hi;
+          for (int j = 0; j < 4; ++j) v[j] = silu(acc[mi][ni][4 * i + j]) * acc[mi][ni + NI / 2][4 * i + j];
+          const int f = 128 * tn + (WTN / 2) * wn + ni * 32 + 8 * i + 4 * fr_hi;
           store4<bf16_t>(C + (long)m * F + f, v);
         }
     } else {
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int n = tn * BN + wn * 128 + ni * 32 + 8 * i + 4 * fr_hi;
+          const int n = tn * BN + wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
           float v[4] = {acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1], acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]};
           if (EPI == kEpiGatedResid)
             epi_gated<bf16_t>(C, N, m, n, v, ea);
@@ -283,6 +290,11 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
 
 // ---------------------------------------------------------------- launchers
 
+#ifndef MINIH3_GEMM_WAVES
+#define MINIH3_GEMM_WAVES 8
+#endif
+constexpr int kGemmWGM = 2, kGemmWGN = MINIH3_GEMM_WAVES / 2;
+
 template <>
 hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, bf16_t* C, int M, int N, int K,
                                const EpiArgs& ea, hipStream_t st) {
@@ -290,10 +302,13 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, bf16_t
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
+  constexpr int NT = 64 * kGemmWGM * kGemmWGN;
   switch (epi) {
-    case kEpiStore: k_gemm_bf16<kEpiStore><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
-    case kEpiGatedResid: k_gemm_bf16<kEpiGatedResid><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
-    case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiStore: k_gemm_bf16<kEpiStore, kGemmWGM, kGemmWGN><<<grid, NT, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiGatedResid:
+      k_gemm_bf16<kEpiGatedResid, kGemmWGM, kGemmWGN><<<grid, NT, 0, st>>>(A, W, C, M, N, K, ea);
+      break;
+    case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU, kGemmWGM, kGemmWGN><<<grid, NT, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
