@@ -12,13 +12,12 @@
 //   kEpiSwiGLU     : W rows [0,F) gate, [F,2F) up; C[:, f] = silu(g_f) * u_f
 //
 // bf16 kernel (gfx950): 256x256 output tile per workgroup of 8 waves (two per
-// SIMD), each wave 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 tiles; K step 64 staged in
-// LDS (2 stages, 128 KiB). Rows are 128 bytes; the 16-byte chunk c of row r
-// sits at c ^ ((r >> 1) & 7), so the 16 lanes a ds_read_b128 serves together
-// (16 consecutive rows, one chunk) hit 16 different bank groups of the 64
-// banks, and so do tile stores (2 rows x 8 chunks); global loads of step k+1 are in
-// flight while step k is multiplied. Tiles are ordered so that the
-// workgroups an XCD runs together share A and W panels in its L2.
+// SIMD), each wave 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 tiles. K steps of 32
+// go through a ring of 4 LDS stages (128 KiB) filled by direct global->LDS
+// loads (global_load_lds_dwordx4) three steps ahead, so no registers stage
+// the operands and the load latency hides behind three steps of MFMA work;
+// one barrier per step. Tiles are ordered so that the workgroups an XCD runs
+// together share A and W panels in its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -78,20 +77,49 @@ __device__ __forceinline__ void epi_gated(T* C, int ldc, int m, int n, const flo
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KiB
+constexpr int BM = 256, BN = 256;
+#ifndef MINIH3_GEMM_BK
+#define MINIH3_GEMM_BK 64
+#endif
+#ifndef MINIH3_GEMM_STAGES
+#define MINIH3_GEMM_STAGES 2
+#endif
+constexpr int BK = MINIH3_GEMM_BK;                  // K step (32 or 64)
+constexpr int kStages = MINIH3_GEMM_STAGES;         // LDS ring depth; loads run kStages-1 steps ahead
+constexpr int kRowBytes = BK * 2;                   // one tile row per stage
+constexpr int kCPR = kRowBytes / 16;                // 16-byte chunks per row
+constexpr int kOpBytes = BM * kRowBytes;            // one operand tile per stage
+constexpr int kStageBytes = 2 * kOpBytes;           // A + W
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS");
 
-// WGM x WGN waves; each wave owns a (256/WGM) x (256/WGN) block of the tile.
+// Logical chunk c of tile row r sits at chunk c ^ swz(r): the 16 lanes a
+// ds_read_b128 serves together read 16 consecutive rows at one chunk, and
+// (r * kCPR + physical chunk) mod 16 -- the 16-byte bank group -- is then
+// different for all 16.
+__device__ __forceinline__ int gemm_swz(int r) { return (r / (16 / kCPR)) % kCPR; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+// WGM x WGN waves (two per SIMD); each wave owns a (256/WGM) x (256/WGN)
+// block of the 256x256 tile.
 template <int EPI, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
     k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, int M, int N,
                 int K, EpiArgs ea) {
-  constexpr int NT = 64 * WGM * WGN;
+  constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int MI = WTM / 32, NI = WTN / 32;    // 32x32 MFMA blocks per wave
-  constexpr int LPT = BM * 8 / NT;               // 16-byte chunks per thread per operand and K step
-  constexpr int RSTEP = NT / 8;                  // row step between a thread's chunks
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+  constexpr int INSTS = 2 * kOpBytes / 1024;     // 1 KiB LDS-DMA wave instructions per stage (A then W)
+  constexpr int IPW = INSTS / NW;                // ... per wave
+  static_assert(INSTS % NW == 0, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid % WGM, wn = wid / WGM;
@@ -112,29 +140,41 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   const int tn = (pid % npg) / gsz;
   const int m0 = tm * BM;
 
-  // ---- global -> LDS mapping: thread owns chunk column (tid & 7) of rows (tid >> 3) + RSTEP i
-  const int ck = tid & 7;
-  const int r0 = tid >> 3;
-  const int swz = ck ^ ((r0 >> 1) & 7);  // rows r0 + RSTEP i share (row >> 1) & 7
-  const bf16_t* a_src[LPT];
-  const bf16_t* w_src[LPT];
+  // ---- LDS-DMA sources. A DMA wave instruction fills 1 KiB of a stage =
+  // 1024 / kRowBytes rows; lane L writes row (1024 / kRowBytes) u + L / kCPR,
+  // physical chunk L % kCPR, i.e. logical chunk (L % kCPR) ^ swz(row).
+  const bf16_t* src[IPW];
+  int dst_off[IPW];
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int row = r0 + RSTEP * i;
-    int am = m0 + row;
-    am = am < M ? am : M - 1;
-    a_src[i] = A + (long)am * K + ck * 8;
-    int wr;
-    if (EPI == kEpiSwiGLU) {
-      // wave block of WTN rows: first half gate rows, second half the matching up rows
-      const int wblk = row / WTN, sel = (row % WTN) / (WTN / 2), o = row % (WTN / 2);
-      wr = sel * ea.ffn_dim + 128 * tn + (WTN / 2) * wblk + o;
+  for (int j = 0; j < IPW; ++j) {
+    const int u = wid * IPW + j;                 // instruction index in the stage
+    const bool is_w = u >= INSTS / 2;
+    const int ub = is_w ? u - INSTS / 2 : u;
+    const int row = (1024 / kRowBytes) * ub + lane / kCPR;
+    const int c = (lane % kCPR) ^ gemm_swz(row);
+    if (is_w) {
+      int wr;
+      if (EPI == kEpiSwiGLU) {
+        // wave block of WTN rows: first half gate rows, second half the matching up rows
+        const int wblk = row / WTN, sel = (row % WTN) / (WTN / 2), o = row % (WTN / 2);
+        wr = sel * ea.ffn_dim + 128 * tn + (WTN / 2) * wblk + o;
+      } else {
+        wr = tn * BN + row;
+      }
+      src[j] = W + (long)wr * K + c * 8;
     } else {
-      wr = tn * BN + row;
+      int am = m0 + row;
+      am = am < M ? am : M - 1;
+      src[j] = A + (long)am * K + c * 8;
     }
-    w_src[i] = W + (long)wr * K + ck * 8;
+    dst_off[j] = (is_w ? kOpBytes : 0) + ub * 1024;
   }
-  const int st_off = r0 * 128 + (swz << 4);  // + i * RSTEP * 128
+  auto issue = [&](int kt) {
+    uint8_t* stage = lds + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr_t)(stage + dst_off[j]), 16, 0, 0);
+  };
 
   floatx16 acc[MI][NI];
 #pragma unroll
@@ -144,54 +184,49 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  u32x4 ra[LPT], rw[LPT];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK);
-      rw[i] = *reinterpret_cast<const u32x4*>(w_src[i] + kt * BK);
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* As = lds + stage * kStageBytes;
-    uint8_t* Ws = As + BM * BK * 2;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      *reinterpret_cast<u32x4*>(As + st_off + i * RSTEP * 128) = ra[i];
-      *reinterpret_cast<u32x4*>(Ws + st_off + i * RSTEP * 128) = rw[i];
-    }
-  };
-
   // fragment read offsets: row (lane & 31) of a 32-row block, chunk 2kk + (lane >> 5)
-  const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = (fr_row >> 1) & 7;
-
-  const int KT = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint8_t* As = lds + stage * kStageBytes;
-    const uint8_t* Ws = As + BM * BK * 2;
+  const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = gemm_swz(fr_row);
+  auto compute = [&](int kt) {
+    const uint8_t* As = lds + (kt % kStages) * kStageBytes;
+    const uint8_t* Ws = As + kOpBytes;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       const int chunk = ((2 * kk + fr_hi) ^ fr_sw) << 4;
       bf16x8 wf[NI], af[MI];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        wf[ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * 128 + chunk);
+        wf[ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * kRowBytes + chunk);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * 128 + chunk);
+        af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * kRowBytes + chunk);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ni], af[mi], acc[mi][ni], 0, 0, 0);
     }
-    if (kt + 1 < KT) lstore(stage ^ 1);
-    __syncthreads();
+  };
+
+  // ---- pipeline: stages kt+1 .. kt+3 in flight while kt is multiplied.
+  // Before the barrier of step kt a wave waits until its own DMA of stage kt
+  // has landed (at most the later stages' IPW-instruction groups outstanding);
+  // the barrier then publishes stage kt to every wave and guarantees that
+  // all waves are done with the stage the next DMA overwrites.
+  const int KT = K / BK;
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < KT) issue(p);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int later = KT - 1 - kt;  // stages issued after kt (at most kStages - 2)
+    if (kStages >= 4 && later >= 2)
+      wait_vmcnt<(kStages >= 4 ? 2 : 0) * IPW>();
+    else if (kStages >= 3 && later >= 1)
+      wait_vmcnt<(kStages >= 3 ? 1 : 0) * IPW>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+    compute(kt);
   }
 
   // ---- epilogue: lane holds row m = ... + (lane & 31), columns 8i + 4*(lane>>5) + j
@@ -298,7 +333,7 @@ constexpr int kGemmWGM = 2, kGemmWGN = MINIH3_GEMM_WAVES / 2;
 template <>
 hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, bf16_t* C, int M, int N, int K,
                                const EpiArgs& ea, hipStream_t st) {
-  if (M <= 0 || N % BN != 0 || K % BK != 0) return hipErrorInvalidValue;
+  if (M <= 0 || N % BN != 0 || K % 64 != 0) return hipErrorInvalidValue;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
