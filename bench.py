@@ -43,6 +43,27 @@ def flop_counts(dims, layout):
     return gemm, attn
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attention_clip32k_traffic.md")
+ATTENTION_SOURCE = os.path.join(ROOT, "joint_video_audio_amd", "csrc", "attention.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when it covers another workload or another version of
+    the kernel source."""
+    import hashlib
+    import re
+    if workload != "clip32k" or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m_sha = re.search(r"attention\.hip sha256: ([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch: ([0-9]+)", text)
+    if not (m_sha and m_b):
+        return None
+    sha = hashlib.sha256(open(ATTENTION_SOURCE, "rb").read()).hexdigest()
+    return int(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
 def cpu_baseline(wl, rows: int):
     """The oracle (fp64 numpy) timed on the first `rows` packed rows of the
     workload taken as their own sequence; scaled to rows/s of the full
@@ -85,6 +106,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
+                         "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the block is measured on a single "
@@ -100,6 +124,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     m.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+
+    if a.copy_calibration:
+        src = torch.ones(a.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     t0 = time.time()
     wl = synth.make_workload(a.workload, seed=a.seed)
@@ -162,7 +194,7 @@ def main():
         "kernel_avg_ms": kernels,
         "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(att_tflops, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(a.workload),
                      "avg_launch_ms": round(att_avg, 4)},
     }
     if not a.no_cpu_baseline:

@@ -21,11 +21,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Kernel ids reported by minih3_profile_collect.
 enum KernelId {
-  kKLayout = 0, kKTiles, kKAdaLN1, kKQKV, kKQKNormRope, kKAttention, kKOutProj, kKAdaLN2, kKGateUp, kKDown,
-  kKNumIds
+  kKLayout = 0, kKTiles, kKAdaLN1, kKQKV, kKQKNormRope, kKAttnPrep, kKAttention, kKOutProj, kKAdaLN2, kKGateUp,
+  kKDown, kKNumIds
 };
 const char* kKernelNames[kKNumIds] = {"layout_validate", "attention_tiles", "adaln_pre_attention",
-                                      "qkv_projection", "qk_norm_rope", "attention",
+                                      "qkv_projection", "qk_norm_rope", "attention_key_norms", "attention",
                                       "out_projection_gated_residual", "adaln_pre_ffn", "gate_up_swiglu",
                                       "down_projection_gated_residual"};
 
@@ -243,6 +243,10 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       if (taps->v_t) HIPCHECK(hipMemcpyAsync(taps->v_t, vt, hb, hipMemcpyDeviceToDevice, st));
     }
     {
+      Timed tm(prof, kKAttnPrep, st);
+      HIPCHECK(launch_attention_prep<T>(kn, w.masks, w.attn_scratch, B, S, H, Sp, st));
+    }
+    {
       Timed tm(prof, kKAttention, st);
       HIPCHECK(launch_attention<T>(qn, kn, vt, o, w.masks, w.list_real, w.list_pad, w.meta, w.attn_scratch, B, S, H,
                                    Sp, scale, st));
@@ -409,6 +413,8 @@ int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, cons
   }
   HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, masks, list_real, list_pad, meta, st));
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)c->head_dim);
+  if (c->act_dtype == MINIH3_BF16)
+    HIPCHECK(launch_attention_prep<bf16_t>((const bf16_t*)k, masks, scratch, L->batch, S, c->num_heads, seq_stride, st));
   if (c->act_dtype == MINIH3_BF16)
     HIPCHECK(launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v_t, (bf16_t*)out, masks,
                                       list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, seq_stride, scale,

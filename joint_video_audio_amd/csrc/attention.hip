@@ -636,6 +636,15 @@ size_t attention_scratch_bytes(int B, int S, int H) {
 }
 
 template <>
+hipError_t launch_attention_prep<bf16_t>(const bf16_t* k, const uint64_t* masks, void* scratch, int B, int S, int H,
+                                         int stride, hipStream_t st) {
+  float* kmax = reinterpret_cast<float*>(scratch);
+  k_zero_f32<<<(2 * B * H + 255) / 256, 256, 0, st>>>(kmax, 2 * B * H);
+  k_key_norm_max<<<dim3((unsigned)((S + 63) / 64), (unsigned)(B * H)), 256, 0, st>>>(k, masks, kmax, S, stride);
+  return hipGetLastError();
+}
+
+template <>
 hipError_t launch_attention<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* out,
                                     const uint64_t* masks, const int32_t* list_real, const int32_t* list_pad,
                                     const int32_t* meta, void* scratch, int B, int S, int H, int stride, float scale,
@@ -643,15 +652,18 @@ hipError_t launch_attention<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16
   const int n_qt = (S + kQG - 1) / kQG;
   const int total = n_qt * H * B;
   const float c_log2 = scale * 1.4426950408889634f;
-  float* kmax = reinterpret_cast<float*>(scratch);
-  int32_t* flags = reinterpret_cast<int32_t*>(kmax + 2 * B * H);
-  k_zero_f32<<<(2 * B * H + 255) / 256, 256, 0, st>>>(kmax, 2 * B * H);
-  k_key_norm_max<<<dim3((unsigned)((S + 63) / 64), (unsigned)(B * H)), 256, 0, st>>>(k, masks, kmax, S, stride);
+  const float* kmax = reinterpret_cast<const float*>(scratch);
+  int32_t* flags = reinterpret_cast<int32_t*>(reinterpret_cast<float*>(scratch) + 2 * B * H);
   k_attn_fixed<<<total, kNW * 64, 0, st>>>(q, k, vt, out, masks, list_real, list_pad, meta, kmax, flags, S, H,
                                             stride, c_log2, n_qt, total);
   k_attn_running<<<total, kNW * 64, 0, st>>>(q, k, vt, out, masks, list_real, list_pad, meta, flags, S, H, stride,
                                               c_log2, n_qt, total);
   return hipGetLastError();
+}
+
+template <>
+hipError_t launch_attention_prep<float>(const float*, const uint64_t*, void*, int, int, int, int, hipStream_t) {
+  return hipSuccess;
 }
 
 template <>

@@ -64,6 +64,10 @@ hipError_t launch_gemm(int epi, const T* A, const T* W, T* C, int M, int N, int 
 // scratch: attention_scratch_bytes(B, S, H) bytes (per-head key-norm maxima
 // and per-workgroup flags).
 size_t attention_scratch_bytes(int B, int S, int H);
+// Per-document key-norm maxima into scratch (runs before launch_attention).
+template <typename T>
+hipError_t launch_attention_prep(const T* k, const uint64_t* masks, void* scratch, int B, int S, int H, int stride,
+                                 hipStream_t st);
 template <typename T>
 hipError_t launch_attention(const T* q, const T* k, const T* vt, T* out, const uint64_t* masks,
                             const int32_t* list_real, const int32_t* list_pad, const int32_t* meta, void* scratch,
