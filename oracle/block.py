@@ -163,8 +163,18 @@ def attention_doc_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, doc: np.nd
         for h in range(H):
             one_head(h)
     else:
-        with cf.ThreadPoolExecutor(n_threads) as ex:
-            list(ex.map(one_head, range(H)))
+        # heads run in parallel threads, each with a single-threaded BLAS
+        try:
+            from threadpoolctl import threadpool_limits
+            limit = threadpool_limits(limits=1, user_api="blas")
+        except ImportError:  # pragma: no cover
+            limit = None
+        try:
+            with cf.ThreadPoolExecutor(n_threads) as ex:
+                list(ex.map(one_head, range(H)))
+        finally:
+            if limit is not None:
+                limit.restore_original_limits()
     return out
 
 
