@@ -132,7 +132,9 @@ int minih3_workspace_bytes(const minih3_config* cfg, int32_t batch, int32_t seq_
  * projection, per-head q/k RMSNorm, 3-D RoPE, attention within documents
  * (padding rows alone), output projection with gated residual, AdaLN,
  * SwiGLU FFN with gated residual. Padding rows leave the block unchanged.
- * x_out must not alias x_in or the workspace. */
+ * x_out must not alias x_in or the workspace. For bf16 every projection
+ * operand (B*S rows of D, H*hd or ffn_dim values) must stay below 4 GiB
+ * (MINIH3_E_UNSUPPORTED otherwise). */
 int minih3_block_forward(const minih3_config* cfg, const minih3_layout* layout,
                          const minih3_block_weights* blocks, int32_t num_blocks,
                          const void* x_in, void* x_out, void* workspace, size_t workspace_bytes,
@@ -176,7 +178,8 @@ int minih3_qk_norm_rope(const minih3_config* cfg, const minih3_layout* layout, c
                         void* v_t_out, int32_t seq_stride, void* stream);
 
 /* Plain projection c[M, N] = a[M, K] . w[N, K]^T in `dtype`, fp32
- * accumulation. Constraints: N % 256 == 0, K % 64 == 0, M >= 1. */
+ * accumulation. Constraints: N % 256 == 0, K % 64 == 0, M >= 1; for bf16
+ * also 2*M*K and 2*N*K below 4 GiB (MINIH3_E_UNSUPPORTED otherwise). */
 int minih3_linear(int32_t dtype, const void* a, const void* w, void* c, int32_t M, int32_t N, int32_t K,
                   void* stream);
 

@@ -7,7 +7,9 @@
 //
 // HBM-bound: one workgroup per row, the row held in registers between the
 // mean, variance and output passes, 16-byte coalesced loads and stores,
-// fp32 statistics.
+// fp32 statistics. The input may be the fp32 residual stream of a bf16
+// block (the library keeps the residual in fp32 between the two gated
+// residual adds and between blocks).
 #include "common.h"
 #include "kernels.h"
 
@@ -46,6 +48,18 @@ template <> struct Vec<float> {
   }
 };
 
+// VN input values of type TI (VN = the output vector width)
+template <typename TI, int VN>
+__device__ __forceinline__ void load_in(const TI* p, float* v) {
+  if constexpr (sizeof(TI) == 4) {
+#pragma unroll
+    for (int i = 0; i < VN; i += 4) Vec<float>::load(reinterpret_cast<const float*>(p) + i, v + i);
+  } else {
+    static_assert(VN == Vec<bf16_t>::N, "bf16 input feeds a bf16 output");
+    Vec<bf16_t>::load(reinterpret_cast<const bf16_t*>(p), v);
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -59,8 +73,8 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-template <typename T, int NT, int MAXV>
-__global__ void __launch_bounds__(NT) k_adaln(const T* x, T* y,  // x and y may alias: a row is read whole first
+template <typename TI, typename T, int NT, int MAXV>
+__global__ void __launch_bounds__(NT) k_adaln(const TI* x, T* y,  // x and y may alias: a row is read whole first
                                               const float* __restrict__ table, const int32_t* __restrict__ tags,
                                               const int32_t* __restrict__ tidx, int S, int D, int which, float eps,
                                               int num_tags, int num_tvals) {
@@ -69,7 +83,7 @@ __global__ void __launch_bounds__(NT) k_adaln(const T* x, T* y,  // x and y may 
   const long row = blockIdx.x;
   const int s = (int)(row % S);
   const int nv = D / VN;
-  const T* xr = x + row * D;
+  const TI* xr = x + row * D;
   T* yr = y + row * D;
 
   float v[MAXV][VN];
@@ -78,7 +92,7 @@ __global__ void __launch_bounds__(NT) k_adaln(const T* x, T* y,  // x and y may 
   for (int i = 0; i < MAXV; ++i) {
     int c = threadIdx.x + i * NT;
     if (c < nv) {
-      Vec<T>::load(xr + c * VN, v[i]);
+      load_in<TI, VN>(xr + c * VN, v[i]);
 #pragma unroll
       for (int e = 0; e < VN; ++e) sum += v[i][e];
     }
@@ -124,28 +138,55 @@ __global__ void __launch_bounds__(NT) k_adaln(const T* x, T* y,  // x and y may 
   }
 }
 
-template <typename T>
-hipError_t launch_adaln(const T* x, T* y, const float* table, const int32_t* tags, const int32_t* tidx, int B, int S,
-                        int D, int which, float eps, int num_tags, int num_tvals, hipStream_t st) {
+template <typename TI, typename T>
+hipError_t launch_adaln_t(const TI* x, T* y, const float* table, const int32_t* tags, const int32_t* tidx, int B,
+                          int S, int D, int which, float eps, int num_tags, int num_tvals, hipStream_t st) {
   constexpr int NT = 256;
   const int nv = D / Vec<T>::N;
   dim3 grid((unsigned)((long)B * S));
   if (nv <= NT * 1)
-    k_adaln<T, NT, 1><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+    k_adaln<TI, T, NT, 1><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
   else if (nv <= NT * 2)
-    k_adaln<T, NT, 2><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+    k_adaln<TI, T, NT, 2><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
   else if (nv <= NT * 3)
-    k_adaln<T, NT, 3><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+    k_adaln<TI, T, NT, 3><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
   else if (nv <= NT * 4)
-    k_adaln<T, NT, 4><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+    k_adaln<TI, T, NT, 4><<<grid, NT, 0, st>>>(x, y, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-template hipError_t launch_adaln<bf16_t>(const bf16_t*, bf16_t*, const float*, const int32_t*, const int32_t*, int,
-                                         int, int, int, float, int, int, hipStream_t);
-template hipError_t launch_adaln<float>(const float*, float*, const float*, const int32_t*, const int32_t*, int, int,
-                                        int, int, float, int, int, hipStream_t);
+template <typename T>
+hipError_t launch_adaln(const void* x, bool x_f32, T* y, const float* table, const int32_t* tags,
+                        const int32_t* tidx, int B, int S, int D, int which, float eps, int num_tags, int num_tvals,
+                        hipStream_t st) {
+  if (x_f32)
+    return launch_adaln_t<float, T>(static_cast<const float*>(x), y, table, tags, tidx, B, S, D, which, eps,
+                                    num_tags, num_tvals, st);
+  return launch_adaln_t<T, T>(static_cast<const T*>(x), y, table, tags, tidx, B, S, D, which, eps, num_tags,
+                              num_tvals, st);
+}
+
+template hipError_t launch_adaln<bf16_t>(const void*, bool, bf16_t*, const float*, const int32_t*, const int32_t*,
+                                         int, int, int, int, float, int, int, hipStream_t);
+template hipError_t launch_adaln<float>(const void*, bool, float*, const float*, const int32_t*, const int32_t*, int,
+                                        int, int, int, float, int, int, hipStream_t);
+
+// fp32 -> act copy (taps of the fp32 residual stream)
+template <typename T>
+__global__ void __launch_bounds__(256) k_cast_f32(const float* __restrict__ x, T* __restrict__ y, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) Act<T>::st(y + i, x[i]);
+}
+
+template <typename T>
+hipError_t launch_cast_f32(const float* x, T* y, long n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  k_cast_f32<T><<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(x, y, n);
+  return hipGetLastError();
+}
+template hipError_t launch_cast_f32<bf16_t>(const float*, bf16_t*, long, hipStream_t);
+template hipError_t launch_cast_f32<float>(const float*, float*, long, hipStream_t);
 
 }  // namespace minih3

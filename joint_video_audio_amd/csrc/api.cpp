@@ -93,6 +93,9 @@ int check_config_attention(const minih3_config* c) {
   return MINIH3_OK;
 }
 
+// The bf16 projection kernel addresses each operand with 32-bit byte offsets.
+bool gemm_fits(long M, long N, long K) { return M * K * 2 <= 0xFFFFFFFFL && N * K * 2 <= 0xFFFFFFFFL; }
+
 int check_layout(const minih3_layout* L, bool need_indices) {
   if (!L) return MINIH3_E_ARG;
   if (L->batch < 1 || L->seq_len < 1) return MINIH3_E_ARG;
@@ -159,8 +162,8 @@ Workspace carve(const minih3_config* c, int B, int S, char* base) {
   w.kn = take((size_t)B * H * Sp * hd * e);
   w.vt = take((size_t)B * H * Sp * hd * e);
   w.o = take(M * Wd * e);
-  w.xmid = take(M * D * e);
-  w.xping = take(M * D * e);
+  w.xmid = take(M * D * 4);   // fp32 residual stream
+  w.xping = take(M * D * 4);
   char* tb = take(tiles_bytes(B, S, (int)H, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr));
   if (base) tiles_bytes(B, S, (int)H, &w.list_real, &w.list_pad, &w.meta, &w.masks, &w.attn_scratch, tb);
   w.counts = (int32_t*)take(4 * (size_t)S);
@@ -204,13 +207,18 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
   T* a = (T*)w.a;
   T* qkv = (T*)w.qkvh;
   T* hbuf = (T*)w.qkvh;  // the SwiGLU output reuses the QKV buffer
-  T *qn = (T*)w.qn, *kn = (T*)w.kn, *vt = (T*)w.vt, *o = (T*)w.o, *xmid = (T*)w.xmid, *ping = (T*)w.xping;
+  T *qn = (T*)w.qn, *kn = (T*)w.kn, *vt = (T*)w.vt, *o = (T*)w.o;
+  // The residual stream stays fp32 between the block's two gated adds and
+  // between blocks; only x_out is rounded to the activation type.
+  float *xmid = (float*)w.xmid, *ping = (float*)w.xping;
   const float scale = 1.f / sqrtf((float)hd);
 
-  const T* src = x_in;
+  const void* src = x_in;
+  bool src_f32 = sizeof(T) == 4;
   for (int i = 0; i < nb; ++i) {
     const minih3_block_weights& bw = blocks[i];
-    T* dst = ((nb - 1 - i) % 2 == 0) ? x_out : ping;
+    const bool last = i == nb - 1;
+    void* dst = last ? (void*)x_out : (void*)ping;  // ping may be src: src is consumed before dst is written
     const bool tap = taps && i == 0;
     EpiArgs ea{};
     ea.table = bw.adaln_table;
@@ -223,8 +231,8 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
 
     {
       Timed tm(prof, kKAdaLN1, st);
-      HIPCHECK(launch_adaln<T>(src, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 0, c->norm_eps,
-                               c->num_tags, c->num_tvals, st));
+      HIPCHECK(launch_adaln<T>(src, src_f32, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 0,
+                               c->norm_eps, c->num_tags, c->num_tvals, st));
     }
     if (tap && taps->adaln1) HIPCHECK(hipMemcpyAsync(taps->adaln1, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
     {
@@ -252,18 +260,20 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
                                    Sp, scale, st));
     }
     if (tap && taps->attn_o) HIPCHECK(hipMemcpyAsync(taps->attn_o, o, (size_t)M * Wd * e, hipMemcpyDeviceToDevice, st));
-    if (tap && taps->attn_proj) HIPCHECK(launch_gemm<T>(kEpiStore, o, (const T*)bw.w_out, (T*)taps->attn_proj, M, D, Wd, ea, st));
+    if (tap && taps->attn_proj) HIPCHECK(launch_gemm<T>(kEpiStore, o, (const T*)bw.w_out, taps->attn_proj, M, D, Wd, ea, st));
     {
       Timed tm(prof, kKOutProj, st);
       ea.resid = src;
+      ea.resid_f32 = src_f32;
+      ea.out_f32 = 1;
       ea.gate_slot = 2;
       HIPCHECK(launch_gemm<T>(kEpiGatedResid, o, (const T*)bw.w_out, xmid, M, D, Wd, ea, st));
     }
-    if (tap && taps->x_mid) HIPCHECK(hipMemcpyAsync(taps->x_mid, xmid, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
+    if (tap && taps->x_mid) HIPCHECK(launch_cast_f32<T>(xmid, (T*)taps->x_mid, (long)M * D, st));
     {
       Timed tm(prof, kKAdaLN2, st);
-      HIPCHECK(launch_adaln<T>(xmid, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 1, c->norm_eps,
-                               c->num_tags, c->num_tvals, st));
+      HIPCHECK(launch_adaln<T>(xmid, true, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 1,
+                               c->norm_eps, c->num_tags, c->num_tvals, st));
     }
     if (tap && taps->adaln2) HIPCHECK(hipMemcpyAsync(taps->adaln2, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
     {
@@ -271,14 +281,17 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       HIPCHECK(launch_gemm<T>(kEpiSwiGLU, a, (const T*)bw.w_gate_up, hbuf, M, 2 * F, D, ea, st));
     }
     if (tap && taps->ffn_h) HIPCHECK(hipMemcpyAsync(taps->ffn_h, hbuf, (size_t)M * F * e, hipMemcpyDeviceToDevice, st));
-    if (tap && taps->ffn_out) HIPCHECK(launch_gemm<T>(kEpiStore, hbuf, (const T*)bw.w_down, (T*)taps->ffn_out, M, D, F, ea, st));
+    if (tap && taps->ffn_out) HIPCHECK(launch_gemm<T>(kEpiStore, hbuf, (const T*)bw.w_down, taps->ffn_out, M, D, F, ea, st));
     {
       Timed tm(prof, kKDown, st);
       ea.resid = xmid;
+      ea.resid_f32 = 1;
+      ea.out_f32 = last ? (sizeof(T) == 4) : 1;
       ea.gate_slot = 5;
       HIPCHECK(launch_gemm<T>(kEpiGatedResid, hbuf, (const T*)bw.w_down, dst, M, D, F, ea, st));
     }
     src = dst;
+    src_f32 = !last || sizeof(T) == 4;
   }
   return MINIH3_OK;
 }
@@ -354,6 +367,12 @@ int minih3_block_forward(const minih3_config* c, const minih3_layout* L, const m
     const minih3_block_weights& b = blocks[i];
     if (!b.w_qkv || !b.w_out || !b.w_gate_up || !b.w_down || !b.q_norm || !b.k_norm || !b.adaln_table)
       return MINIH3_E_ARG;
+  }
+  if (c->act_dtype == MINIH3_BF16) {
+    const long rows = (long)L->batch * L->seq_len, D = c->hidden, W = (long)c->num_heads * c->head_dim;
+    const long F = c->ffn_dim;
+    if (!gemm_fits(rows, 3 * W, D) || !gemm_fits(rows, D, W) || !gemm_fits(rows, 2 * F, D) || !gemm_fits(rows, D, F))
+      return MINIH3_E_UNSUPPORTED;
   }
   Workspace w = carve(c, L->batch, L->seq_len, (char*)workspace);
   if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
@@ -435,10 +454,10 @@ int minih3_adaln_modulate(const minih3_config* c, const minih3_layout* L, const 
   if (!x || !table || !y || (which != 0 && which != 1)) return MINIH3_E_ARG;
   hipStream_t st = (hipStream_t)stream;
   if (c->act_dtype == MINIH3_BF16)
-    HIPCHECK(launch_adaln<bf16_t>((const bf16_t*)x, (bf16_t*)y, table, L->token_tags, L->timestep_indices, L->batch,
+    HIPCHECK(launch_adaln<bf16_t>(x, false, (bf16_t*)y, table, L->token_tags, L->timestep_indices, L->batch,
                                   L->seq_len, c->hidden, which, c->norm_eps, c->num_tags, c->num_tvals, st));
   else
-    HIPCHECK(launch_adaln<float>((const float*)x, (float*)y, table, L->token_tags, L->timestep_indices, L->batch,
+    HIPCHECK(launch_adaln<float>(x, false, (float*)y, table, L->token_tags, L->timestep_indices, L->batch,
                                  L->seq_len, c->hidden, which, c->norm_eps, c->num_tags, c->num_tvals, st));
   return MINIH3_OK;
 }
@@ -469,7 +488,7 @@ int minih3_linear(int32_t dtype, const void* a, const void* w, void* c, int32_t 
   hipStream_t st = (hipStream_t)stream;
   EpiArgs ea{};
   if (dtype == MINIH3_BF16) {
-    if (N % 256 != 0 || K % 64 != 0) return MINIH3_E_UNSUPPORTED;
+    if (N % 256 != 0 || K % 64 != 0 || !gemm_fits(M, N, K)) return MINIH3_E_UNSUPPORTED;
     HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)a, (const bf16_t*)w, (bf16_t*)c, M, N, K, ea, st));
   } else if (dtype == MINIH3_F32) {
     if (N % 64 != 0 || K % 16 != 0) return MINIH3_E_UNSUPPORTED;

@@ -11,13 +11,14 @@
 //                    a padding row keeps resid unchanged)
 //   kEpiSwiGLU     : W rows [0,F) gate, [F,2F) up; C[:, f] = silu(g_f) * u_f
 //
-// bf16 kernel (gfx950): 256x256 output tile per workgroup of 8 waves (two per
-// SIMD), each wave 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 tiles. K steps of 32
-// go through a ring of 4 LDS stages (128 KiB) filled by direct global->LDS
-// loads (global_load_lds_dwordx4) three steps ahead, so no registers stage
-// the operands and the load latency hides behind three steps of MFMA work;
-// one barrier per step. Tiles are ordered so that the workgroups an XCD runs
-// together share A and W panels in its L2.
+// bf16 kernel (gfx950): 256x256 output tile per workgroup of 4 waves, one per
+// SIMD, each 128x128 as 4x4 v_mfma_f32_32x32x16_bf16 accumulators in AGPRs.
+// Operands reach LDS by direct buffer->LDS DMA in K steps of 64 through a
+// ring of five 32 KiB slots (the A and W halves of a step are loaded at
+// different times, see the kernel); fragments are read one MFMA step ahead
+// and the instruction order inside a step is fixed with sched_group_barrier.
+// One barrier per K step. Tiles are ordered so that the workgroups an XCD
+// runs together share A and W panels in its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -75,22 +76,39 @@ __device__ __forceinline__ void epi_gated(T* C, int ldc, int m, int n, const flo
   store4<T>(C + (long)m * ldc + n, r);
 }
 
+// Gated residual of the bf16 kernel: the residual and the output are each
+// bf16 or fp32 (the fp32 residual stream between the block's two gated adds
+// and between blocks).
+__device__ __forceinline__ void epi_gated_mixed(void* C, int ldc, int m, int n, const float* acc, const EpiArgs& ea) {
+  float r[4];
+  const long at = (long)m * ldc + n;
+  if (ea.resid_f32)
+    load4<float>(static_cast<const float*>(ea.resid) + at, r);
+  else
+    load4<bf16_t>(static_cast<const bf16_t*>(ea.resid) + at, r);
+  const int s = m % ea.S;
+  const int tr = table_row_of(ea.tags[s], ea.tidx[s], ea.num_tags, ea.num_tvals);
+  if (tr >= 0) {
+    floatx4 g = *reinterpret_cast<const floatx4*>(ea.table + ((long)tr * 6 + ea.gate_slot) * ldc + n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] += g[j] * acc[j];
+  }
+  if (ea.out_f32)
+    store4<float>(static_cast<float*>(C) + at, r);
+  else
+    store4<bf16_t>(static_cast<bf16_t*>(C) + at, r);
+}
+
 // ---------------------------------------------------------------- bf16 MFMA kernel
 
-constexpr int BM = 256, BN = 256;
-#ifndef MINIH3_GEMM_BK
-#define MINIH3_GEMM_BK 64
-#endif
-#ifndef MINIH3_GEMM_STAGES
-#define MINIH3_GEMM_STAGES 2
-#endif
-constexpr int BK = MINIH3_GEMM_BK;                  // K step (32 or 64)
-constexpr int kStages = MINIH3_GEMM_STAGES;         // LDS ring depth; loads run kStages-1 steps ahead
-constexpr int kRowBytes = BK * 2;                   // one tile row per stage
-constexpr int kCPR = kRowBytes / 16;                // 16-byte chunks per row
-constexpr int kOpBytes = BM * kRowBytes;            // one operand tile per stage
-constexpr int kStageBytes = 2 * kOpBytes;           // A + W
-static_assert(kStages * kStageBytes <= 160 * 1024, "LDS");
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kRowBytes = BK * 2;         // 128: one tile row of one K step
+constexpr int kCPR = kRowBytes / 16;      // 16-byte chunks per row
+constexpr int kSlotBytes = BM * kRowBytes;  // one operand (A or W) of one K step: 32 KiB
+constexpr int kSlots = 5;                 // LDS ring: 160 KiB
+constexpr int kWaves = 4;                 // one per SIMD, 128 x 128 outputs each
+constexpr int kIPW = kSlotBytes / 1024 / kWaves;  // 1 KiB DMA instructions per wave per slot
+static_assert(BM == BN, "A and W slots share a layout");
 
 // Logical chunk c of tile row r sits at chunk c ^ swz(r): the 16 lanes a
 // ds_read_b128 serves together read 16 consecutive rows at one chunk, and
@@ -100,29 +118,49 @@ __device__ __forceinline__ int gemm_swz(int r) { return (r / (16 / kCPR)) % kCPR
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// 16 bytes per lane from global memory straight into LDS (buffer form):
+// base wave-uniform, voff the lane's byte offset, soff a uniform byte offset.
+// Lane L lands at dst + 16 L.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t soff, lds_ptr_t dst) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// WGM x WGN waves (two per SIMD); each wave owns a (256/WGM) x (256/WGN)
-// block of the 256x256 tile.
-template <int EPI, int WGM, int WGN>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1)
-    k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ C, int M, int N,
+// sched_group_barrier masks
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+
+// 256 x 256 output tile per workgroup of four waves; wave (wm, wn) owns the
+// 128 x 128 block at (128 wm, 128 wn) as 4 x 4 v_mfma_f32_32x32x16_bf16
+// accumulators (256 AGPRs).
+//
+// K advances in steps of 64. The A and W operands of a step each fill one
+// 32 KiB slot of a 5-slot LDS ring (slot of A_k: 2k mod 5, W_k: 2k + 1 mod
+// 5), loaded by direct buffer->LDS DMA. Within step k the four MFMA steps
+// (K 16 each) read their fragments one MFMA step ahead. A_{k+2} is loaded
+// during the first two MFMA steps of k (its slot held W_{k-1}); after the
+// third, every wave waits for its own DMA of step k + 1 and one barrier
+// publishes it and frees A_k's and W_k's slots; W_{k+2} is then loaded into
+// A_k's slot while the last MFMA step of k runs. A_k therefore has about two
+// K steps to arrive, W_k one, and no more than half a step of DMA is ever
+// queued behind a barrier.
+template <int EPI>
+__global__ void __launch_bounds__(64 * kWaves, 1)
+    k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
                 int K, EpiArgs ea) {
-  constexpr int NW = WGM * WGN;
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
-  constexpr int MI = WTM / 32, NI = WTN / 32;    // 32x32 MFMA blocks per wave
-  constexpr int INSTS = 2 * kOpBytes / 1024;     // 1 KiB LDS-DMA wave instructions per stage (A then W)
-  constexpr int IPW = INSTS / NW;                // ... per wave
-  static_assert(INSTS % NW == 0, "DMA split");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
+  constexpr int WTM = 128, WTN = 128, MI = WTM / 32, NI = WTN / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid % WGM, wn = wid / WGM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid & 1, wn = wid >> 1;
 
   // ---- tile order: XCD-contiguous ranges, then groups of 8 M-tiles
   const int MT = (M + BM - 1) / BM, NTL = N / BN;
@@ -140,40 +178,44 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   const int tn = (pid % npg) / gsz;
   const int m0 = tm * BM;
 
-  // ---- LDS-DMA sources. A DMA wave instruction fills 1 KiB of a stage =
-  // 1024 / kRowBytes rows; lane L writes row (1024 / kRowBytes) u + L / kCPR,
-  // physical chunk L % kCPR, i.e. logical chunk (L % kCPR) ^ swz(row).
-  const bf16_t* src[IPW];
-  int dst_off[IPW];
+  // ---- DMA byte offsets. Wave w fills rows 64 w .. 64 w + 63 of every slot:
+  // instruction j covers rows 64 w + 8 j .. + 7 (1 KiB); lane L takes row
+  // 64 w + 8 j + L / 8, logical chunk (L % 8) ^ swz(row).
+  uint32_t voff_a[kIPW], voff_w[kIPW];
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int u = wid * IPW + j;                 // instruction index in the stage
-    const bool is_w = u >= INSTS / 2;
-    const int ub = is_w ? u - INSTS / 2 : u;
-    const int row = (1024 / kRowBytes) * ub + lane / kCPR;
+  for (int j = 0; j < kIPW; ++j) {
+    const int row = 64 * wid + 8 * j + lane / kCPR;
     const int c = (lane % kCPR) ^ gemm_swz(row);
-    if (is_w) {
-      int wr;
-      if (EPI == kEpiSwiGLU) {
-        // wave block of WTN rows: first half gate rows, second half the matching up rows
-        const int wblk = row / WTN, sel = (row % WTN) / (WTN / 2), o = row % (WTN / 2);
-        wr = sel * ea.ffn_dim + 128 * tn + (WTN / 2) * wblk + o;
-      } else {
-        wr = tn * BN + row;
-      }
-      src[j] = W + (long)wr * K + c * 8;
+    int am = m0 + row;
+    am = am < M ? am : M - 1;
+    int wr;
+    if (EPI == kEpiSwiGLU) {
+      // wave block of WTN rows: first half gate rows, second half the matching up rows
+      const int wblk = row / WTN, sel = (row % WTN) / (WTN / 2), o = row % (WTN / 2);
+      wr = sel * ea.ffn_dim + 128 * tn + (WTN / 2) * wblk + o;
     } else {
-      int am = m0 + row;
-      am = am < M ? am : M - 1;
-      src[j] = A + (long)am * K + c * 8;
+      wr = tn * BN + row;
     }
-    dst_off[j] = (is_w ? kOpBytes : 0) + ub * 1024;
+    voff_a[j] = (uint32_t)(((long)am * K + c * 8) * 2);
+    voff_w[j] = (uint32_t)(((long)wr * K + c * 8) * 2);
   }
-  auto issue = [&](int kt) {
-    uint8_t* stage = lds + (kt % kStages) * kStageBytes;
+  const int KT = K / BK;
+  auto slot_ptr = [&](int s) { return lds + s * kSlotBytes; };
+  // DMA instructions j0 .. j1-1 of operand A (or W) of K step k into slot s;
+  // past the end of K the last step is loaded again (the slot is free).
+  auto dma_a = [&](int k, int j0, int j1) {
+    const int s = (2 * k) % kSlots;
+    const uint32_t soff = (uint32_t)((k < KT ? k : KT - 1) * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < IPW; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_ptr_t)(stage + dst_off[j]), 16, 0, 0);
+    for (int j = j0; j < j1; ++j)
+      dma16(A, voff_a[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+  };
+  auto dma_w = [&](int k) {
+    const int s = (2 * k + 1) % kSlots;
+    const uint32_t soff = (uint32_t)((k < KT ? k : KT - 1) * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < kIPW; ++j)
+      dma16(W, voff_w[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
   };
 
   floatx16 acc[MI][NI];
@@ -184,50 +226,83 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragment read offsets: row (lane & 31) of a 32-row block, chunk 2kk + (lane >> 5)
+  // fragment reads: row (lane & 31) of a 32-row block, chunk 2 kk + (lane >> 5)
   const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = gemm_swz(fr_row);
-  auto compute = [&](int kt) {
-    const uint8_t* As = lds + (kt % kStages) * kStageBytes;
-    const uint8_t* Ws = As + kOpBytes;
+  bf16x8 fa[2][MI], fw[2][NI];
+  auto read_frags = [&](int k, int kk, int slot) {
+    const uint8_t* As = slot_ptr((2 * k) % kSlots);
+    const uint8_t* Ws = slot_ptr((2 * k + 1) % kSlots);
+    const int chunk = ((2 * kk + fr_hi) ^ fr_sw) << 4;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int chunk = ((2 * kk + fr_hi) ^ fr_sw) << 4;
-      bf16x8 wf[NI], af[MI];
+    for (int ni = 0; ni < NI; ++ni)
+      fw[slot][ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * kRowBytes + chunk);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      fa[slot][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * kRowBytes + chunk);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        wf[ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * kRowBytes + chunk);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * kRowBytes + chunk);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ni], af[mi], acc[mi][ni], 0, 0, 0);
-    }
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[slot][ni], fa[slot][mi], acc[mi][ni], 0, 0, 0);
   };
-
-  // ---- pipeline: stages kt+1 .. kt+3 in flight while kt is multiplied.
-  // Before the barrier of step kt a wave waits until its own DMA of stage kt
-  // has landed (at most the later stages' IPW-instruction groups outstanding);
-  // the barrier then publishes stage kt to every wave and guarantees that
-  // all waves are done with the stage the next DMA overwrites.
-  const int KT = K / BK;
+  // instruction order of one MFMA step: its 16 MFMAs with the next step's
+  // 8 fragment reads and `dma` DMA instructions slotted between the first 8
+  auto sched = [&](int dma) {
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < KT) issue(p);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int later = KT - 1 - kt;  // stages issued after kt (at most kStages - 2)
-    if (kStages >= 4 && later >= 2)
-      wait_vmcnt<(kStages >= 4 ? 2 : 0) * IPW>();
-    else if (kStages >= 3 && later >= 1)
-      wait_vmcnt<(kStages >= 3 ? 1 : 0) * IPW>();
-    else
-      wait_vmcnt<0>();
+    for (int i = 0; i < MI + NI; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      if (i < dma) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, MI * NI - (MI + NI), 0);
+  };
+  static_assert(kIPW == MI + NI, "one DMA per slotted MFMA in the last step");
+
+  // ---- prologue: A0 W0 A1 W1 in flight, wait for step 0
+  dma_a(0, 0, kIPW);
+  dma_w(0);
+  dma_a(1, 0, kIPW);
+  dma_w(1);
+  wait_vmcnt<2 * kIPW>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0, 0);
+
+  for (int kt = 0; kt < KT - 1; ++kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(kt + 2, 0, kIPW / 2);
+    read_frags(kt, 1, 1);
+    mfmas(0);
+    sched(kIPW / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(kt + 2, kIPW / 2, kIPW);
+    read_frags(kt, 2, 0);
+    mfmas(1);
+    sched(kIPW / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(kt, 3, 1);
+    mfmas(0);
+    sched(0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kIPW>();  // A_{kt+1}, W_{kt+1} landed; A_{kt+2} may be in flight
+    wait_lgkm0();        // this wave's reads of step kt are done
     __builtin_amdgcn_s_barrier();
-    if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
-    compute(kt);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_w(kt + 2);
+    read_frags(kt + 1, 0, 0);
+    mfmas(1);
+    sched(kIPW);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags(KT - 1, 1, 1);
+  mfmas(0);
+  read_frags(KT - 1, 2, 0);
+  mfmas(1);
+  read_frags(KT - 1, 3, 1);
+  mfmas(0);
+  mfmas(1);
+  wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
 
   // ---- epilogue: lane holds row m = ... + (lane & 31), columns 8i + 4*(lane>>5) + j
 #pragma unroll
@@ -244,7 +319,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[j] = silu(acc[mi][ni][4 * i + j]) * acc[mi][ni + NI / 2][4 * i + j];
           const int f = 128 * tn + (WTN / 2) * wn + ni * 32 + 8 * i + 4 * fr_hi;
-          store4<bf16_t>(C + (long)m * F + f, v);
+          store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * F + f, v);
         }
     } else {
 #pragma unroll
@@ -254,9 +329,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
           const int n = tn * BN + wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
           float v[4] = {acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1], acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]};
           if (EPI == kEpiGatedResid)
-            epi_gated<bf16_t>(C, N, m, n, v, ea);
+            epi_gated_mixed(Cv, N, m, n, v, ea);
           else
-            store4<bf16_t>(C + (long)m * N + n, v);
+            store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * N + n, v);
         }
     }
   }
@@ -325,34 +400,29 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
 
 // ---------------------------------------------------------------- launchers
 
-#ifndef MINIH3_GEMM_WAVES
-#define MINIH3_GEMM_WAVES 8
-#endif
-constexpr int kGemmWGM = 2, kGemmWGN = MINIH3_GEMM_WAVES / 2;
-
 template <>
-hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, bf16_t* C, int M, int N, int K,
+hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* C, int M, int N, int K,
                                const EpiArgs& ea, hipStream_t st) {
-  if (M <= 0 || N % BN != 0 || K % 64 != 0) return hipErrorInvalidValue;
+  if (M <= 0 || N % BN != 0 || K % BK != 0) return hipErrorInvalidValue;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
+  // DMA offsets are 32-bit byte offsets into A and W
+  if ((unsigned long)M * K * 2 > 0xFFFFFFFFul || (unsigned long)N * K * 2 > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
-  constexpr int NT = 64 * kGemmWGM * kGemmWGN;
   switch (epi) {
-    case kEpiStore: k_gemm_bf16<kEpiStore, kGemmWGM, kGemmWGN><<<grid, NT, 0, st>>>(A, W, C, M, N, K, ea); break;
-    case kEpiGatedResid:
-      k_gemm_bf16<kEpiGatedResid, kGemmWGM, kGemmWGN><<<grid, NT, 0, st>>>(A, W, C, M, N, K, ea);
-      break;
-    case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU, kGemmWGM, kGemmWGN><<<grid, NT, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiStore: k_gemm_bf16<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiGatedResid: k_gemm_bf16<kEpiGatedResid><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <>
-hipError_t launch_gemm<float>(int epi, const float* A, const float* W, float* C, int M, int N, int K,
+hipError_t launch_gemm<float>(int epi, const float* A, const float* W, void* Cv, int M, int N, int K,
                               const EpiArgs& ea, hipStream_t st) {
   if (M <= 0 || N % 64 != 0 || K % 16 != 0) return hipErrorInvalidValue;
+  float* C = static_cast<float*>(Cv);
   const int ncols = epi == kEpiSwiGLU ? ea.ffn_dim : N;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 64 != 0)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(ncols / 64), (unsigned)((M + 63) / 64));

@@ -35,8 +35,11 @@ hipError_t launch_attn_tiles(const int32_t* tags, int S, int assume_padless, uin
 
 // ---- AdaLN ----
 template <typename T>
-hipError_t launch_adaln(const T* x, T* y, const float* table, const int32_t* tags, const int32_t* tidx, int B, int S,
-                        int D, int which, float eps, int num_tags, int num_tvals, hipStream_t st);
+hipError_t launch_adaln(const void* x, bool x_f32, T* y, const float* table, const int32_t* tags,
+                        const int32_t* tidx, int B, int S, int D, int which, float eps, int num_tags, int num_tvals,
+                        hipStream_t st);  // x: [B*S, D] fp32 if x_f32 else T
+template <typename T>
+hipError_t launch_cast_f32(const float* x, T* y, long n, hipStream_t st);
 
 // ---- q/k RMSNorm + RoPE + V transpose ----
 template <typename T>
@@ -47,7 +50,8 @@ hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, c
 // ---- GEMM: C[M,N] = A[M,K] . W[N,K]^T with fused epilogues ----
 enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2 };
 struct EpiArgs {
-  const void* resid;     // [M, ldc] act (gated residual)
+  const void* resid;     // [M, ldc] gated residual: fp32 if resid_f32 else act
+  int resid_f32, out_f32;  // bf16 kernel only: precision of resid and of C (gated residual)
   const float* table;    // adaln table
   const int32_t* tags;   // [S]
   const int32_t* tidx;   // [S]
@@ -57,7 +61,7 @@ struct EpiArgs {
   int ffn_dim;           // SwiGLU: F (W rows [0,F) gate, [F,2F) up)
 };
 template <typename T>
-hipError_t launch_gemm(int epi, const T* A, const T* W, T* C, int M, int N, int K, const EpiArgs& ea,
+hipError_t launch_gemm(int epi, const T* A, const T* W, void* C, int M, int N, int K, const EpiArgs& ea,
                        hipStream_t st);
 
 // ---- attention ----

@@ -137,7 +137,10 @@ def test_block_gate_zero_and_padless_flag():
     assert torch.equal(c, x)
 
 
-def test_chain_equals_sequential_blocks():
+def test_chain_keeps_fp32_residual_between_blocks():
+    # One call over three blocks keeps the residual stream in fp32 between
+    # them; three one-block calls round it to bf16 twice on the way. Both
+    # meet the bar, the chained call at least as closely.
     print("chain of 3", flush=True)
     dims = dims_bf16()
     wl = workload(dims, pads=9, seed=7, blocks=3)
@@ -146,10 +149,16 @@ def test_chain_equals_sequential_blocks():
     y = x
     for blk in blocks:
         y = m.block_forward(cfg, lay, [blk], y)
+    one = m.block_forward(cfg, lay, blocks[:1], x)
+    first = m.block_forward(cfg, lay, blocks[:1], x)
     torch.cuda.synchronize()
-    assert torch.equal(chained, y)
+    assert torch.equal(one, first)  # deterministic
     ref = ob.chain_forward(wl.x.values()[0], wl.layout, [oracle.weights_f64(b) for b in wl.blocks], dims)
     assert_close(to_np64(chained[0]), ref, "chain")
+    assert_close(to_np64(y[0]), ref, "sequential calls")
+    r_chain, r_seq = rel_l2(to_np64(chained[0]), ref), rel_l2(to_np64(y[0]), ref)
+    print(f"rel_l2 chained {r_chain:.3e} sequential {r_seq:.3e}", flush=True)
+    assert r_chain <= r_seq
 
 
 def _layout_status(wl, **mut):

@@ -55,3 +55,11 @@ def test_host_side_queries_and_argument_errors():
     assert s == m.E_WORKSPACE
     assert lib.minih3_linear(0, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 4, 100, 64,
                              None) == m.E_UNSUPPORTED
+    # bf16 projection operands above 4 GiB are refused before any GPU work
+    assert lib.minih3_linear(0, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), 300000, 256, 7168,
+                             None) == m.E_UNSUPPORTED
+    L_big = m._Layout(1, 160000, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None, 0, None, 0,
+                      None, 0)
+    s = lib.minih3_block_forward(ctypes.byref(cfg), ctypes.byref(L_big), bw, 1, ctypes.c_void_p(16),
+                                 ctypes.c_void_p(32), ctypes.c_void_p(64), 10, 0, None, None)
+    assert s == m.E_UNSUPPORTED
