@@ -130,7 +130,7 @@ size_t tiles_bytes(int B, int S, int H, int32_t** list_real, int32_t** list_pad,
     return base ? base + o : nullptr;
   };
   char* p;
-  p = take(16 * nt);
+  p = take(48 * nt);  // per-tile masks, then the masks of each list entry (two lists)
   if (masks) *masks = (uint64_t*)p;
   p = take(4 * nt);
   if (list_real) *list_real = (int32_t*)p;

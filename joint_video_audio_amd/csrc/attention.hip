@@ -85,6 +85,7 @@ struct TileWalk {
   static constexpr int CH = 1024 / NT;           // 16-byte chunks per thread per tile (K or V^T)
 
   const int* list;
+  const uint64_t* recs;   // masks of walk position p at recs[2p], recs[2p + 1]
   int n_iter;
   bool wq_real, wq_pad;   // documents present among this wave's queries
   int qdoc;               // this lane's query document
@@ -112,13 +113,16 @@ struct TileWalk {
       g_pad |= masks[2 * (r / kKV) + 1] != 0;
     }
     list = nullptr;
+    recs = masks;
     if (g_real && g_pad) {
       n_iter = nt_real;  // every tile
     } else if (g_pad) {
       list = list_pad;
+      recs = masks + 4 * nt_real;
       n_iter = meta[1];
     } else {
       list = list_real;
+      recs = masks + 2 * nt_real;
       n_iter = meta[0];
     }
     qdoc = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
@@ -406,16 +410,57 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 
-  auto mask_tile = [&](floatx16(&sc)[2], int t) {
-    const uint64_t mreal = masks[2 * t], mpad = masks[2 * t + 1];
-    const bool clean = (tw.wq_real && !tw.wq_pad && mreal == ~0ull) || (tw.wq_pad && !tw.wq_real && mpad == ~0ull);
-    if (!clean) apply_doc_mask(sc, tw.qdoc ? mpad : mreal, hi);
+  // The tile walk is prefetched 64 positions at a time: lane j of a block
+  // holds the tile of walk position 64 blk + j and its two document masks.
+  // A step reads what it needs with readlane from the current block or the
+  // next; when the walk enters the next block it becomes the current one
+  // (loaded 64 steps earlier) and the block after it is requested.
+  struct Ahead {
+    int t;
+    uint64_t mr, mp;
+  };
+  struct Blk {
+    int t;
+    u32x4 m;
+  };
+  auto load_blk = [&](int blk) {
+    Blk r;
+    int pos = blk * 64 + lane;
+    pos = pos < n ? pos : n - 1;
+    r.t = tw.list ? tw.list[pos] : pos;
+    r.m = *reinterpret_cast<const u32x4*>(tw.recs + 2 * pos);
+    return r;
+  };
+  Blk bcur = load_blk(0), bnext = load_blk(1);
+  // position pos of block cb (bcur) or cb + 1 (bnext)
+  auto at = [&](int pos, int cb) {
+    const bool nx = (pos >> 6) != cb;
+    const int l = pos & 63;
+    Ahead a;
+    a.t = __builtin_amdgcn_readlane(nx ? bnext.t : bcur.t, l);
+    const uint32_t m0 = __builtin_amdgcn_readlane(nx ? bnext.m[0] : bcur.m[0], l);
+    const uint32_t m1 = __builtin_amdgcn_readlane(nx ? bnext.m[1] : bcur.m[1], l);
+    const uint32_t m2 = __builtin_amdgcn_readlane(nx ? bnext.m[2] : bcur.m[2], l);
+    const uint32_t m3 = __builtin_amdgcn_readlane(nx ? bnext.m[3] : bcur.m[3], l);
+    a.mr = (uint64_t)m0 | ((uint64_t)m1 << 32);
+    a.mp = (uint64_t)m2 | ((uint64_t)m3 << 32);
+    return a;
+  };
+  auto mask_tile = [&](floatx16(&sc)[2], const Ahead& a) {
+    const bool clean = (tw.wq_real && !tw.wq_pad && a.mr == ~0ull) || (tw.wq_pad && !tw.wq_real && a.mp == ~0ull);
+    if (!clean) apply_doc_mask(sc, tw.qdoc ? a.mp : a.mr, hi);
   };
   // one pipelined step: scores of tile it+1 into nxt, probabilities and O^T of tile it from cur
   auto step = [&](int it, floatx16(&cur)[2], floatx16(&nxt)[2]) {
-    const int t1 = tw.tile(it + 1);
-    tw.gload_k(tw.tile(it + 2 < n ? it + 2 : n - 1));  // the repeat at the end is never read
-    tw.gload_v(t1);
+    const int cb = (it + 1) >> 6;
+    if (((it + 1) & 63) == 0) {  // the walk enters block cb: positions below it + 1 are done with
+      bcur = bnext;
+      bnext = load_blk(cb + 1);
+    }
+    const Ahead a1 = at(it + 1, cb);
+    const int t2 = at(it + 2 < n ? it + 2 : n - 1, cb).t;  // the repeat at the end is never read
+    tw.gload_k(t2);
+    tw.gload_v(a1.t);
     const uint8_t* Kn = lds + ((it + 1) & 1) * KB;
     const uint8_t* Vc = lds + 2 * KB + (it & 1) * KB;
 #pragma unroll
@@ -429,7 +474,7 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       }
       prob_quarter(cur, qq, o, lsum, Vc, c);
     }
-    mask_tile(nxt, t1);
+    mask_tile(nxt, a1);
     tw.lstore_k(lds + (it & 1) * KB);
     tw.lstore_v(lds + 2 * KB + ((it + 1) & 1) * KB);
     __syncthreads();
@@ -442,19 +487,20 @@ __global__ void __launch_bounds__(kNW * 64, 1)
 
   if (n > 0) {
     // ---- prologue: K0 = K(0), V0 = V(0), K1 = K(1); scores of tile 0
-    const int t0 = tw.tile(0);
-    tw.gload_k(t0);
-    tw.gload_v(t0);
+    const Ahead a0 = at(0, 0);
+    const int t1 = at(n > 1 ? 1 : 0, 0).t;
+    tw.gload_k(a0.t);
+    tw.gload_v(a0.t);
     tw.lstore_k(lds);
     tw.lstore_v(lds + 2 * KB);
     if (n > 1) {
-      tw.gload_k(tw.tile(1));
+      tw.gload_k(t1);
       tw.lstore_k(lds + KB);
     }
     __syncthreads();
     floatx16 sa[2], sb[2];
     scores_full(sa, lds, c);
-    mask_tile(sa, t0);
+    mask_tile(sa, a0);
     int it = 0;
     for (; it + 2 < n; it += 2) {
       step(it, sa, sb);

@@ -30,6 +30,8 @@ hipError_t launch_layout_validate(const LayoutDev& L, int assume_padless, int32_
 // Attention tile lists: for each 64-row tile the masks of its non-padding
 // and padding rows (u64 each), and the compacted lists of tiles holding
 // any non-padding / padding row. meta[0] = #real tiles, meta[1] = #pad tiles.
+// masks holds 6 * ceil(S/64) u64: [2t, 2t+1] the masks of tile t, then at
+// 2 ntiles + 2i (4 ntiles + 2i) the masks of tile list_real[i] (list_pad[i]).
 hipError_t launch_attn_tiles(const int32_t* tags, int S, int assume_padless, uint64_t* masks, int32_t* list_real,
                              int32_t* list_pad, int32_t* meta, hipStream_t st);
 

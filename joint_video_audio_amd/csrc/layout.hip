@@ -121,8 +121,19 @@ __global__ void __launch_bounds__(1024) k_attn_tiles(const int32_t* tags, int S,
       offr += wave_tot[0][w];
       offp += wave_tot[1][w];
     }
-    if (mr) list_real[offr + pr] = t;
-    if (mp) list_pad[offp + pp] = t;
+    // the masks of each listed tile again, aligned with the list (records
+    // [2 ntiles, 4 ntiles) for the non-padding list, [4 ntiles, 6 ntiles)
+    // for the padding list), so a walk over a list reads them with its entries
+    if (mr) {
+      list_real[offr + pr] = t;
+      masks[2 * ntiles + 2 * (offr + pr)] = mr;
+      masks[2 * ntiles + 2 * (offr + pr) + 1] = mp;
+    }
+    if (mp) {
+      list_pad[offp + pp] = t;
+      masks[4 * ntiles + 2 * (offp + pp)] = mr;
+      masks[4 * ntiles + 2 * (offp + pp) + 1] = mp;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
       for (int w = 0; w < 16; ++w) {
