@@ -18,7 +18,8 @@
 // different times, see the kernel); fragments are read one MFMA step ahead
 // and the instruction order inside a step is fixed with sched_group_barrier.
 // One barrier per K step. Tiles are ordered so that the workgroups an XCD
-// runs together share A and W panels in its L2.
+// runs together share A and W panels in its L2. Plain (store) tiles are
+// staged in LDS and written as whole contiguous rows.
 #include "common.h"
 #include "kernels.h"
 
@@ -304,13 +305,35 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   mfmas(1);
   wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
 
-  // ---- epilogue: lane holds row m = ... + (lane & 31), columns 8i + 4*(lane>>5) + j
+  // ---- epilogue. The plain output goes through LDS (the ring is free now)
+  // so that global memory sees whole contiguous rows. A lane's accumulators hold
+  // row m = tile row (wm*128 + mi*32 + (lane & 31)), columns
+  // wn*128 + ni*32 + 8i + 4*(lane>>5) + j (j < 4).
+  if constexpr (EPI == kEpiGatedResid) {
+    // gated residual straight from the accumulators: each lane's row keeps one
+    // table row for all of its columns (staging through LDS serialises the
+    // per-row residual and gate loads behind the stores, and measured slower;
+    // so did staging the SwiGLU output)
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int m = m0 + wm * WTM + mi * 32 + fr_row;
-    if (m >= M) continue;
-    if (EPI == kEpiSwiGLU) {
-      const int F = ea.ffn_dim;
+    for (int mi = 0; mi < MI; ++mi) {
+      const int m = m0 + wm * WTM + mi * 32 + fr_row;
+      if (m >= M) continue;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = tn * BN + wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
+          float v[4] = {acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1], acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]};
+          epi_gated_mixed(Cv, N, m, n, v, ea);
+        }
+    }
+  } else if constexpr (EPI == kEpiSwiGLU) {
+    // silu(gate) * up straight from the accumulators (gate block ni, up block ni + NI/2)
+    const int F = ea.ffn_dim;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int m = m0 + wm * WTM + mi * 32 + fr_row;
+      if (m >= M) continue;
 #pragma unroll
       for (int ni = 0; ni < NI / 2; ++ni)
 #pragma unroll
@@ -321,18 +344,31 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
           const int f = 128 * tn + (WTN / 2) * wn + ni * 32 + 8 * i + 4 * fr_hi;
           store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * F + f, v);
         }
-    } else {
+    }
+  } else {
+    // bf16 staging: 256 rows x 256 columns, rows padded by 8 bytes so that the
+    // 32 rows an 8-byte ds_write covers hit 32 different bank pairs
+    constexpr int RB = BN * 2 + 8;
+    __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int n = tn * BN + wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
-          float v[4] = {acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1], acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]};
-          if (EPI == kEpiGatedResid)
-            epi_gated_mixed(Cv, N, m, n, v, ea);
-          else
-            store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * N + n, v);
+          const int r = wm * WTM + mi * 32 + fr_row, c = wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1]);
+          pk[1] = pack_bf16x2(acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]);
+          *reinterpret_cast<u32x2*>(lds + r * RB + c * 2) = pk;
         }
+    __syncthreads();
+    // one row (512 bytes) per wave instruction: lane owns columns 4*lane .. +3
+    for (int rr = wid; rr < BM; rr += kWaves) {
+      const int m = m0 + rr;
+      if (m < M)
+        *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(Cv) + (long)m * N + tn * BN + 4 * lane) =
+            *reinterpret_cast<const u32x2*>(lds + rr * RB + lane * 8);
     }
   }
 }
