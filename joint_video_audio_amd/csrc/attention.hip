@@ -297,47 +297,32 @@ __global__ void k_zero_f32(float* p, int n) {
 }
 
 // ---------------------------------------------------------------- fixed-reference kernel
-// Software-pipelined: while the VALU turns the scores of tile j into
-// probabilities, the MFMA unit already multiplies K of tile j+1. K is
-// staged in LDS one tile ahead of V^T (buffers K0, K1, V0, V1). Each step
-// runs in four quarters: four score MFMAs of tile j+1, the exponentials of
-// 16 keys of tile j, and the four O^T MFMAs that consume them.
-struct FixedCtx {
-  const Frag* fr;
-  const bf16x8* qf;
-  bf16x2 ones2;
-  int l32, hi;
-};
+// K and V^T tiles reach LDS by buffer->LDS DMA through rings of three slots,
+// two tiles ahead of their use; one barrier per tile. Per tile a wave runs
+// 32 MFMAs, alternating the score MFMAs of the next tile with the O^T MFMAs
+// of this one, and issues their 32 fragment reads kAhead MFMAs early; the
+// first reads of a tile overlap the exponentials, which need no LDS. The
+// scores of a tile live in one register set: each 32-key half becomes
+// probabilities before the next tile's scores overwrite it.
+constexpr int kRing = 3;
+constexpr int kTileBytes = kKV * HD * 2;  // one K or V^T tile: 16 KiB
+constexpr int kAhead = 6;                 // fragment reads in flight ahead of the MFMAs
 
-__device__ __forceinline__ void scores_full(floatx16 (&s)[2], const uint8_t* Ks, const FixedCtx& c) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fr->k(Ks, kb, 0, c.hi), c.qf[0], floatx16{}, 0, 0, 0);
-#pragma unroll
-  for (int kk = 1; kk < 8; ++kk)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fr->k(Ks, kb, kk, c.hi), c.qf[kk], s[kb], 0, 0, 0);
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// probabilities of keys 16*qq .. 16*qq+15 of a tile (block kb = qq>>1, half cc = qq&1), then O^T += V^T P^T
-__device__ __forceinline__ void prob_quarter(const floatx16 (&cur)[2], int qq, floatx16 (&o)[4], float (&lsum)[4],
-                                             const uint8_t* Vs, const FixedCtx& c) {
-  const int kb = qq >> 1, cc = qq & 1;
-  bf16x8 pv;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pv[e] = (__bf16)fast_exp2(cur[kb][8 * cc + e]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16x2 pair;
-    pair[0] = pv[2 * e];
-    pair[1] = pv[2 * e + 1];
-    lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, c.ones2, lsum[e], false);
-  }
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fr->v(Vs, db, kb, cc, c.l32, c.hi), pv, o[db], 0, 0, 0);
+// 16 bytes per lane from global memory straight into LDS (buffer form):
+// base wave-uniform, voff the lane's byte offset, soff a uniform byte
+// offset; lane L lands at dst + 16 L.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t soff, lds_ptr_t dst) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __global__ void __launch_bounds__(kNW * 64, 1)
     k_attn_fixed(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
@@ -345,17 +330,20 @@ __global__ void __launch_bounds__(kNW * 64, 1)
                  const int32_t* __restrict__ list_pad, const int32_t* __restrict__ meta,
                  const float* __restrict__ kmax, int32_t* __restrict__ wg_flag, int S, int H, int stride,
                  float c_log2, int n_qt, int total) {
-  constexpr int KB = TileWalk::KT_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * KB];  // K0 K1 V0 V1
-  __shared__ int s_big;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // One LDS object only: with a second one the compiler tags LDS accesses with
+  // alias scopes and then makes every fragment read wait for the DMA just
+  // issued into the same object. The flag word sits after the slots.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kRing * kTileBytes + 16];  // K slots, V^T slots, flag
+  int& s_big = *reinterpret_cast<int*>(lds + 2 * kRing * kTileBytes);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const WgPos wp = wg_pos(n_qt, total);
   const int h = wp.bh % H, b = wp.bh / H;
   const int qw0 = wp.qt * kQG + wid * 32;
   const int qr = qw0 + l32;
 
-  // ---- q scaled by scale*log2(e), rounded to bf16; its norm gives the reference
+  // ---- q scaled by scale*log2(e), rounded to bf16; its norm gives the bound
   bf16x8 qf[8];
   float qsq = 0.f;
   {
@@ -367,19 +355,19 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       bf16x8 v;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const __bf16 a = (__bf16)(__uint_as_float(raw[w] << 16) * c_log2);
-        const __bf16 c = (__bf16)(__uint_as_float(raw[w] & 0xffff0000u) * c_log2);
-        v[2 * w] = a;
-        v[2 * w + 1] = c;
-        const float fa = (float)a, fc = (float)c;
-        qsq += fa * fa + fc * fc;
+        const __bf16 x0 = (__bf16)(__uint_as_float(raw[w] << 16) * c_log2);
+        const __bf16 x1 = (__bf16)(__uint_as_float(raw[w] & 0xffff0000u) * c_log2);
+        v[2 * w] = x0;
+        v[2 * w + 1] = x1;
+        const float f0 = (float)x0, f1 = (float)x1;
+        qsq += f0 * f0 + f1 * f1;
       }
       qf[kk] = v;
     }
   }
   qsq += __shfl_xor(qsq, 32, 64);
-  const int qd = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
-  const float bound = sqrtf(qsq) * kmax[2 * wp.bh + qd] * 1.001f + 1e-6f;
+  const int qdoc = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
+  const float bound = sqrtf(qsq) * kmax[2 * wp.bh + qdoc] * 1.001f + 1e-6f;
   if (tid == 0) s_big = 0;
   __syncthreads();
   if (__builtin_amdgcn_ballot_w64(qr < S && !(bound <= kMaxRef)) && lane == 0) atomicOr(&s_big, 1);
@@ -390,31 +378,37 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   }
   if (tid == 0) wg_flag[wp.pid] = 0;
 
-  TileWalk tw;
-  tw.init(k, vt, masks, list_real, list_pad, meta, S, stride, wp.qt, wp.bh, qw0, qr);
-  const Frag fr(l32);
-  const int n = tw.n_iter;
-
-  FixedCtx c;
-  c.fr = &fr;
-  c.qf = qf;
-  c.ones2[0] = (__bf16)1.f;
-  c.ones2[1] = (__bf16)1.f;
-  c.l32 = l32;
-  c.hi = hi;
-
-  floatx16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-
-  // The tile walk is prefetched 64 positions at a time: lane j of a block
-  // holds the tile of walk position 64 blk + j and its two document masks.
-  // A step reads what it needs with readlane from the current block or the
-  // next; when the walk enters the next block it becomes the current one
-  // (loaded 64 steps earlier) and the block after it is requested.
+  // ---- documents and the tile walk
+  const int nt = (S + kKV - 1) / kKV;
+  bool wq_real = false, wq_pad = false;  // documents among the rows of this wave's 64-row tile
+  if (qw0 < S) {
+    wq_real = masks[2 * (qw0 / kKV)] != 0;
+    wq_pad = masks[2 * (qw0 / kKV) + 1] != 0;
+  }
+  bool g_real = false, g_pad = false;
+  for (int r = wp.qt * kQG; r < wp.qt * kQG + kQG && r < S; r += kKV) {
+    g_real |= masks[2 * (r / kKV)] != 0;
+    g_pad |= masks[2 * (r / kKV) + 1] != 0;
+  }
+  const int32_t* list = nullptr;
+  const uint64_t* recs = masks;  // masks of walk position p at recs[2p], recs[2p + 1]
+  int n;
+  if (g_real && g_pad) {
+    n = nt;  // every tile
+  } else if (g_pad) {
+    list = list_pad;
+    recs = masks + 4 * nt;
+    n = meta[1];
+  } else {
+    list = list_real;
+    recs = masks + 2 * nt;
+    n = meta[0];
+  }
+  // The walk is prefetched 64 positions at a time: lane j of a block holds
+  // the tile of position 64 blk + j and its two document masks; a step reads
+  // what it needs with readlane from the current block or the next. When the
+  // walk enters the next block, that one (loaded 64 steps earlier) becomes
+  // current and the block after it is requested.
   struct Ahead {
     int t;
     uint64_t mr, mp;
@@ -427,13 +421,13 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     Blk r;
     int pos = blk * 64 + lane;
     pos = pos < n ? pos : n - 1;
-    r.t = tw.list ? tw.list[pos] : pos;
-    r.m = *reinterpret_cast<const u32x4*>(tw.recs + 2 * pos);
+    r.t = list ? list[pos] : pos;
+    r.m = *reinterpret_cast<const u32x4*>(recs + 2 * pos);
     return r;
   };
   Blk bcur = load_blk(0), bnext = load_blk(1);
-  // position pos of block cb (bcur) or cb + 1 (bnext)
-  auto at = [&](int pos, int cb) {
+  auto at = [&](int pos, int cb) {  // pos past the end: the last position
+    pos = pos < n ? pos : n - 1;
     const bool nx = (pos >> 6) != cb;
     const int l = pos & 63;
     Ahead a;
@@ -446,73 +440,174 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     a.mp = (uint64_t)m2 | ((uint64_t)m3 << 32);
     return a;
   };
-  auto mask_tile = [&](floatx16(&sc)[2], const Ahead& a) {
-    const bool clean = (tw.wq_real && !tw.wq_pad && a.mr == ~0ull) || (tw.wq_pad && !tw.wq_real && a.mp == ~0ull);
-    if (!clean) apply_doc_mask(sc, tw.qdoc ? a.mp : a.mr, hi);
+
+  // ---- DMA: wave w fills rows [8w, 8w+8) of a K tile and rows [16w, 16w+16)
+  // of a V^T tile (two 1 KiB instructions each), swizzled as the readers expect
+  const bf16_t* kh = k + (long)wp.bh * stride * HD;
+  const bf16_t* vh = vt + (long)wp.bh * HD * stride;
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int kr = 8 * wid + 4 * j + lane / 16;
+    koff[j] = (uint32_t)((kr * HD + ((lane % 16) ^ kswz(kr)) * 8) * 2);
+    const int vr = 16 * wid + 8 * j + lane / 8;
+    voff[j] = (uint32_t)(((long)vr * stride + ((lane % 8) ^ vswz(vr)) * 8) * 2);
+  }
+  auto kslot = [&](int s) { return lds + s * kTileBytes; };
+  auto vslot = [&](int s) { return lds + (kRing + s) * kTileBytes; };
+  auto dma_k = [&](int t, int s) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma16(kh, koff[j], (uint32_t)t * kTileBytes, (lds_ptr_t)(kslot(s) + (8 * wid + 4 * j) * 256));
   };
-  // one pipelined step: scores of tile it+1 into nxt, probabilities and O^T of tile it from cur
-  auto step = [&](int it, floatx16(&cur)[2], floatx16(&nxt)[2]) {
-    const int cb = (it + 1) >> 6;
-    if (((it + 1) & 63) == 0) {  // the walk enters block cb: positions below it + 1 are done with
+  auto dma_v = [&](int t, int s) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dma16(vh, voff[j], (uint32_t)t * (kKV * 2), (lds_ptr_t)(vslot(s) + (16 * wid + 8 * j) * 128));
+  };
+  // values of keys >= S in V^T slot s (tile t) set to zero: rows [16w, 16w+16)
+  auto zero_tail = [&](int t, int s) {
+    const int valid = S - t * kKV;  // keys of the tile below S (1..63)
+    uint8_t* base = vslot(s);
+    for (int e = lane; e < 16 * kKV; e += 64) {
+      const int r = 16 * wid + e / kKV, key = e % kKV;
+      if (key >= valid)
+        *reinterpret_cast<uint16_t*>(base + r * 128 + (((key / 8) ^ vswz(r)) << 4) + (key % 8) * 2) = 0;
+    }
+  };
+
+  const Frag fr(l32);
+  floatx16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+  bf16x2 ones2;
+  ones2[0] = (__bf16)1.f;
+  ones2[1] = (__bf16)1.f;
+
+  auto mask_tile = [&](floatx16(&sc)[2], const Ahead& a) {
+    const bool clean = (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
+    if (!clean) apply_doc_mask(sc, qdoc ? a.mp : a.mr, hi);
+  };
+  // probabilities of keys 16 qq .. 16 qq + 15 (block qq/2, half qq%2)
+  auto probs = [&](const floatx16(&sc)[2], int qq) {
+    const int kb = qq >> 1, cc = qq & 1;
+    bf16x8 pv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] = (__bf16)fast_exp2(sc[kb][8 * cc + e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16x2 pair;
+      pair[0] = pv[2 * e];
+      pair[1] = pv[2 * e + 1];
+      lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, lsum[e], false);
+    }
+    return pv;
+  };
+  // MFMA i of a step (i < 32): even i = score MFMA (block i/16, K step (i%16)/2)
+  // of the next tile, odd i = O^T MFMA (value rows block ((i%16)/2)/2, key
+  // half ((i%16)/2)%2 of block i/16) of this tile
+  auto frag = [&](const uint8_t* Kn, const uint8_t* Vc, int i) {
+    const int kb = i / 16, j = (i % 16) / 2;
+    return (i % 2 == 0) ? fr.k(Kn, kb, j, hi) : fr.v(Vc, j / 2, kb, j % 2, l32, hi);
+  };
+  // A step of the walk. On entry sc holds the scores of tile j (index tj).
+  auto enter = [&](int j, int& tj, Ahead& a1) {
+    const int cb = (j + 1) >> 6;
+    if (((j + 1) & 63) == 0) {  // the walk enters block cb
       bcur = bnext;
       bnext = load_blk(cb + 1);
+      // wait here, once per 64 steps, so that no later instruction of the
+      // loop has to assume these loads are still in flight
+      wait_vmcnt<0>();
     }
-    const Ahead a1 = at(it + 1, cb);
-    const int t2 = at(it + 2 < n ? it + 2 : n - 1, cb).t;  // the repeat at the end is never read
-    tw.gload_k(t2);
-    tw.gload_v(a1.t);
-    const uint8_t* Kn = lds + ((it + 1) & 1) * KB;
-    const uint8_t* Vc = lds + 2 * KB + (it & 1) * KB;
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int kb = qq >> 1, k0 = (qq & 1) * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = k0 + j;
-        nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(Kn, kb, kk, hi), qf[kk], kk == 0 ? floatx16{} : nxt[kb],
-                                                          0, 0, 0);
-      }
-      prob_quarter(cur, qq, o, lsum, Vc, c);
+    a1 = at(j + 1, cb);
+    const int t2 = at(j + 2, cb).t, t3 = at(j + 3, cb).t;  // past the end: the last tile again, never read
+    wait_vmcnt<4>();  // own DMA of K(j+1), V(j) landed; K(j+2), V(j+1) may be in flight
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    if (tj * kKV + kKV > S) {  // the tile holding key S-1: zero the values of keys >= S
+      zero_tail(tj, j % kRing);
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
     }
-    mask_tile(nxt, a1);
-    tw.lstore_k(lds + (it & 1) * KB);
-    tw.lstore_v(lds + 2 * KB + ((it + 1) & 1) * KB);
-    __syncthreads();
+    dma_k(t3, j % kRing);        // K(j+3) into the slot of K(j)
+    dma_v(t2, (j + 2) % kRing);  // V(j+2) into the slot of V(j-1)
   };
-  auto last = [&](int it, floatx16(&cur)[2]) {
-    const uint8_t* Vc = lds + 2 * KB + (it & 1) * KB;
+  auto step = [&](int j, floatx16(&sc)[2], int& tj) {
+    Ahead a1;
+    enter(j, tj, a1);
+    const uint8_t* Kn = kslot((j + 1) % kRing);
+    const uint8_t* Vc = vslot(j % kRing);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 F[32];
+    bf16x8 P[4];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) prob_quarter(cur, qq, o, lsum, Vc, c);
+    for (int i = 0; i < kAhead; ++i) F[i] = frag(Kn, Vc, i);
+    P[0] = probs(sc, 0);
+    P[1] = probs(sc, 1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + kAhead < 32) F[i + kAhead] = frag(Kn, Vc, i + kAhead);
+      if (i == 16) {  // before the next tile's scores overwrite block 1
+        P[2] = probs(sc, 2);
+        P[3] = probs(sc, 3);
+      }
+      const int kb = i / 16, jj = (i % 16) / 2;
+      if (i % 2 == 0)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], qf[jj], jj == 0 ? floatx16{} : sc[kb], 0, 0, 0);
+      else
+        o[jj / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], P[2 * kb + jj % 2], o[jj / 2], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + kAhead < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mask_tile(sc, a1);
+    tj = a1.t;
   };
 
   if (n > 0) {
-    // ---- prologue: K0 = K(0), V0 = V(0), K1 = K(1); scores of tile 0
     const Ahead a0 = at(0, 0);
-    const int t1 = at(n > 1 ? 1 : 0, 0).t;
-    tw.gload_k(a0.t);
-    tw.gload_v(a0.t);
-    tw.lstore_k(lds);
-    tw.lstore_v(lds + 2 * KB);
-    if (n > 1) {
-      tw.gload_k(t1);
-      tw.lstore_k(lds + KB);
-    }
-    __syncthreads();
-    floatx16 sa[2], sb[2];
-    scores_full(sa, lds, c);
-    mask_tile(sa, a0);
-    int it = 0;
-    for (; it + 2 < n; it += 2) {
-      step(it, sa, sb);
-      step(it + 1, sb, sa);
-    }
-    if (it + 1 < n) {
-      step(it, sa, sb);
-      last(it + 1, sb);
-    } else {
-      last(it, sa);
+    const int t1 = at(1, 0).t, t2 = at(2, 0).t;
+    dma_k(a0.t, 0);
+    dma_v(a0.t, 0);
+    dma_k(t1, 1);
+    dma_v(t1, 1);
+    dma_k(t2, 2);
+    wait_vmcnt<8>();  // own K(0)
+    __builtin_amdgcn_s_barrier();
+    floatx16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(kslot(0), kb, 0, hi), qf[0], floatx16{}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < 8; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(kslot(0), kb, kk, hi), qf[kk], sc[kb], 0, 0, 0);
+    mask_tile(sc, a0);
+    int tj = a0.t;
+    for (int j = 0; j < n - 1; ++j) step(j, sc, tj);
+    // last tile: probabilities and O^T only
+    Ahead a1;
+    enter(n - 1, tj, a1);
+    const uint8_t* Vc = vslot((n - 1) % kRing);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const bf16x8 pv = probs(sc, qq);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vc, db, qq >> 1, qq & 1, l32, hi), pv, o[db], 0, 0, 0);
     }
   }
+  wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
   store_out(out, o, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]), S, H, b, h, qr, hi);
 }
 
