@@ -10,9 +10,9 @@
 //
 // bf16 kernels (gfx950), flash-style, fp32 softmax:
 //   * a workgroup is 8 waves x 32 queries of one head; q stays in registers;
-//   * K tiles [64 keys][128] and V^T tiles [128][64 keys] are staged in LDS
-//     (2 stages, XOR-swizzled 16-byte chunks); the next tile's global loads
-//     are in flight while the current one is used;
+//   * K tiles [64 keys][128] and V^T tiles [128][64 keys] reach LDS by
+//     buffer->LDS DMA (XOR-swizzled 16-byte chunks) through rings of three
+//     slots, two to three tiles ahead of their use;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
 //     so each lane owns one query column and all per-query state is
 //     per-lane. Key rows enter the MFMA in an order (bits 2 and 3 of the row
