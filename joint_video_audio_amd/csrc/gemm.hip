@@ -15,8 +15,10 @@
 // SIMD, each 128x128 as 4x4 v_mfma_f32_32x32x16_bf16 accumulators in AGPRs.
 // Operands reach LDS by direct buffer->LDS DMA in K steps of 64 through a
 // ring of five 32 KiB slots (the A and W halves of a step are loaded at
-// different times, see the kernel); fragments are read one MFMA step ahead
-// and the instruction order inside a step is fixed with sched_group_barrier.
+// different times, see the kernel); fragments are read one MFMA step ahead.
+// The issue order inside a step is fixed instruction group by instruction
+// group (sched_barrier fences): one DMA instruction per four MFMAs, so the
+// four waves of a CU never queue a burst of DMA at the address unit.
 // One barrier per K step. Tiles are ordered so that the workgroups an XCD
 // runs together share A and W panels in its L2. Plain (store) tiles are
 // staged in LDS and written as whole contiguous rows.
@@ -135,8 +137,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// sched_group_barrier masks
-constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
 
 // 256 x 256 output tile per workgroup of four waves; wave (wm, wn) owns the
 // 128 x 128 block at (128 wm, 128 wn) as 4 x 4 v_mfma_f32_32x32x16_bf16
@@ -145,13 +145,12 @@ constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
 // K advances in steps of 64. The A and W operands of a step each fill one
 // 32 KiB slot of a 5-slot LDS ring (slot of A_k: 2k mod 5, W_k: 2k + 1 mod
 // 5), loaded by direct buffer->LDS DMA. Within step k the four MFMA steps
-// (K 16 each) read their fragments one MFMA step ahead. A_{k+2} is loaded
-// during the first two MFMA steps of k (its slot held W_{k-1}); after the
-// third, every wave waits for its own DMA of step k + 1 and one barrier
-// publishes it and frees A_k's and W_k's slots; W_{k+2} is then loaded into
-// A_k's slot while the last MFMA step of k runs. A_k therefore has about two
-// K steps to arrive, W_k one, and no more than half a step of DMA is ever
-// queued behind a barrier.
+// (K 16 each) read their fragments one MFMA step ahead. Each wave issues
+// one DMA instruction per four MFMAs: the second half of W_{k+1} during
+// MFMA step 0, A_{k+2} during steps 1 and 2 (its slot held W_{k-1}); after
+// step 2 every wave waits for its own DMA of step k + 1 and one barrier
+// publishes it and frees A_k's and W_k's slots; the first half of W_{k+2}
+// then goes into A_k's slot during step 3.
 template <int EPI>
 __global__ void __launch_bounds__(64 * kWaves, 1)
     k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
@@ -204,19 +203,17 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   auto slot_ptr = [&](int s) { return lds + s * kSlotBytes; };
   // DMA instructions j0 .. j1-1 of operand A (or W) of K step k into slot s;
   // past the end of K the last step is loaded again (the slot is free).
-  auto dma_a = [&](int k, int j0, int j1) {
+  // DMA instruction j of operand A (or W) of K step k into its ring slot;
+  // past the end of K the last step is loaded again (the slot is free).
+  auto dma_a1 = [&](int k, int j) {
     const int s = (2 * k) % kSlots;
     const uint32_t soff = (uint32_t)((k < KT ? k : KT - 1) * kRowBytes);
-#pragma unroll
-    for (int j = j0; j < j1; ++j)
-      dma16(A, voff_a[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+    dma16(A, voff_a[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
   };
-  auto dma_w = [&](int k) {
+  auto dma_w1 = [&](int k, int j) {
     const int s = (2 * k + 1) % kSlots;
     const uint32_t soff = (uint32_t)((k < KT ? k : KT - 1) * kRowBytes);
-#pragma unroll
-    for (int j = 0; j < kIPW; ++j)
-      dma16(W, voff_w[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+    dma16(W, voff_w[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
   };
 
   floatx16 acc[MI][NI];
@@ -230,79 +227,81 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   // fragment reads: row (lane & 31) of a 32-row block, chunk 2 kk + (lane >> 5)
   const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = gemm_swz(fr_row);
   bf16x8 fa[2][MI], fw[2][NI];
-  auto read_frags = [&](int k, int kk, int slot) {
-    const uint8_t* As = slot_ptr((2 * k) % kSlots);
-    const uint8_t* Ws = slot_ptr((2 * k + 1) % kSlots);
+  // fragment r (0..7) of MFMA step kk of K step k into register set `set`, in
+  // the order the MFMAs use them: a0 w0 w1 w2 w3 a1 a2 a3
+  auto read_frag = [&](int k, int kk, int set, int r) {
     const int chunk = ((2 * kk + fr_hi) ^ fr_sw) << 4;
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-      fw[slot][ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * kRowBytes + chunk);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      fa[slot][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * kRowBytes + chunk);
-  };
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[slot][ni], fa[slot][mi], acc[mi][ni], 0, 0, 0);
-  };
-  // instruction order of one MFMA step: its 16 MFMAs with the next step's
-  // 8 fragment reads and `dma` DMA instructions slotted between the first 8
-  auto sched = [&](int dma) {
-#pragma unroll
-    for (int i = 0; i < MI + NI; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      if (i < dma) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    if (r >= 1 && r <= NI) {
+      const uint8_t* Ws = slot_ptr((2 * k + 1) % kSlots);
+      const int ni = r - 1;
+      fw[set][ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * kRowBytes + chunk);
+    } else {
+      const uint8_t* As = slot_ptr((2 * k) % kSlots);
+      const int mi = r == 0 ? 0 : r - NI;
+      fa[set][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * kRowBytes + chunk);
     }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, MI * NI - (MI + NI), 0);
   };
-  static_assert(kIPW == MI + NI, "one DMA per slotted MFMA in the last step");
+  auto read_frags = [&](int k, int kk, int set) {
+#pragma unroll
+    for (int r = 0; r < MI + NI; ++r) read_frag(k, kk, set, r);
+  };
+  auto mfma1 = [&](int set, int i) {
+    const int mi = i / NI, ni = i % NI;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
+  };
+  // One MFMA step in a fixed issue order: MFMA i, then (i < 8) fragment i of
+  // the next step, then (i % 4 == 3) one DMA instruction; each group is
+  // fenced so the DMA of the four waves reaches the address unit evenly.
+  auto step = [&](int set, int nk, int nkk, bool reads, int dk, bool dw, int dj) {
+#pragma unroll
+    for (int i = 0; i < MI * NI; ++i) {
+      mfma1(set, i);
+      if (reads && i < MI + NI) read_frag(nk, nkk, set ^ 1, i);
+      if (dk >= 0 && (i & 3) == 3) {
+        if (dw)
+          dma_w1(dk, dj + (i >> 2));
+        else
+          dma_a1(dk, dj + (i >> 2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  static_assert(kIPW == 8 && MI * NI == 16, "four DMA instructions per MFMA step");
 
-  // ---- prologue: A0 W0 A1 W1 in flight, wait for step 0
-  dma_a(0, 0, kIPW);
-  dma_w(0);
-  dma_a(1, 0, kIPW);
-  dma_w(1);
-  wait_vmcnt<2 * kIPW>();
+  // ---- prologue: A0 W0 A1 and the first half of W1 in flight, wait for step 0
+#pragma unroll
+  for (int j = 0; j < kIPW; ++j) dma_a1(0, j);
+#pragma unroll
+  for (int j = 0; j < kIPW; ++j) dma_w1(0, j);
+#pragma unroll
+  for (int j = 0; j < kIPW; ++j) dma_a1(1, j);
+#pragma unroll
+  for (int j = 0; j < kIPW / 2; ++j) dma_w1(1, j);
+  wait_vmcnt<kIPW + kIPW / 2>();
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0, 0);
 
+  // K step kt: the second half of W_{kt+1} during MFMA step 0, A_{kt+2}
+  // during steps 1 and 2 (its slot held W_{kt-1}); then each wave waits for
+  // its own DMA of step kt + 1 and one barrier publishes it and frees the
+  // slots of A_kt and W_kt; the first half of W_{kt+2} goes into A_kt's slot
+  // during step 3.
   for (int kt = 0; kt < KT - 1; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
-    dma_a(kt + 2, 0, kIPW / 2);
-    read_frags(kt, 1, 1);
-    mfmas(0);
-    sched(kIPW / 2);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_a(kt + 2, kIPW / 2, kIPW);
-    read_frags(kt, 2, 0);
-    mfmas(1);
-    sched(kIPW / 2);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(kt, 3, 1);
-    mfmas(0);
-    sched(0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kIPW>();  // A_{kt+1}, W_{kt+1} landed; A_{kt+2} may be in flight
+    step(0, kt, 1, true, kt + 1, true, kIPW / 2);
+    step(1, kt, 2, true, kt + 2, false, 0);
+    step(0, kt, 3, true, kt + 2, false, kIPW / 2);
+    wait_vmcnt<kIPW>();  // W_{kt+1} landed; A_{kt+2} may be in flight
     wait_lgkm0();        // this wave's reads of step kt are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    dma_w(kt + 2);
-    read_frags(kt + 1, 0, 0);
-    mfmas(1);
-    sched(kIPW);
+    step(1, kt + 1, 0, true, kt + 2, true, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  read_frags(KT - 1, 1, 1);
-  mfmas(0);
-  read_frags(KT - 1, 2, 0);
-  mfmas(1);
-  read_frags(KT - 1, 3, 1);
-  mfmas(0);
-  mfmas(1);
+  step(0, KT - 1, 1, true, -1, false, 0);
+  step(1, KT - 1, 2, true, -1, false, 0);
+  step(0, KT - 1, 3, true, -1, false, 0);
+  step(1, 0, 0, false, -1, false, 0);
   wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
 
   // ---- epilogue. The plain output goes through LDS (the ring is free now)
