@@ -11,8 +11,8 @@
 // bf16 kernels (gfx950), flash-style, fp32 softmax:
 //   * a workgroup is 8 waves x 32 queries of one head; q stays in registers;
 //   * K tiles [64 keys][128] and V^T tiles [128][64 keys] reach LDS by
-//     buffer->LDS DMA (XOR-swizzled 16-byte chunks) through rings of three
-//     slots, two to three tiles ahead of their use;
+//     buffer->LDS DMA (XOR-swizzled 16-byte chunks) through rings of four
+//     slots, three to four tiles ahead of their use;
 //   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
 //     so each lane owns one query column and all per-query state is
 //     per-lane. Key rows enter the MFMA in an order (bits 2 and 3 of the row
@@ -243,6 +243,14 @@ __device__ __forceinline__ void apply_doc_mask(floatx16 (&s)[2], uint64_t msel, 
   }
 }
 
+__device__ __forceinline__ void apply_doc_mask_half(floatx16& s, uint64_t msel, int hi, int kb) {
+  const uint32_t m32 = (uint32_t)(msel >> (kb * 32 + 8 * hi));
+  const uint32_t b16 = (m32 & 0xffu) | ((m32 >> 8) & 0xff00u);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (!((b16 >> r) & 1u)) s[r] = -INFINITY;
+}
+
 __device__ __forceinline__ void store_out(bf16_t* out, const floatx16 (&o)[4], float l_run, int S, int H, int b,
                                           int h, int qr, int hi) {
   const float lt = l_run + __shfl_xor(l_run, 32, 64);
@@ -297,16 +305,17 @@ __global__ void k_zero_f32(float* p, int n) {
 }
 
 // ---------------------------------------------------------------- fixed-reference kernel
-// K and V^T tiles reach LDS by buffer->LDS DMA through rings of three slots,
-// two tiles ahead of their use; one barrier per tile. Per tile a wave runs
-// 32 MFMAs, alternating the score MFMAs of the next tile with the O^T MFMAs
-// of this one, and issues their 32 fragment reads kAhead MFMAs early; the
-// first reads of a tile overlap the exponentials, which need no LDS. The
-// scores of a tile live in one register set: each 32-key half becomes
-// probabilities before the next tile's scores overwrite it.
-constexpr int kRing = 3;
+// K and V^T tiles reach LDS by buffer->LDS DMA through rings of four slots
+// (K four tiles ahead of its use, V three); one barrier per tile publishes
+// the tiles of the step after next, so the fragment reads run kAhead MFMAs
+// ahead without a break: the first reads of a step are issued before its
+// barrier. Per tile a wave runs 32 MFMAs, alternating the score MFMAs of the
+// next tile with the O^T MFMAs of this one. The scores of a tile live in one
+// register set; each 32-key half becomes probabilities while the MFMAs of
+// the other half run (the exponentials never wait for a barrier).
+constexpr int kRing = 4;
 constexpr int kTileBytes = kKV * HD * 2;  // one K or V^T tile: 16 KiB
-constexpr int kAhead = 6;                 // fragment reads in flight ahead of the MFMAs
+constexpr int kAhead = 4;                 // fragment reads in flight ahead of the MFMAs
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -323,6 +332,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
 
 __global__ void __launch_bounds__(kNW * 64, 1)
     k_attn_fixed(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
@@ -491,6 +505,10 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     const bool clean = (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
     if (!clean) apply_doc_mask(sc, qdoc ? a.mp : a.mr, hi);
   };
+  auto mask_half = [&](floatx16& s, const Ahead& a, int kb) {
+    const bool clean = (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
+    if (!clean) apply_doc_mask_half(s, qdoc ? a.mp : a.mr, hi, kb);
+  };
   // probabilities of keys 16 qq .. 16 qq + 15 (block qq/2, half qq%2)
   auto probs = [&](const floatx16(&sc)[2], int qq) {
     const int kb = qq >> 1, cc = qq & 1;
@@ -514,7 +532,11 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     return (i % 2 == 0) ? fr.k(Kn, kb, j, hi) : fr.v(Vc, j / 2, kb, j % 2, l32, hi);
   };
   // A step of the walk. On entry sc holds the scores of tile j (index tj).
-  auto enter = [&](int j, int& tj, Ahead& a1) {
+  // Entering step j of the walk: every wave waits for its own DMA of K(j+2)
+  // and V(j+1) and for its reads of step j - 1 (the first kAhead reads of
+  // step j, issued at the end of step j - 1, may still be in flight); one
+  // barrier publishes K(j+2), V(j+1) and frees the slots of K(j) and V(j-1).
+  auto enter = [&](int j, Ahead& a1) {
     const int cb = (j + 1) >> 6;
     if (((j + 1) & 63) == 0) {  // the walk enters block cb
       bcur = bnext;
@@ -524,65 +546,97 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       wait_vmcnt<0>();
     }
     a1 = at(j + 1, cb);
-    const int t2 = at(j + 2, cb).t, t3 = at(j + 3, cb).t;  // past the end: the last tile again, never read
-    wait_vmcnt<4>();  // own DMA of K(j+1), V(j) landed; K(j+2), V(j+1) may be in flight
-    wait_lgkm0();
+    const int t3 = at(j + 3, cb).t, t4 = at(j + 4, cb).t;  // past the end: the last tile again, never read
+    wait_vmcnt<4>();
+    wait_lgkm<kAhead>();
     __builtin_amdgcn_s_barrier();
-    if (tj * kKV + kKV > S) {  // the tile holding key S-1: zero the values of keys >= S
-      zero_tail(tj, j % kRing);
+    if (a1.t * kKV + kKV > S) {  // V(j+1) holds key S-1: zero the values of keys >= S before it is read
+      zero_tail(a1.t, (j + 1) % kRing);
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
     }
-    dma_k(t3, j % kRing);        // K(j+3) into the slot of K(j)
-    dma_v(t2, (j + 2) % kRing);  // V(j+2) into the slot of V(j-1)
+    dma_k(t4, j % kRing);        // K(j+4) into the slot of K(j)
+    dma_v(t3, (j + 3) % kRing);  // V(j+3) into the slot of V(j-1)
   };
-  auto step = [&](int j, floatx16(&sc)[2], int& tj) {
+  // A step of the walk. On entry sc holds the scores of tile j (the first
+  // half already turned into P[0], P[1], the second half masked) and G the
+  // first kAhead fragments of the step. MFMAs 0..15 run the first half of
+  // the next tile's scores and the O^T MFMAs of P[0], P[1] while the second
+  // half of tile j becomes P[2], P[3]; MFMAs 16..31 run the second half of
+  // the scores and the O^T MFMAs of P[2], P[3] while the (masked) first half
+  // of the next tile becomes its P[0], P[1]. The last kAhead reads fetch the
+  // first fragments of step j + 1, whose tiles the barrier of step j published.
+  auto step = [&](int j, floatx16(&sc)[2], bf16x8(&P)[4], bf16x8(&G)[kAhead]) {
     Ahead a1;
-    enter(j, tj, a1);
+    enter(j, a1);
     const uint8_t* Kn = kslot((j + 1) % kRing);
     const uint8_t* Vc = vslot(j % kRing);
+    const uint8_t* Kn2 = kslot((j + 2) % kRing);
+    const uint8_t* Vc2 = vslot((j + 1) % kRing);
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 F[32];
-    bf16x8 P[4];
+    bf16x8 F[32 + kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) F[i] = frag(Kn, Vc, i);
-    P[0] = probs(sc, 0);
-    P[1] = probs(sc, 1);
+    for (int i = 0; i < kAhead; ++i) F[i] = G[i];
+    auto rd = [&](int i) { F[i] = i < 32 ? frag(Kn, Vc, i) : frag(Kn2, Vc2, i - 32); };
+    P[2] = probs(sc, 2);
+    P[3] = probs(sc, 3);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i + kAhead < 32) F[i + kAhead] = frag(Kn, Vc, i + kAhead);
-      if (i == 16) {  // before the next tile's scores overwrite block 1
-        P[2] = probs(sc, 2);
-        P[3] = probs(sc, 3);
-      }
-      const int kb = i / 16, jj = (i % 16) / 2;
+    for (int i = 0; i < 16; ++i) {
+      rd(i + kAhead);
+      const int jj = i / 2;
       if (i % 2 == 0)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], qf[jj], jj == 0 ? floatx16{} : sc[kb], 0, 0, 0);
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], qf[jj], jj == 0 ? floatx16{} : sc[0], 0, 0, 0);
       else
-        o[jj / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], P[2 * kb + jj % 2], o[jj / 2], 0, 0, 0);
+        o[jj / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], P[jj % 2], o[jj / 2], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i + kAhead < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
     __builtin_amdgcn_sched_barrier(0);
-    mask_tile(sc, a1);
-    tj = a1.t;
+    mask_half(sc[0], a1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 Pn0 = probs(sc, 0), Pn1 = probs(sc, 1);
+#pragma unroll
+    for (int i = 16; i < 32; ++i) {
+      rd(i + kAhead);
+      const int jj = (i % 16) / 2;
+      if (i % 2 == 0)
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], qf[jj], jj == 0 ? floatx16{} : sc[1], 0, 0, 0);
+      else
+        o[jj / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], P[2 + jj % 2], o[jj / 2], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 16; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) G[i] = F[32 + i];
+    P[0] = Pn0;
+    P[1] = Pn1;
+    mask_half(sc[1], a1, 1);
   };
 
   if (n > 0) {
     const Ahead a0 = at(0, 0);
-    const int t1 = at(1, 0).t, t2 = at(2, 0).t;
+    const int t1 = at(1, 0).t, t2 = at(2, 0).t, t3 = at(3, 0).t;
     dma_k(a0.t, 0);
-    dma_v(a0.t, 0);
     dma_k(t1, 1);
-    dma_v(t1, 1);
+    dma_v(a0.t, 0);
     dma_k(t2, 2);
-    wait_vmcnt<8>();  // own K(0)
+    dma_v(t1, 1);
+    dma_k(t3, 3);
+    dma_v(t2, 2);
+    wait_vmcnt<8>();  // own K(0), K(1), V(0)
     __builtin_amdgcn_s_barrier();
+    if (a0.t * kKV + kKV > S) {
+      zero_tail(a0.t, 0);
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+    }
     floatx16 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -593,19 +647,25 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       for (int kb = 0; kb < 2; ++kb)
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(kslot(0), kb, kk, hi), qf[kk], sc[kb], 0, 0, 0);
     mask_tile(sc, a0);
-    int tj = a0.t;
-    for (int j = 0; j < n - 1; ++j) step(j, sc, tj);
-    // last tile: probabilities and O^T only
-    Ahead a1;
-    enter(n - 1, tj, a1);
-    const uint8_t* Vc = vslot((n - 1) % kRing);
+    bf16x8 P[4];
+    P[0] = probs(sc, 0);
+    P[1] = probs(sc, 1);
+    bf16x8 G[kAhead];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const bf16x8 pv = probs(sc, qq);
+    for (int i = 0; i < kAhead; ++i) G[i] = frag(kslot(1), vslot(0), i);
+    for (int j = 0; j < n - 1; ++j) step(j, sc, P, G);
+    // last tile: O^T only (its values were made visible, and their tail
+    // zeroed, when step n - 2 was entered)
+    Ahead a1;
+    enter(n - 1, a1);
+    const uint8_t* Vc = vslot((n - 1) % kRing);
+    P[2] = probs(sc, 2);
+    P[3] = probs(sc, 3);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vc, db, qq >> 1, qq & 1, l32, hi), pv, o[db], 0, 0, 0);
-    }
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vc, db, qq >> 1, qq & 1, l32, hi), P[qq], o[db], 0, 0, 0);
   }
   wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
   store_out(out, o, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]), S, H, b, h, qr, hi);
