@@ -240,19 +240,21 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       HIPCHECK(launch_gemm<T>(kEpiStore, a, (const T*)bw.w_qkv, qkv, M, 3 * Wd, D, ea, st));
     }
     {
+      // bf16: the same pass records the key norms the attention kernel needs
       Timed tm(prof, kKQKNormRope, st);
+      float* kmax = nullptr;
+      if (sizeof(T) == 2) {
+        kmax = static_cast<float*>(w.attn_scratch);
+        HIPCHECK(launch_zero_f32(kmax, 2 * B * H, st));
+      }
       HIPCHECK(launch_qk_norm_rope<T>(qkv, bw.q_norm, bw.k_norm, L->position_ids, qn, kn, vt, B, S, H, Sp,
-                                      c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st));
+                                      c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st, w.masks, kmax));
     }
     if (tap) {
       const size_t hb = (size_t)B * H * Sp * hd * e;
       if (taps->q_rot) HIPCHECK(hipMemcpyAsync(taps->q_rot, qn, hb, hipMemcpyDeviceToDevice, st));
       if (taps->k_rot) HIPCHECK(hipMemcpyAsync(taps->k_rot, kn, hb, hipMemcpyDeviceToDevice, st));
       if (taps->v_t) HIPCHECK(hipMemcpyAsync(taps->v_t, vt, hb, hipMemcpyDeviceToDevice, st));
-    }
-    {
-      Timed tm(prof, kKAttnPrep, st);
-      HIPCHECK(launch_attention_prep<T>(kn, w.masks, w.attn_scratch, B, S, H, Sp, st));
     }
     {
       Timed tm(prof, kKAttention, st);

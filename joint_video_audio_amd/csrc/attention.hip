@@ -836,6 +836,11 @@ size_t attention_scratch_bytes(int B, int S, int H) {
   return 8 * (size_t)B * H + 4 * n_qt * H * B;  // kmax per document + workgroup flags
 }
 
+hipError_t launch_zero_f32(float* p, int n, hipStream_t st) {
+  if (n > 0) k_zero_f32<<<(n + 255) / 256, 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
 template <>
 hipError_t launch_attention_prep<bf16_t>(const bf16_t* k, const uint64_t* masks, void* scratch, int B, int S, int H,
                                          int stride, hipStream_t st) {

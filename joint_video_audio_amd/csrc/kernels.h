@@ -47,7 +47,11 @@ hipError_t launch_cast_f32(const float* x, T* y, long n, hipStream_t st);
 template <typename T>
 hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, const int32_t* pos, T* qo, T* ko,
                                T* vto, int B, int S, int H, int stride, int fd, float theta, float eps,
-                               hipStream_t st);
+                               hipStream_t st, const uint64_t* masks = nullptr, float* kmax = nullptr);
+// kmax (bf16 only; zeroed by the caller): per (b, h) and document the largest
+// |k| of the stored keys, as launch_attention_prep computes it; masks are the
+// tile masks of launch_attn_tiles.
+hipError_t launch_zero_f32(float* p, int n, hipStream_t st);
 
 // ---- GEMM: C[M,N] = A[M,K] . W[N,K]^T with fused epilogues ----
 enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2 };

@@ -11,9 +11,14 @@
 // [2fd*a, 2fd*(a+1)) and its pair j is channels (2j, 2j+1), turned by
 // pos[a] * theta^(-j/fd); the remaining channels pass through.
 //
-// One workgroup handles 64 rows of one head. In the q/k pass lane l of a
-// wave owns channel pair l of a row, so the RMS is one wave reduction and
-// the rotation is lane-local. HBM-bound.
+// One workgroup handles 64 rows of HG heads (2 when the head count is even,
+// else 1). In the q/k pass a lane owns 16 bytes of a row (8 bf16 channels),
+// so a row's RMS is a reduction over 16 lanes done with DPP moves and the
+// rotation pairs stay inside the lane; a row's sines and cosines are taken
+// once for the HG heads.
+// On request (bf16) the pass also records, per head and document, the
+// largest |k| of the stored keys, which the attention kernel bounds its
+// scores with. HBM-bound.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,124 +28,246 @@ struct RopeFreqs {
   float inv_freq[64];
 };
 
-template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float& a, float& b) {
-    uint32_t r = *reinterpret_cast<const uint32_t*>(p);
-    a = __uint_as_float(r << 16);
-    b = __uint_as_float(r & 0xffff0000u);
+// 16 bytes of one row: CPL channels as fp32; stored() is the value a channel
+// has once written back in T.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(r[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
   }
-  static __device__ __forceinline__ void store(bf16_t* p, float a, float b) {
-    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(p) = r;
+  }
+  static __device__ __forceinline__ float stored(float x) {
+    return __uint_as_float(pack_bf16x2(x, 0.f) << 16);
   }
 };
-template <> struct Pair<float> {
-  static __device__ __forceinline__ void load(const float* p, float& a, float& b) {
-    float2 r = *reinterpret_cast<const float2*>(p);
-    a = r.x;
-    b = r.y;
+template <> struct Chunk<float> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    const floatx4 r = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = r[i];
   }
-  static __device__ __forceinline__ void store(float* p, float a, float b) {
-    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<floatx4*>(p) = floatx4{v[0], v[1], v[2], v[3]};
   }
+  static __device__ __forceinline__ float stored(float x) { return x; }
 };
 
-template <typename T>
+// Sum over the N lanes of a row (N = 16 or 32, aligned groups), result in
+// every lane of the row: DPP within 16 lanes (quad xor 1, quad xor 2, half
+// mirror, mirror), then one lane exchange across the two 16-lane halves.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(N == 16 || N == 32, "row width");
+  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dppf<0x141>(v);  // row_half_mirror
+  v += dppf<0x140>(v);  // row_mirror
+  if (N == 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
+template <typename T, int HG>
 __global__ void __launch_bounds__(256) k_qk_norm_rope(const T* __restrict__ qkv, const float* __restrict__ gq,
                                                       const float* __restrict__ gk, const int32_t* __restrict__ pos,
                                                       T* __restrict__ qo, T* __restrict__ ko, T* __restrict__ vto,
+                                                      const uint64_t* __restrict__ masks, float* __restrict__ kmax,
                                                       int S, int H, int stride, int fd, float eps, RopeFreqs fr) {
   constexpr int HD = 128;
   constexpr int VN = 16 / sizeof(T);        // elements per 16-byte chunk
   constexpr int CPR = HD / VN;              // chunks per row of one head
   constexpr int PITCH = 64 + VN;            // LDS row pitch (elements) of the transposed tile
   __shared__ T vs[HD * PITCH];
+  __shared__ float red[4][HG][2];
 
-  const int s0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int s0 = blockIdx.x * 64, h0 = blockIdx.y * HG, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int W = H * HD;
-  const long head_base = ((long)b * H + h) * stride;  // row offset of (b, h) in [B, H, stride, hd]
 
-  // ---- q and k: RMSNorm + RoPE, lane owns channels (2*lane, 2*lane+1)
-  const float gq0 = gq[2 * lane], gq1 = gq[2 * lane + 1];
-  const float gk0 = gk[2 * lane], gk1 = gk[2 * lane + 1];
-  const int axis = fd > 0 ? lane / fd : 3;
-  const bool rot = lane < 3 * fd;
-  const float invf = rot ? fr.inv_freq[lane - axis * fd] : 0.f;
-  for (int r = wid; r < 64; r += 4) {
-    const int s = s0 + r;
-    float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f;
-    if (s < S) {
-      const T* src = qkv + ((long)b * S + s) * (3L * W) + h * HD + 2 * lane;
-      Pair<T>::load(src, q0, q1);
-      Pair<T>::load(src + W, k0, k1);
-      const float rq = rsqrtf(wave_sum(q0 * q0 + q1 * q1) * (1.f / HD) + eps);
-      const float rk = rsqrtf(wave_sum(k0 * k0 + k1 * k1) * (1.f / HD) + eps);
-      q0 *= rq * gq0;
-      q1 *= rq * gq1;
-      k0 *= rk * gk0;
-      k1 *= rk * gk1;
-      if (rot) {
-        const float ang = (float)pos[3L * s + axis] * invf;
-        float sn, cs;
-        sincosf(ang, &sn, &cs);
-        float a = q0 * cs - q1 * sn, c = q0 * sn + q1 * cs;
-        q0 = a;
-        q1 = c;
-        a = k0 * cs - k1 * sn;
-        c = k0 * sn + k1 * cs;
-        k0 = a;
-        k1 = c;
+  // ---- q and k: RMSNorm + RoPE. Lane l owns the CPL channels of chunk
+  // l % LPR of row l / LPR of the wave's group of RPW rows, so one 16-byte
+  // load per tensor, sums over the LPR lanes of a row, and rotation pairs
+  // inside the lane; a row's sines and cosines serve the HG heads.
+  constexpr int CPL = 16 / sizeof(T), LPR = HD / CPL, RPW = 64 / LPR, PPL = CPL / 2;
+  const int sub = lane / LPR, cl = lane % LPR;
+  float gqv[CPL], gkv[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    gqv[e] = gq[cl * CPL + e];
+    gkv[e] = gk[cl * CPL + e];
+  }
+  int ax[PPL];
+  float invf[PPL];
+  bool rot[PPL];
+#pragma unroll
+  for (int p = 0; p < PPL; ++p) {
+    const int j = cl * PPL + p;  // rotation pair (channels 2j, 2j+1)
+    ax[p] = fd > 0 ? j / fd : 3;
+    rot[p] = j < 3 * fd;
+    invf[p] = rot[p] ? fr.inv_freq[j - ax[p] * fd] : 0.f;
+  }
+  // key norms (bf16 path): largest |k| per head and document over this tile's
+  // rows, taken from the stored values; padding rows are document 1
+  const bool norms = kmax && s0 < S;  // the tile masks cover rows below S only
+  const uint64_t mpad = norms ? masks[2 * blockIdx.x + 1] : 0ull;
+  float mx[HG][2];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) mx[hh][0] = mx[hh][1] = 0.f;
+  for (int r0 = wid * RPW; r0 < 64; r0 += 4 * RPW) {
+    const int r = r0 + sub, s = s0 + r;
+    const bool live = s < S;
+    float sn[PPL], cs[PPL];
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      sn[p] = 0.f;
+      cs[p] = 1.f;
+      if (live && rot[p]) sincosf((float)pos[3L * s + ax[p]] * invf[p], &sn[p], &cs[p]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const int h = h0 + hh;
+      const long head_base = ((long)b * H + h) * stride;  // row offset of (b, h) in [B, H, stride, hd]
+      float q[CPL], k[CPL];
+      if (live) {
+        const T* src = qkv + ((long)b * S + s) * (3L * W) + h * HD + cl * CPL;
+        Chunk<T>::load(src, q);
+        Chunk<T>::load(src + W, k);
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) q[e] = k[e] = 0.f;
+      }
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        sq += q[e] * q[e];
+        sk += k[e] * k[e];
+      }
+      const float rq = rsqrtf(row_sum<LPR>(sq) * (1.f / HD) + eps);
+      const float rk = rsqrtf(row_sum<LPR>(sk) * (1.f / HD) + eps);
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        const float q0 = q[2 * p] * rq * gqv[2 * p], q1 = q[2 * p + 1] * rq * gqv[2 * p + 1];
+        const float k0 = k[2 * p] * rk * gkv[2 * p], k1 = k[2 * p + 1] * rk * gkv[2 * p + 1];
+        q[2 * p] = q0 * cs[p] - q1 * sn[p];
+        q[2 * p + 1] = q0 * sn[p] + q1 * cs[p];
+        k[2 * p] = k0 * cs[p] - k1 * sn[p];
+        k[2 * p + 1] = k0 * sn[p] + k1 * cs[p];
+      }
+      if (!live) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) q[e] = k[e] = 0.f;
+      }
+      if (norms) {
+        float n2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const float a = Chunk<T>::stored(k[e]);
+          n2 += a * a;
+        }
+        n2 = row_sum<LPR>(n2);
+        const int d = (int)((mpad >> r) & 1ull);
+        if (live) mx[hh][d] = fmaxf(mx[hh][d], n2);
+      }
+      if (s < stride) {
+        Chunk<T>::store(qo + (head_base + s) * HD + cl * CPL, q);
+        Chunk<T>::store(ko + (head_base + s) * HD + cl * CPL, k);
       }
     }
-    if (s < stride) {
-      Pair<T>::store(qo + (head_base + s) * HD + 2 * lane, q0, q1);
-      Pair<T>::store(ko + (head_base + s) * HD + 2 * lane, k0, k1);
+  }
+  if (norms) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) mx[hh][d] = fmaxf(mx[hh][d], __shfl_xor(mx[hh][d], o, 64));
+    if (lane == 0)
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        red[wid][hh][0] = mx[hh][0];
+        red[wid][hh][1] = mx[hh][1];
+      }
+    __syncthreads();
+    if (threadIdx.x < 2 * HG) {
+      const int hh = threadIdx.x >> 1, d = threadIdx.x & 1;
+      const float m = sqrtf(fmaxf(fmaxf(red[0][hh][d], red[1][hh][d]), fmaxf(red[2][hh][d], red[3][hh][d])));
+      // non-negative floats order as ints
+      atomicMax(reinterpret_cast<int*>(kmax + 2 * ((long)b * H + h0 + hh) + d), __float_as_int(m));
     }
   }
 
-  // ---- v: [64 rows][128] -> [128][64 rows] through LDS
-  for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
-    const int r = c / CPR, d0 = (c % CPR) * VN;
-    const int s = s0 + r;
-    T tmp[VN];
-    if (s < S) {
-      const T* src = qkv + ((long)b * S + s) * (3L * W) + 2 * W + h * HD + d0;
-      *reinterpret_cast<u32x4*>(tmp) = *reinterpret_cast<const u32x4*>(src);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VN; ++e) tmp[e] = T(0);
-    }
-#pragma unroll
-    for (int e = 0; e < VN; ++e) vs[(d0 + e) * PITCH + r] = tmp[e];
-  }
-  __syncthreads();
+  // ---- v: [64 rows][128] -> [128][64 rows] through LDS, head by head
   const int n_cols = stride - s0 < 64 ? stride - s0 : 64;
-  for (int c = threadIdx.x; c < HD * (64 / VN); c += 256) {
-    const int d = c / (64 / VN), r0 = (c % (64 / VN)) * VN;
-    if (r0 < n_cols) {
-      T* dst = vto + (((long)b * H + h) * HD + d) * stride + s0 + r0;
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&vs[d * PITCH + r0]);
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = h0 + hh;
+    if (hh > 0) __syncthreads();  // the previous head's columns are out of LDS
+    for (int c = threadIdx.x; c < 64 * CPR; c += 256) {
+      const int r = c / CPR, d0 = (c % CPR) * VN;
+      const int s = s0 + r;
+      T tmp[VN];
+      if (s < S) {
+        const T* src = qkv + ((long)b * S + s) * (3L * W) + 2 * W + h * HD + d0;
+        *reinterpret_cast<u32x4*>(tmp) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) tmp[e] = T(0);
+      }
+#pragma unroll
+      for (int e = 0; e < VN; ++e) vs[(d0 + e) * PITCH + r] = tmp[e];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < HD * (64 / VN); c += 256) {
+      const int d = c / (64 / VN), r0 = (c % (64 / VN)) * VN;
+      if (r0 < n_cols) {
+        T* dst = vto + (((long)b * H + h) * HD + d) * stride + s0 + r0;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&vs[d * PITCH + r0]);
+      }
     }
   }
+}
+
+template <typename T, int HG>
+static void launch_heads(dim3 grid, const T* qkv, const float* gq, const float* gk, const int32_t* pos, T* qo, T* ko,
+                         T* vto, const uint64_t* masks, float* kmax, int S, int H, int stride, int fd, float eps,
+                         const RopeFreqs& fr, hipStream_t st) {
+  grid.y = (unsigned)(H / HG);
+  k_qk_norm_rope<T, HG><<<grid, 256, 0, st>>>(qkv, gq, gk, pos, qo, ko, vto, masks, kmax, S, H, stride, fd, eps, fr);
 }
 
 template <typename T>
 hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, const int32_t* pos, T* qo, T* ko,
                                T* vto, int B, int S, int H, int stride, int fd, float theta, float eps,
-                               hipStream_t st) {
+                               hipStream_t st, const uint64_t* masks, float* kmax) {
   if (fd < 0 || 6 * fd > 128 || stride % 64 != 0 || stride < S) return hipErrorInvalidValue;
+  if (kmax && (!masks || sizeof(T) != 2)) return hipErrorInvalidValue;
   RopeFreqs fr;
   for (int j = 0; j < 64; ++j) fr.inv_freq[j] = j < fd ? (float)pow((double)theta, -(double)j / fd) : 0.f;
-  dim3 grid((unsigned)(stride / 64), (unsigned)H, (unsigned)B);
-  k_qk_norm_rope<T><<<grid, 256, 0, st>>>(qkv, gq, gk, pos, qo, ko, vto, S, H, stride, fd, eps, fr);
+  const dim3 grid((unsigned)(stride / 64), 1u, (unsigned)B);
+  if (H % 2 == 0)
+    launch_heads<T, 2>(grid, qkv, gq, gk, pos, qo, ko, vto, masks, kmax, S, H, stride, fd, eps, fr, st);
+  else
+    launch_heads<T, 1>(grid, qkv, gq, gk, pos, qo, ko, vto, masks, kmax, S, H, stride, fd, eps, fr, st);
   return hipGetLastError();
 }
 
 template hipError_t launch_qk_norm_rope<bf16_t>(const bf16_t*, const float*, const float*, const int32_t*, bf16_t*,
                                                 bf16_t*, bf16_t*, int, int, int, int, int, float, float,
-                                                hipStream_t);
+                                                hipStream_t, const uint64_t*, float*);
 template hipError_t launch_qk_norm_rope<float>(const float*, const float*, const float*, const int32_t*, float*,
-                                               float*, float*, int, int, int, int, int, float, float, hipStream_t);
+                                               float*, float*, int, int, int, int, int, float, float, hipStream_t,
+                                               const uint64_t*, float*);
 
 }  // namespace minih3
