@@ -172,7 +172,9 @@ int minih3_adaln_modulate(const minih3_config* cfg, const minih3_layout* layout,
  * by position[a] * rope_theta^(-j/fd); other channels pass through.
  * qkv   : [B, S, 3W] act (the QKV projection output)
  * q_out, k_out : [B, H, seq_stride, hd] act;  v_t_out : [B, H, hd, seq_stride] act
- * Rows [S, seq_stride) of the outputs are written as zeros. */
+ * Rows [S, seq_stride) of the outputs are written as zeros. Reads head_dim
+ * (128), num_heads (any), act_dtype, rope_freq_dim, rope_theta and
+ * qk_norm_eps of cfg. */
 int minih3_qk_norm_rope(const minih3_config* cfg, const minih3_layout* layout, const void* qkv,
                         const float* q_norm, const float* k_norm, void* q_out, void* k_out,
                         void* v_t_out, int32_t seq_stride, void* stream);

@@ -93,6 +93,16 @@ int check_config_attention(const minih3_config* c) {
   return MINIH3_OK;
 }
 
+// q/k norm + RoPE reads head_dim, num_heads, act_dtype, the rotary fields and
+// qk_norm_eps of the config (any head count).
+int check_config_qk(const minih3_config* c) {
+  int s = check_config_attention(c);
+  if (s) return s;
+  if (c->rope_freq_dim < 0 || 6 * c->rope_freq_dim > c->head_dim) return MINIH3_E_UNSUPPORTED;
+  if (!(c->rope_theta > 0.f) || !(c->qk_norm_eps >= 0.f)) return MINIH3_E_ARG;
+  return MINIH3_OK;
+}
+
 // The bf16 projection kernel addresses each operand with 32-bit byte offsets.
 bool gemm_fits(long M, long N, long K) { return M * K * 2 <= 0xFFFFFFFFL && N * K * 2 <= 0xFFFFFFFFL; }
 
@@ -467,7 +477,7 @@ int minih3_adaln_modulate(const minih3_config* c, const minih3_layout* L, const 
 int minih3_qk_norm_rope(const minih3_config* c, const minih3_layout* L, const void* qkv, const float* q_norm,
                         const float* k_norm, void* q_out, void* k_out, void* v_t_out, int32_t seq_stride,
                         void* stream) {
-  int s = check_config(c);
+  int s = check_config_qk(c);
   if (s) return s;
   if (!L || L->batch < 1 || L->seq_len < 1 || !L->position_ids) return MINIH3_E_ARG;
   if (!qkv || !q_norm || !k_norm || !q_out || !k_out || !v_t_out) return MINIH3_E_ARG;

@@ -12,13 +12,15 @@
 //   kEpiSwiGLU     : W rows [0,F) gate, [F,2F) up; C[:, f] = silu(g_f) * u_f
 //
 // bf16 kernel (gfx950): 256x256 output tile per workgroup of 4 waves, one per
-// SIMD, each 128x128 as 4x4 v_mfma_f32_32x32x16_bf16 accumulators in AGPRs.
+// SIMD, each 128x128 as 8x8 v_mfma_f32_16x16x32_bf16 accumulators in AGPRs
+// (on random data this shape does about an eighth more work per unit of
+// power than 32x32x16, and the chip is power-limited under MFMA load).
 // Operands reach LDS by direct buffer->LDS DMA in K steps of 64 through a
 // ring of five 32 KiB slots (the A and W halves of a step are loaded at
-// different times, see the kernel); fragments are read one MFMA step ahead.
-// The issue order inside a step is fixed instruction group by instruction
-// group (sched_barrier fences): one DMA instruction per four MFMAs, so the
-// four waves of a CU never queue a burst of DMA at the address unit.
+// different times, see the kernel); fragments are read half a K step ahead.
+// The issue order is fixed instruction group by instruction group
+// (sched_barrier fences): one DMA instruction per eight MFMAs, so the four
+// waves of a CU never queue a burst of DMA at the address unit.
 // One barrier per K step. Tiles are ordered so that the workgroups an XCD
 // runs together share A and W panels in its L2. Plain (store) tiles are
 // staged in LDS and written as whole contiguous rows.
@@ -139,23 +141,22 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 
 // 256 x 256 output tile per workgroup of four waves; wave (wm, wn) owns the
-// 128 x 128 block at (128 wm, 128 wn) as 4 x 4 v_mfma_f32_32x32x16_bf16
+// 128 x 128 block at (128 wm, 128 wn) as 8 x 8 v_mfma_f32_16x16x32_bf16
 // accumulators (256 AGPRs).
 //
 // K advances in steps of 64. The A and W operands of a step each fill one
 // 32 KiB slot of a 5-slot LDS ring (slot of A_k: 2k mod 5, W_k: 2k + 1 mod
-// 5), loaded by direct buffer->LDS DMA. Within step k the four MFMA steps
-// (K 16 each) read their fragments one MFMA step ahead. Each wave issues
-// one DMA instruction per four MFMAs: the second half of W_{k+1} during
-// MFMA step 0, A_{k+2} during steps 1 and 2 (its slot held W_{k-1}); after
-// step 2 every wave waits for its own DMA of step k + 1 and one barrier
-// publishes it and frees A_k's and W_k's slots; the first half of W_{k+2}
-// then goes into A_k's slot during step 3.
+// 5), loaded by direct buffer->LDS DMA. Step k runs in two halves (K 32, 64
+// MFMAs each) whose fragments are read one half ahead. The first half loads
+// A_{k+2} (its slot held W_{k-1}); every wave then waits for its own DMA of
+// step k + 1 and one barrier publishes it and frees A_k's and W_k's slots;
+// the second half loads W_{k+2} into A_k's slot. A_k has about two K steps
+// to arrive, W_k one.
 template <int EPI>
 __global__ void __launch_bounds__(64 * kWaves, 1)
     k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
                 int K, EpiArgs ea) {
-  constexpr int WTM = 128, WTN = 128, MI = WTM / 32, NI = WTN / 32;
+  constexpr int WTM = 128, WTN = 128, MI = WTM / 16, NI = WTN / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -201,8 +202,6 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   }
   const int KT = K / BK;
   auto slot_ptr = [&](int s) { return lds + s * kSlotBytes; };
-  // DMA instructions j0 .. j1-1 of operand A (or W) of K step k into slot s;
-  // past the end of K the last step is loaded again (the slot is free).
   // DMA instruction j of operand A (or W) of K step k into its ring slot;
   // past the end of K the last step is loaded again (the slot is free).
   auto dma_a1 = [&](int k, int j) {
@@ -216,59 +215,83 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
     dma16(W, voff_w[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
   };
 
-  floatx16 acc[MI][NI];
+  floatx4 acc[MI][NI];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NI; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  // fragment reads: row (lane & 31) of a 32-row block, chunk 2 kk + (lane >> 5)
-  const int fr_row = lane & 31, fr_hi = lane >> 5, fr_sw = gemm_swz(fr_row);
+  // fragment reads (16x16x32 operands): row (lane & 15) of a 16-row block,
+  // 16-byte chunk 4 h + (lane >> 4) of half h of the K step
+  const int fr_row = lane & 15, fr_q = lane >> 4, fr_sw = gemm_swz(fr_row);
   bf16x8 fa[2][MI], fw[2][NI];
-  // fragment r (0..7) of MFMA step kk of K step k into register set `set`, in
-  // the order the MFMAs use them: a0 w0 w1 w2 w3 a1 a2 a3
-  auto read_frag = [&](int k, int kk, int set, int r) {
-    const int chunk = ((2 * kk + fr_hi) ^ fr_sw) << 4;
+  // fragment r (0..15) of half h of K step k into register set `set`, in the
+  // order the MFMAs first use them: a0 w0..w7 a1..a7
+  auto read_frag = [&](int k, int h, int set, int r) {
+    const int chunk = ((4 * h + fr_q) ^ fr_sw) << 4;
     if (r >= 1 && r <= NI) {
       const uint8_t* Ws = slot_ptr((2 * k + 1) % kSlots);
       const int ni = r - 1;
-      fw[set][ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 32 + fr_row) * kRowBytes + chunk);
+      fw[set][ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 16 + fr_row) * kRowBytes + chunk);
     } else {
       const uint8_t* As = slot_ptr((2 * k) % kSlots);
       const int mi = r == 0 ? 0 : r - NI;
-      fa[set][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 32 + fr_row) * kRowBytes + chunk);
+      fa[set][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 16 + fr_row) * kRowBytes + chunk);
     }
   };
-  auto read_frags = [&](int k, int kk, int set) {
-#pragma unroll
-    for (int r = 0; r < MI + NI; ++r) read_frag(k, kk, set, r);
-  };
+  // C[m][n] for m = row (lane & 15) of block mi, n = 4 (lane >> 4) + e of
+  // block ni: the W fragment is the MFMA's A operand, the A fragment its B.
+  // Written as an in-place instruction: with the builtin the compiler moves the
+  // 4-register accumulators between AGPRs on every K step. The compiler does
+  // not see this as an MFMA, so the wait states around the accumulators are
+  // explicit (fence_acc, after the zeroing and after the loop); fragment
+  // registers are rewritten no sooner than 12 MFMAs after their last use.
   auto mfma1 = [&](int set, int i) {
     const int mi = i / NI, ni = i % NI;
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[set][ni], fa[set][mi], acc[mi][ni], 0, 0, 0);
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(fw[set][ni]), "v"(fa[set][mi]));
   };
-  // One MFMA step in a fixed issue order: MFMA i, then (i < 8) fragment i of
-  // the next step, then (i % 4 == 3) one DMA instruction; each group is
-  // fenced so the DMA of the four waves reaches the address unit evenly.
-  auto step = [&](int set, int nk, int nkk, bool reads, int dk, bool dw, int dj) {
+  // One half K step (64 MFMAs) in a fixed issue order: MFMA i, then after
+  // every fourth MFMA one fragment of the next half, after every eighth one
+  // DMA instruction of (dk, W or A); each group is fenced so the DMA of the
+  // four waves reaches the address unit evenly.
+  auto half = [&](int set, int nk, int nh, bool reads, int dk, bool dw) {
 #pragma unroll
     for (int i = 0; i < MI * NI; ++i) {
       mfma1(set, i);
-      if (reads && i < MI + NI) read_frag(nk, nkk, set ^ 1, i);
-      if (dk >= 0 && (i & 3) == 3) {
+      if (reads && (i & 3) == 0) read_frag(nk, nh, set ^ 1, i >> 2);
+      if (dk >= 0 && (i & 7) == 7) {
         if (dw)
-          dma_w1(dk, dj + (i >> 2));
+          dma_w1(dk, i >> 3);
         else
-          dma_a1(dk, dj + (i >> 2));
+          dma_a1(dk, i >> 3);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  static_assert(kIPW == 8 && MI * NI == 16, "four DMA instructions per MFMA step");
+  static_assert(kIPW == 8 && MI * NI == 64, "eight DMA instructions per half K step");
 
-  // ---- prologue: A0 W0 A1 and the first half of W1 in flight, wait for step 0
+  // The accumulators pass through these statements (which the compiler cannot
+  // move them across): the first gives the zeroing its wait states before any
+  // MFMA reads an accumulator; after the loop the same gives the last MFMAs
+  // theirs before the epilogue reads them.
+  auto fence_acc = [&](bool after_mfma) {
+    if (after_mfma)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]),
+                   "+a"(acc[0][3]), "+a"(acc[0][4]), "+a"(acc[0][5]), "+a"(acc[0][6]), "+a"(acc[0][7]));
+    else
+      asm volatile("s_nop 1" : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                   "+a"(acc[0][4]), "+a"(acc[0][5]), "+a"(acc[0][6]), "+a"(acc[0][7]));
+#pragma unroll
+    for (int mi = 1; mi < MI; ++mi)
+      asm volatile("" : "+a"(acc[mi][0]), "+a"(acc[mi][1]), "+a"(acc[mi][2]), "+a"(acc[mi][3]), "+a"(acc[mi][4]),
+                   "+a"(acc[mi][5]), "+a"(acc[mi][6]), "+a"(acc[mi][7]));
+  };
+  static_assert(NI == 8, "eight accumulators per fence statement");
+
+  // ---- prologue: A0 W0 A1 W1 in flight, wait for step 0
+  fence_acc(false);
 #pragma unroll
   for (int j = 0; j < kIPW; ++j) dma_a1(0, j);
 #pragma unroll
@@ -276,38 +299,35 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
 #pragma unroll
   for (int j = 0; j < kIPW; ++j) dma_a1(1, j);
 #pragma unroll
-  for (int j = 0; j < kIPW / 2; ++j) dma_w1(1, j);
-  wait_vmcnt<kIPW + kIPW / 2>();
+  for (int j = 0; j < kIPW; ++j) dma_w1(1, j);
+  wait_vmcnt<2 * kIPW>();
   __builtin_amdgcn_s_barrier();
-  read_frags(0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < MI + NI; ++r) read_frag(0, 0, 0, r);
 
-  // K step kt: the second half of W_{kt+1} during MFMA step 0, A_{kt+2}
-  // during steps 1 and 2 (its slot held W_{kt-1}); then each wave waits for
-  // its own DMA of step kt + 1 and one barrier publishes it and frees the
-  // slots of A_kt and W_kt; the first half of W_{kt+2} goes into A_kt's slot
-  // during step 3.
-  for (int kt = 0; kt < KT - 1; ++kt) {
+  // K step kt: its first half loads A_{kt+2} (the slot of W_{kt-1}) and reads
+  // the second half's fragments; every wave then waits for its own DMA of
+  // step kt + 1 and one barrier publishes it and frees the slots of A_kt and
+  // W_kt; the second half loads W_{kt+2} into A_kt's slot and reads the first
+  // fragments of step kt + 1.
+  // The last step runs the same code: its DMA (clamped to step KT - 1) goes
+  // to freed slots and the fragments it reads for a step KT are never used,
+  // so the accumulators leave the loop in place (no copies after it).
+  for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
-    step(0, kt, 1, true, kt + 1, true, kIPW / 2);
-    step(1, kt, 2, true, kt + 2, false, 0);
-    step(0, kt, 3, true, kt + 2, false, kIPW / 2);
-    wait_vmcnt<kIPW>();  // W_{kt+1} landed; A_{kt+2} may be in flight
+    half(0, kt, 1, true, kt + 2, false);
+    wait_vmcnt<kIPW>();  // A_{kt+1}, W_{kt+1} landed; A_{kt+2} may be in flight
     wait_lgkm0();        // this wave's reads of step kt are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    step(1, kt + 1, 0, true, kt + 2, true, 0);
+    half(1, kt + 1, 0, true, kt + 2, true);
   }
   __builtin_amdgcn_sched_barrier(0);
-  step(0, KT - 1, 1, true, -1, false, 0);
-  step(1, KT - 1, 2, true, -1, false, 0);
-  step(0, KT - 1, 3, true, -1, false, 0);
-  step(1, 0, 0, false, -1, false, 0);
+  fence_acc(true);
   wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
 
-  // ---- epilogue. The plain output goes through LDS (the ring is free now)
-  // so that global memory sees whole contiguous rows. A lane's accumulators hold
-  // row m = tile row (wm*128 + mi*32 + (lane & 31)), columns
-  // wn*128 + ni*32 + 8i + 4*(lane>>5) + j (j < 4).
+  // ---- epilogue. A lane's accumulators hold row m = tile row
+  // (wm*128 + mi*16 + (lane & 15)), columns wn*128 + ni*16 + 4*(lane>>4) + e.
   if constexpr (EPI == kEpiGatedResid) {
     // gated residual straight from the accumulators: each lane's row keeps one
     // table row for all of its columns (staging through LDS serialises the
@@ -315,52 +335,46 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
     // so did staging the SwiGLU output)
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int m = m0 + wm * WTM + mi * 32 + fr_row;
+      const int m = m0 + wm * WTM + mi * 16 + fr_row;
       if (m >= M) continue;
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = tn * BN + wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
-          float v[4] = {acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1], acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]};
-          epi_gated_mixed(Cv, N, m, n, v, ea);
-        }
+      for (int ni = 0; ni < NI; ++ni) {
+        const int n = tn * BN + wn * WTN + ni * 16 + 4 * fr_q;
+        float v[4] = {acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
+        epi_gated_mixed(Cv, N, m, n, v, ea);
+      }
     }
   } else if constexpr (EPI == kEpiSwiGLU) {
     // silu(gate) * up straight from the accumulators (gate block ni, up block ni + NI/2)
     const int F = ea.ffn_dim;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int m = m0 + wm * WTM + mi * 32 + fr_row;
+      const int m = m0 + wm * WTM + mi * 16 + fr_row;
       if (m >= M) continue;
 #pragma unroll
-      for (int ni = 0; ni < NI / 2; ++ni)
+      for (int ni = 0; ni < NI / 2; ++ni) {
+        float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = silu(acc[mi][ni][4 * i + j]) * acc[mi][ni + NI / 2][4 * i + j];
-          const int f = 128 * tn + (WTN / 2) * wn + ni * 32 + 8 * i + 4 * fr_hi;
-          store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * F + f, v);
-        }
+        for (int e = 0; e < 4; ++e) v[e] = silu(acc[mi][ni][e]) * acc[mi][ni + NI / 2][e];
+        const int f = 128 * tn + (WTN / 2) * wn + ni * 16 + 4 * fr_q;
+        store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * F + f, v);
+      }
     }
   } else {
     // bf16 staging: 256 rows x 256 columns, rows padded by 8 bytes so that the
-    // 32 rows an 8-byte ds_write covers hit 32 different bank pairs
+    // 16 rows an 8-byte ds_write covers hit different bank pairs
     constexpr int RB = BN * 2 + 8;
     __syncthreads();  // every wave is done reading the ring
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * WTM + mi * 32 + fr_row, c = wn * WTN + ni * 32 + 8 * i + 4 * fr_hi;
-          u32x2 pk;
-          pk[0] = pack_bf16x2(acc[mi][ni][4 * i], acc[mi][ni][4 * i + 1]);
-          pk[1] = pack_bf16x2(acc[mi][ni][4 * i + 2], acc[mi][ni][4 * i + 3]);
-          *reinterpret_cast<u32x2*>(lds + r * RB + c * 2) = pk;
-        }
+      for (int ni = 0; ni < NI; ++ni) {
+        const int r = wm * WTM + mi * 16 + fr_row, c = wn * WTN + ni * 16 + 4 * fr_q;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
+        pk[1] = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+        *reinterpret_cast<u32x2*>(lds + r * RB + c * 2) = pk;
+      }
     __syncthreads();
     // one row (512 bytes) per wave instruction: lane owns columns 4*lane .. +3
     for (int rr = wid; rr < BM; rr += kWaves) {

@@ -91,8 +91,9 @@ def test_adaln_modulate(dtype, which):
 # ---------------------------------------------------------------- RMSNorm + RoPE
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_qk_norm_rope(dtype):
-    dims = small_bf16_dims(dtype=dtype)
+@pytest.mark.parametrize("heads", [4, 3])  # two heads per workgroup, and one (odd head count)
+def test_qk_norm_rope(dtype, heads):
+    dims = small_bf16_dims(dtype=dtype, num_heads=heads)
     wl = small_workload(dims, batch=2)
     cfg, lay, blocks, _ = dv.upload(wl)
     B, S, H, hd = 2, wl.layout.seq_len, dims.num_heads, dims.head_dim
