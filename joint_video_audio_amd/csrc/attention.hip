@@ -13,11 +13,15 @@
 //   * K tiles [64 keys][128] and V^T tiles [128][64 keys] reach LDS by
 //     buffer->LDS DMA (XOR-swizzled 16-byte chunks) through rings of four
 //     slots, three to four tiles ahead of their use;
-//   * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
-//     so each lane owns one query column and all per-query state is
-//     per-lane. Key rows enter the MFMA in an order (bits 2 and 3 of the row
-//     swapped) that makes the score registers exactly the B operand of
-//     O^T += V^T P^T: P never leaves registers;
+//   * scores are computed transposed, S^T = K Q^T, so every per-query
+//     quantity is per lane. The main kernel uses v_mfma_f32_16x16x32_bf16
+//     (on random data it does about an eighth more work per unit of power
+//     than 32x32x16, and the chip is power-limited under MFMA load): a lane
+//     owns one query of each 16-query block, and the K rows enter the MFMA
+//     in an order that makes a lane's score registers exactly its B operand
+//     of O^T += V^T P^T, so P never leaves registers. The running-max kernel
+//     does the same with v_mfma_f32_32x32x16_bf16 (bits 2 and 3 of the key
+//     row swapped);
 //   * bounded-score softmax: with scale * log2(e) folded into q, every score
 //     s_ij of query i obeys |s_ij| <= B_i = |q_i| * max_j |k_j| over the keys
 //     of the query's document (Cauchy-Schwarz). When B_i <= 64, exp2(s_ij)
@@ -60,6 +64,10 @@ __device__ __forceinline__ int kswz(int row) {
   return (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
 }
 __device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+// K tile of the fixed-reference kernel: its 16 lanes read rows
+// 32kc + 4h + {8a + b : a, b < 4} at one logical chunk; the physical chunk is
+// the logical one XOR (b | a << 2).
+__device__ __forceinline__ int kswz16(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 
 // Workgroup -> (query tile, b*H + h) with XCD-contiguous ranges.
 struct WgPos {
@@ -243,14 +251,6 @@ __device__ __forceinline__ void apply_doc_mask(floatx16 (&s)[2], uint64_t msel, 
   }
 }
 
-__device__ __forceinline__ void apply_doc_mask_half(floatx16& s, uint64_t msel, int hi, int kb) {
-  const uint32_t m32 = (uint32_t)(msel >> (kb * 32 + 8 * hi));
-  const uint32_t b16 = (m32 & 0xffu) | ((m32 >> 8) & 0xff00u);
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    if (!((b16 >> r) & 1u)) s[r] = -INFINITY;
-}
-
 __device__ __forceinline__ void store_out(bf16_t* out, const floatx16 (&o)[4], float l_run, int S, int H, int b,
                                           int h, int qr, int hi) {
   const float lt = l_run + __shfl_xor(l_run, 32, 64);
@@ -307,15 +307,16 @@ __global__ void k_zero_f32(float* p, int n) {
 // ---------------------------------------------------------------- fixed-reference kernel
 // K and V^T tiles reach LDS by buffer->LDS DMA through rings of four slots
 // (K four tiles ahead of its use, V three); one barrier per tile publishes
-// the tiles of the step after next, so the fragment reads run kAhead MFMAs
+// the tiles of the step after next, so the fragment reads run kAhead reads
 // ahead without a break: the first reads of a step are issued before its
-// barrier. Per tile a wave runs 32 MFMAs, alternating the score MFMAs of the
-// next tile with the O^T MFMAs of this one. The scores of a tile live in one
-// register set; each 32-key half becomes probabilities while the MFMAs of
-// the other half run (the exponentials never wait for a barrier).
+// barrier. Per tile a wave runs 64 16x16x32 MFMAs, pairs of score MFMAs of
+// the next tile (one per 16-query block) alternating with pairs of O^T MFMAs
+// of this one; each fragment read feeds one pair. The scores of a tile live
+// in one register set; each 32-key half becomes probabilities while the
+// MFMAs of the other half run (the exponentials never wait for a barrier).
 constexpr int kRing = 4;
 constexpr int kTileBytes = kKV * HD * 2;  // one K or V^T tile: 16 KiB
-constexpr int kAhead = 4;                 // fragment reads in flight ahead of the MFMAs
+constexpr int kAhead = 4;                 // fragment reads in flight ahead of their MFMA pair
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -351,21 +352,24 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   int& s_big = *reinterpret_cast<int*>(lds + 2 * kRing * kTileBytes);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
+  const int l16 = lane & 15, g4 = lane >> 4;
   const WgPos wp = wg_pos(n_qt, total);
   const int h = wp.bh % H, b = wp.bh / H;
   const int qw0 = wp.qt * kQG + wid * 32;
-  const int qr = qw0 + l32;
+  const int qr[2] = {qw0 + l16, qw0 + 16 + l16};  // the lane's queries in blocks 0 and 1
 
-  // ---- q scaled by scale*log2(e), rounded to bf16; its norm gives the bound
-  bf16x8 qf[8];
-  float qsq = 0.f;
-  {
-    const int qc = qr < stride ? qr : stride - 1;
-    const bf16_t* src = q + ((long)wp.bh * stride + qc) * HD + 8 * hi;
+  // ---- q scaled by scale*log2(e), rounded to bf16: the B operands of the
+  // score MFMAs (query l16 of block qb, channels 32c + 8 g4 .. +7); its norm
+  // gives the bound
+  bf16x8 qf[2][4];
+  float qsq[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 16 * kk);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qc = qr[qb] < stride ? qr[qb] : stride - 1;
+    const bf16_t* src = q + ((long)wp.bh * stride + qc) * HD + 8 * g4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + 32 * c);
       bf16x8 v;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -374,17 +378,24 @@ __global__ void __launch_bounds__(kNW * 64, 1)
         v[2 * w] = x0;
         v[2 * w + 1] = x1;
         const float f0 = (float)x0, f1 = (float)x1;
-        qsq += f0 * f0 + f1 * f1;
+        qsq[qb] += f0 * f0 + f1 * f1;
       }
-      qf[kk] = v;
+      qf[qb][c] = v;
     }
+    qsq[qb] += __shfl_xor(qsq[qb], 16, 64);
+    qsq[qb] += __shfl_xor(qsq[qb], 32, 64);
   }
-  qsq += __shfl_xor(qsq, 32, 64);
-  const int qdoc = qr < S ? (int)((masks[2 * (qr / kKV) + 1] >> (qr % kKV)) & 1ull) : 0;
-  const float bound = sqrtf(qsq) * kmax[2 * wp.bh + qdoc] * 1.001f + 1e-6f;
+  int qdoc[2];
+  bool big = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    qdoc[qb] = qr[qb] < S ? (int)((masks[2 * (qr[qb] / kKV) + 1] >> (qr[qb] % kKV)) & 1ull) : 0;
+    const float bound = sqrtf(qsq[qb]) * kmax[2 * wp.bh + qdoc[qb]] * 1.001f + 1e-6f;
+    big |= qr[qb] < S && !(bound <= kMaxRef);
+  }
   if (tid == 0) s_big = 0;
   __syncthreads();
-  if (__builtin_amdgcn_ballot_w64(qr < S && !(bound <= kMaxRef)) && lane == 0) atomicOr(&s_big, 1);
+  if (__builtin_amdgcn_ballot_w64(big) && lane == 0) atomicOr(&s_big, 1);
   __syncthreads();
   if (s_big) {
     if (tid == 0) wg_flag[wp.pid] = 1;  // left to the running-max kernel
@@ -463,7 +474,7 @@ __global__ void __launch_bounds__(kNW * 64, 1)
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int kr = 8 * wid + 4 * j + lane / 16;
-    koff[j] = (uint32_t)((kr * HD + ((lane % 16) ^ kswz(kr)) * 8) * 2);
+    koff[j] = (uint32_t)((kr * HD + ((lane % 16) ^ kswz16(kr)) * 8) * 2);
     const int vr = 16 * wid + 8 * j + lane / 8;
     voff[j] = (uint32_t)(((long)vr * stride + ((lane % 8) ^ vswz(vr)) * 8) * 2);
   }
@@ -490,48 +501,70 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     }
   };
 
-  const Frag fr(l32);
-  floatx16 o[4];
+  floatx4 o[8][2];  // O^T: rows 16 db + 4 g4 + r, query l16 of block qb
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float lsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
   bf16x2 ones2;
   ones2[0] = (__bf16)1.f;
   ones2[1] = (__bf16)1.f;
 
-  auto mask_tile = [&](floatx16(&sc)[2], const Ahead& a) {
-    const bool clean = (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
-    if (!clean) apply_doc_mask(sc, qdoc ? a.mp : a.mr, hi);
+  // Scores of one 32-key half kc of a tile: sh[h][qb] register r holds key
+  // 32 kc + 8 g4 + 4 h + r for query l16 of block qb (the K rows enter the
+  // MFMA in that order), so the eight probabilities of a lane are exactly the
+  // B operand (keys 32 kc + 8 g4 .. +7) of the O^T MFMA.
+  typedef floatx4 Half[2][2];
+  auto is_clean = [&](const Ahead& a) {
+    return (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
   };
-  auto mask_half = [&](floatx16& s, const Ahead& a, int kb) {
-    const bool clean = (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
-    if (!clean) apply_doc_mask_half(s, qdoc ? a.mp : a.mr, hi, kb);
+  auto mask_half = [&](Half& sh, const Ahead& a, int kc) {
+    if (is_clean(a)) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const uint32_t m8 = (uint32_t)((qdoc[qb] ? a.mp : a.mr) >> (32 * kc + 8 * g4)) & 0xffu;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!((m8 >> (4 * hh + r)) & 1u)) sh[hh][qb][r] = -INFINITY;
+    }
   };
-  // probabilities of keys 16 qq .. 16 qq + 15 (block qq/2, half qq%2)
-  auto probs = [&](const floatx16(&sc)[2], int qq) {
-    const int kb = qq >> 1, cc = qq & 1;
+  auto probs = [&](const Half& sh, int qb) {
     bf16x8 pv;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = (__bf16)fast_exp2(sc[kb][8 * cc + e]);
+    for (int e = 0; e < 8; ++e) pv[e] = (__bf16)fast_exp2(sh[e >> 2][qb][e & 3]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       bf16x2 pair;
       pair[0] = pv[2 * e];
       pair[1] = pv[2 * e + 1];
-      lsum[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, lsum[e], false);
+      lsum[qb][e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, lsum[qb][e & 1], false);
     }
     return pv;
   };
-  // MFMA i of a step (i < 32): even i = score MFMA (block i/16, K step (i%16)/2)
-  // of the next tile, odd i = O^T MFMA (value rows block ((i%16)/2)/2, key
-  // half ((i%16)/2)%2 of block i/16) of this tile
-  auto frag = [&](const uint8_t* Kn, const uint8_t* Vc, int i) {
-    const int kb = i / 16, j = (i % 16) / 2;
-    return (i % 2 == 0) ? fr.k(Kn, kb, j, hi) : fr.v(Vc, j / 2, kb, j % 2, l32, hi);
+  // Fragment f (0..31) of a step: half kc = f / 16; even f%16 = K fragment
+  // fk = (f%16)/2 (h = fk / 4, channels 32 (fk % 4) ..) of the next tile,
+  // odd = V^T fragment of rows 16 ((f%16)/2) .. of this tile. Lane offsets:
+  // K row 8 (l16/4) + (l16%4) (+ 32 kc + 4 h), chunk (4c + g4) ^ l16; V^T row
+  // l16 (+ 16 db), chunk (4 kc + g4) ^ (l16 >> 1).
+  uint32_t kofs[4], vofs[2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kofs[c] = (8 * (l16 >> 2) + (l16 & 3)) * 256 + (((4 * c + g4) ^ l16) << 4);
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) vofs[kc] = l16 * 128 + (((4 * kc + g4) ^ (l16 >> 1)) << 4);
+  auto frag = [&](const uint8_t* Kn, const uint8_t* Vc, int f) {
+    const int kc = f >> 4, e = f & 15;
+    if ((e & 1) == 0) {
+      const int fk = e >> 1, hh = fk >> 2, c = fk & 3;
+      return *reinterpret_cast<const bf16x8*>(Kn + kofs[c] + (32 * kc + 4 * hh) * 256);
+    }
+    return *reinterpret_cast<const bf16x8*>(Vc + vofs[kc] + (e >> 1) * 2048);
   };
-  // A step of the walk. On entry sc holds the scores of tile j (index tj).
+  auto mfma16 = [&](const bf16x8& a, const bf16x8& bb, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, c, 0, 0, 0);
+  };
   // Entering step j of the walk: every wave waits for its own DMA of K(j+2)
   // and V(j+1) and for its reads of step j - 1 (the first kAhead reads of
   // step j, issued at the end of step j - 1, may still be in flight); one
@@ -559,14 +592,14 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     dma_v(t3, (j + 3) % kRing);  // V(j+3) into the slot of V(j-1)
   };
   // A step of the walk. On entry sc holds the scores of tile j (the first
-  // half already turned into P[0], P[1], the second half masked) and G the
-  // first kAhead fragments of the step. MFMAs 0..15 run the first half of
-  // the next tile's scores and the O^T MFMAs of P[0], P[1] while the second
-  // half of tile j becomes P[2], P[3]; MFMAs 16..31 run the second half of
-  // the scores and the O^T MFMAs of P[2], P[3] while the (masked) first half
-  // of the next tile becomes its P[0], P[1]. The last kAhead reads fetch the
-  // first fragments of step j + 1, whose tiles the barrier of step j published.
-  auto step = [&](int j, floatx16(&sc)[2], bf16x8(&P)[4], bf16x8(&G)[kAhead]) {
+  // half already turned into P[0], the second half masked) and G the first
+  // kAhead fragments of the step. The first half's 32 MFMAs compute the
+  // first key half of the next tile's scores and the O^T MFMAs of P[0] while
+  // the second half of tile j becomes P[1]; the second half's compute the
+  // other key half and the O^T MFMAs of P[1] while the (masked) first half of
+  // the next tile becomes its P[0]. The last kAhead reads fetch the first
+  // fragments of step j + 1, whose tiles the barrier of step j published.
+  auto step = [&](int j, Half (&sc)[2], bf16x8 (&P)[2][2], bf16x8 (&G)[kAhead]) {
     Ahead a1;
     enter(j, a1);
     const uint8_t* Kn = kslot((j + 1) % kRing);
@@ -577,46 +610,46 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     bf16x8 F[32 + kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) F[i] = G[i];
-    auto rd = [&](int i) { F[i] = i < 32 ? frag(Kn, Vc, i) : frag(Kn2, Vc2, i - 32); };
-    P[2] = probs(sc, 2);
-    P[3] = probs(sc, 3);
+    auto rd = [&](int f) { F[f] = f < 32 ? frag(Kn, Vc, f) : frag(Kn2, Vc2, f - 32); };
+    auto half_mfmas = [&](int kc) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      rd(i + kAhead);
-      const int jj = i / 2;
-      if (i % 2 == 0)
-        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], qf[jj], jj == 0 ? floatx16{} : sc[0], 0, 0, 0);
-      else
-        o[jj / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], P[jj % 2], o[jj / 2], 0, 0, 0);
-    }
+      for (int fi = 0; fi < 16; ++fi) {
+        const int f = 16 * kc + fi;
+        rd(f + kAhead);
+        if ((fi & 1) == 0) {
+          const int fk = fi >> 1, hh = fk >> 2, c = fk & 3;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
+          for (int qb = 0; qb < 2; ++qb)
+            sc[kc][hh][qb] = mfma16(F[f], qf[qb][c], c == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sc[kc][hh][qb]);
+        } else {
+          const int db = fi >> 1;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma16(F[f], P[kc][qb], o[db][qb]);
+        }
+      }
+    };
+    auto half_sched = [&]() {
+#pragma unroll
+      for (int fi = 0; fi < 16; ++fi) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      }
+    };
+    P[1][0] = probs(sc[1], 0);
+    P[1][1] = probs(sc[1], 1);
+    half_mfmas(0);
+    half_sched();
     __builtin_amdgcn_sched_barrier(0);
     mask_half(sc[0], a1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 Pn0 = probs(sc, 0), Pn1 = probs(sc, 1);
-#pragma unroll
-    for (int i = 16; i < 32; ++i) {
-      rd(i + kAhead);
-      const int jj = (i % 16) / 2;
-      if (i % 2 == 0)
-        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], qf[jj], jj == 0 ? floatx16{} : sc[1], 0, 0, 0);
-      else
-        o[jj / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[i], P[2 + jj % 2], o[jj / 2], 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 16; i < 32; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
+    const bf16x8 Pn0 = probs(sc[0], 0), Pn1 = probs(sc[0], 1);
+    half_mfmas(1);
+    half_sched();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) G[i] = F[32 + i];
-    P[0] = Pn0;
-    P[1] = Pn1;
+    P[0][0] = Pn0;
+    P[0][1] = Pn1;
     mask_half(sc[1], a1, 1);
   };
 
@@ -637,19 +670,22 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
     }
-    floatx16 sc[2];
+    Half sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(kslot(0), kb, 0, hi), qf[0], floatx16{}, 0, 0, 0);
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-    for (int kk = 1; kk < 8; ++kk)
+      for (int fk = 0; fk < 8; ++fk) {
+        const bf16x8 kf = frag(kslot(0), vslot(0), 16 * kc + 2 * fk);
+        const int hh = fk >> 2, c = fk & 3;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.k(kslot(0), kb, kk, hi), qf[kk], sc[kb], 0, 0, 0);
-    mask_tile(sc, a0);
-    bf16x8 P[4];
-    P[0] = probs(sc, 0);
-    P[1] = probs(sc, 1);
+        for (int qb = 0; qb < 2; ++qb)
+          sc[kc][hh][qb] = mfma16(kf, qf[qb][c], c == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sc[kc][hh][qb]);
+      }
+    mask_half(sc[0], a0, 0);
+    mask_half(sc[1], a0, 1);
+    bf16x8 P[2][2];
+    P[0][0] = probs(sc[0], 0);
+    P[0][1] = probs(sc[0], 1);
     bf16x8 G[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) G[i] = frag(kslot(1), vslot(0), i);
@@ -659,16 +695,35 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     Ahead a1;
     enter(n - 1, a1);
     const uint8_t* Vc = vslot((n - 1) % kRing);
-    P[2] = probs(sc, 2);
-    P[3] = probs(sc, 3);
+    P[1][0] = probs(sc[1], 0);
+    P[1][1] = probs(sc[1], 1);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.v(Vc, db, qq >> 1, qq & 1, l32, hi), P[qq], o[db], 0, 0, 0);
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 vf = frag(kslot(0), Vc, 16 * kc + 2 * db + 1);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma16(vf, P[kc][qb], o[db][qb]);
+      }
   }
   wait_vmcnt<0>();  // no DMA may still write LDS when the workgroup ends
-  store_out(out, o, (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]), S, H, b, h, qr, hi);
+  // ---- output: the row sums of a query are spread over the four lane groups
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float lt = lsum[qb][0] + lsum[qb][1];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qr[qb] >= S) continue;
+    bf16_t* dst = out + ((long)b * S + qr[qb]) * (H * HD) + h * HD + 4 * g4;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[db][qb][0] * inv, o[db][qb][1] * inv);
+      pk[1] = pack_bf16x2(o[db][qb][2] * inv, o[db][qb][3] * inv);
+      *reinterpret_cast<u32x2*>(dst + 16 * db) = pk;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- running-max kernel
