@@ -316,7 +316,7 @@ __global__ void k_zero_f32(float* p, int n) {
 // MFMAs of the other half run (the exponentials never wait for a barrier).
 constexpr int kRing = 4;
 constexpr int kTileBytes = kKV * HD * 2;  // one K or V^T tile: 16 KiB
-constexpr int kAhead = 4;                 // fragment reads in flight ahead of their MFMA pair
+constexpr int kAhead = 2;                 // fragment reads in flight ahead of their MFMA pair
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
