@@ -43,9 +43,20 @@ template <> struct Act<float> {
   static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
 };
 
+// Sum over the 64 lanes, result in every lane: within each 16-lane row by
+// DPP moves (quad xor 1, quad xor 2, half-row mirror, row mirror), then two
+// lane exchanges across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
   return v;
 }
 

@@ -65,17 +65,13 @@ template <> struct Chunk<float> {
 // Sum over the N lanes of a row (N = 16 or 32, aligned groups), result in
 // every lane of the row: DPP within 16 lanes (quad xor 1, quad xor 2, half
 // mirror, mirror), then one lane exchange across the two 16-lane halves.
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
 template <int N>
 __device__ __forceinline__ float row_sum(float v) {
   static_assert(N == 16 || N == 32, "row width");
-  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dppf<0x141>(v);  // row_half_mirror
-  v += dppf<0x140>(v);  // row_mirror
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
   if (N == 32) v += __shfl_xor(v, 16, 64);
   return v;
 }
