@@ -611,7 +611,13 @@ __global__ void __launch_bounds__(kNW * 64, 1)
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) F[i] = G[i];
     auto rd = [&](int f) { F[f] = f < 32 ? frag(Kn, Vc, f) : frag(Kn2, Vc2, f - 32); };
-    auto half_mfmas = [&](int kc) {
+    // One half: group fi = fragment read, the MFMA pair of fragment 16 kc + fi,
+    // and element fi of the softmax of the other half (query block fi / 8,
+    // key e = fi % 8 of the lane's eight): one exponential, and every second
+    // group the bf16 pair and its row-sum dot. Each group is fenced, so the
+    // exponentials run under the MFMAs instead of between them.
+    auto half = [&](int kc, const Half& src, bf16x8 (&dst)[2]) {
+      float ex[2];
 #pragma unroll
       for (int fi = 0; fi < 16; ++fi) {
         const int f = 16 * kc + fi;
@@ -626,30 +632,33 @@ __global__ void __launch_bounds__(kNW * 64, 1)
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma16(F[f], P[kc][qb], o[db][qb]);
         }
+        const int qb = fi >> 3, e = fi & 7;
+        float x = src[e >> 2][qb][e & 3];
+        asm volatile("" : "+v"(x));  // keeps this exponential in its group (not hoisted ...
+        ex[e & 1] = fast_exp2(x);
+        asm volatile("" : "+v"(ex[e & 1]));  // ... nor sunk to its first use)
+        if (e & 1) {
+          bf16x2 pair;
+          pair[0] = (__bf16)ex[0];
+          pair[1] = (__bf16)ex[1];
+          dst[qb][e - 1] = pair[0];
+          dst[qb][e] = pair[1];
+          lsum[qb][(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones2, lsum[qb][(e >> 1) & 1], false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    auto half_sched = [&]() {
-#pragma unroll
-      for (int fi = 0; fi < 16; ++fi) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      }
-    };
-    P[1][0] = probs(sc[1], 0);
-    P[1][1] = probs(sc[1], 1);
-    half_mfmas(0);
-    half_sched();
-    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 P1[2], Pn[2];
+    half(0, sc[1], P1);  // scores of key half 1 of tile j become P[1]
+    P[1][0] = P1[0];
+    P[1][1] = P1[1];
     mask_half(sc[0], a1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 Pn0 = probs(sc[0], 0), Pn1 = probs(sc[0], 1);
-    half_mfmas(1);
-    half_sched();
-    __builtin_amdgcn_sched_barrier(0);
+    half(1, sc[0], Pn);  // the next tile's key half 0 becomes its P[0]
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) G[i] = F[32 + i];
-    P[0][0] = Pn0;
-    P[0][1] = Pn1;
+    P[0][0] = Pn[0];
+    P[0][1] = Pn[1];
     mask_half(sc[1], a1, 1);
   };
 
