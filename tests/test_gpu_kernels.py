@@ -29,7 +29,9 @@ def bf16_vals(a: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("M,N,K", [(300, 512, 384), (1, 256, 64), (513, 768, 640), (2048, 1024, 512)])
+# K steps of 64: one, two, three (the pipeline's prologue and clamped tail loads), and longer
+@pytest.mark.parametrize("M,N,K", [(300, 512, 384), (1, 256, 64), (260, 256, 128), (257, 512, 192), (513, 768, 640),
+                                   (2048, 1024, 512)])
 def test_linear_bf16(M, N, K):
     print(f"linear bf16 M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M + N + K)
