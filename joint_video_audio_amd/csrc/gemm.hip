@@ -81,29 +81,6 @@ __device__ __forceinline__ void epi_gated(T* C, int ldc, int m, int n, const flo
   store4<T>(C + (long)m * ldc + n, r);
 }
 
-// Gated residual of the bf16 kernel: the residual and the output are each
-// bf16 or fp32 (the fp32 residual stream between the block's two gated adds
-// and between blocks).
-__device__ __forceinline__ void epi_gated_mixed(void* C, int ldc, int m, int n, const float* acc, const EpiArgs& ea) {
-  float r[4];
-  const long at = (long)m * ldc + n;
-  if (ea.resid_f32)
-    load4<float>(static_cast<const float*>(ea.resid) + at, r);
-  else
-    load4<bf16_t>(static_cast<const bf16_t*>(ea.resid) + at, r);
-  const int s = m % ea.S;
-  const int tr = table_row_of(ea.tags[s], ea.tidx[s], ea.num_tags, ea.num_tvals);
-  if (tr >= 0) {
-    floatx4 g = *reinterpret_cast<const floatx4*>(ea.table + ((long)tr * 6 + ea.gate_slot) * ldc + n);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] += g[j] * acc[j];
-  }
-  if (ea.out_f32)
-    store4<float>(static_cast<float*>(C) + at, r);
-  else
-    store4<bf16_t>(static_cast<bf16_t*>(C) + at, r);
-}
-
 // ---------------------------------------------------------------- bf16 MFMA kernel
 
 constexpr int BM = 256, BN = 256, BK = 64;
@@ -329,20 +306,57 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   // ---- epilogue. A lane's accumulators hold row m = tile row
   // (wm*128 + mi*16 + (lane & 15)), columns wn*128 + ni*16 + 4*(lane>>4) + e.
   if constexpr (EPI == kEpiGatedResid) {
-    // gated residual straight from the accumulators: each lane's row keeps one
-    // table row for all of its columns (staging through LDS serialises the
-    // per-row residual and gate loads behind the stores, and measured slower;
-    // so did staging the SwiGLU output)
+    // gated residual straight from the accumulators (staging through LDS
+    // measured slower, as did staging the SwiGLU output). Per lane row: its
+    // table row once, then all eight residual and gate loads before any
+    // store, with the storage types fixed outside the loops; a padding row
+    // takes gate 0, which leaves its residual bit for bit.
+    auto gated = [&](auto resid_tag, auto out_tag) {
+      using TR = decltype(resid_tag);
+      using TO = decltype(out_tag);
+      const TR* resid = static_cast<const TR*>(ea.resid);
+      TO* out = static_cast<TO*>(Cv);
+      int trs[MI];  // table rows of the lane's rows, loaded together
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int m = m0 + wm * WTM + mi * 16 + fr_row;
-      if (m >= M) continue;
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int n = tn * BN + wn * WTN + ni * 16 + 4 * fr_q;
-        float v[4] = {acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
-        epi_gated_mixed(Cv, N, m, n, v, ea);
+      for (int mi = 0; mi < MI; ++mi) {
+        int m = m0 + wm * WTM + mi * 16 + fr_row;
+        m = m < M ? m : M - 1;
+        const int s = m % ea.S;
+        trs[mi] = table_row_of(ea.tags[s], ea.tidx[s], ea.num_tags, ea.num_tvals);
       }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int m = m0 + wm * WTM + mi * 16 + fr_row;
+        if (m >= M) continue;
+        const int tr = trs[mi];
+        const float* grow = ea.table + ((long)(tr >= 0 ? tr : 0) * 6 + ea.gate_slot) * N;
+        float r[NI][4];
+        floatx4 g[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = tn * BN + wn * WTN + ni * 16 + 4 * fr_q;
+          load4<TR>(resid + (long)m * N + n, r[ni]);
+          g[ni] = *reinterpret_cast<const floatx4*>(grow + n);
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int n = tn * BN + wn * WTN + ni * 16 + 4 * fr_q;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[ni][e] += (tr >= 0 ? g[ni][e] : 0.f) * acc[mi][ni][e];
+          store4<TO>(out + (long)m * N + n, r[ni]);
+        }
+      }
+    };
+    if (ea.resid_f32) {
+      if (ea.out_f32)
+        gated(float{}, float{});
+      else
+        gated(float{}, bf16_t{});
+    } else {
+      if (ea.out_f32)
+        gated(bf16_t{}, float{});
+      else
+        gated(bf16_t{}, bf16_t{});
     }
   } else if constexpr (EPI == kEpiSwiGLU) {
     // silu(gate) * up straight from the accumulators (gate block ni, up block ni + NI/2)
