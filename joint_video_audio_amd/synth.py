@@ -306,3 +306,77 @@ def permute_rows(layout: Layout, perm: np.ndarray) -> Layout:
     return Layout(layout.token_tags[perm].copy(), layout.timestep_indices[perm].copy(),
                   layout.position_ids[perm].copy(), inv[layout.video_indices].astype(np.int32),
                   inv[layout.audio_indices].astype(np.int32), inv[layout.text_indices].astype(np.int32))
+
+
+# --------------------------------------------------------------------------
+# Timestep conditioning inputs (the AdaLN table build)
+# --------------------------------------------------------------------------
+#
+# Recipe: ``numpy.random.default_rng(seed)``; draw order: base embedder
+# (W1, b1, W2, b2), endpoint embedder (same order, two-time only), then per
+# block the AdaLN projection (W, b). Embedder weights are fp32 with
+# W ~ N(0, 1 / fan_in) and biases ~ N(0, 0.02); the endpoint embedder is the
+# base one plus N(0, 0.1^2 / fan_in) (a merged adapter); gate 0.25. AdaLN
+# projection weights and biases ~ N(0, 0.02) in the activation dtype.
+# Timesteps: value v of n is 1 - v / n; with two-time conditioning over
+# n = k * k values, value v is the pair (t, r) = (g[v // k], g[v % k]) on the
+# k-point grid g_i = 1 - i / k, so the diagonal holds the r = t pairs.
+
+@dataclasses.dataclass
+class TimeEmbedder:
+    w1: np.ndarray  # fp32 [hidden_dim, freq_dim]
+    b1: np.ndarray  # fp32 [hidden_dim]
+    w2: np.ndarray  # fp32 [embed_dim, hidden_dim]
+    b2: np.ndarray  # fp32 [embed_dim]
+
+    def as_dict(self) -> dict:
+        return dict(w1=self.w1, b1=self.b1, w2=self.w2, b2=self.b2)
+
+
+@dataclasses.dataclass
+class Conditioning:
+    freq_dim: int
+    hidden_dim: int
+    embed_dim: int
+    t: np.ndarray                   # fp32 [n_tvals]
+    r: Optional[np.ndarray]         # fp32 [n_tvals] step endpoints (two-time only)
+    base: TimeEmbedder
+    endpoint: Optional[TimeEmbedder]
+    gate: float
+    w_proj: List[Tensor]            # per block [num_tags, 6 D, embed_dim]
+    b_proj: List[Tensor]            # per block [num_tags, 6 D]
+
+
+def _draw_embedder(rng, freq_dim, hidden_dim, embed_dim) -> TimeEmbedder:
+    return TimeEmbedder(_normal(rng, (hidden_dim, freq_dim), freq_dim ** -0.5), _normal(rng, (hidden_dim,), 0.02),
+                        _normal(rng, (embed_dim, hidden_dim), hidden_dim ** -0.5), _normal(rng, (embed_dim,), 0.02))
+
+
+def make_conditioning(dims: ModelDims, num_blocks: int = 1, two_time: bool = False, seed: int = 0,
+                      freq_dim: int = 256, hidden_dim: int = 5376, embed_dim: int = 2688,
+                      num_tvals: Optional[int] = None) -> Conditioning:
+    """Timesteps, timestep-MLP weights and per-block AdaLN projections."""
+    rng = np.random.default_rng(seed)
+    n = dims.num_tvals if num_tvals is None else num_tvals
+    base = _draw_embedder(rng, freq_dim, hidden_dim, embed_dim)
+    endpoint, r = None, None
+    if two_time:
+        k = int(round(n ** 0.5))
+        if k * k != n:
+            raise ValueError("two-time conditioning needs a square number of timestep values")
+        d = _draw_embedder(rng, freq_dim, hidden_dim, embed_dim)
+        endpoint = TimeEmbedder(base.w1 + np.float32(0.1) * d.w1, base.b1.copy(),
+                                base.w2 + np.float32(0.1) * d.w2, base.b2.copy())
+        g = (1.0 - np.arange(k) / k).astype(np.float32)
+        v = np.arange(n)
+        t, r = g[v // k], g[v % k]
+    else:
+        t = (1.0 - np.arange(n) / n).astype(np.float32)
+    D6 = 6 * dims.hidden
+    w_proj, b_proj = [], []
+    for _ in range(num_blocks):
+        w_proj.append(_store(_normal(rng, (dims.num_tags, D6, embed_dim), 0.02), dims.dtype))
+        b_proj.append(_store(_normal(rng, (dims.num_tags, D6), 0.02), dims.dtype))
+    return Conditioning(freq_dim, hidden_dim, embed_dim, np.asarray(t, np.float32),
+                        None if r is None else np.asarray(r, np.float32), base, endpoint,
+                        0.25 if two_time else 0.0, w_proj, b_proj)
