@@ -185,6 +185,64 @@ int minih3_qk_norm_rope(const minih3_config* cfg, const minih3_layout* layout, c
 int minih3_linear(int32_t dtype, const void* a, const void* w, void* c, int32_t M, int32_t N, int32_t K,
                   void* stream);
 
+/* ---- Timestep conditioning: building the AdaLN tables ----
+ * Page "MiniMaxH3Transformer3DModel": Parameters freq_dim (sinusoidal
+ * timestep embedding; timesteps are used unscaled, in [0, 1]),
+ * time_embed_hidden_dim and time_embed_dim (the timestep MLP, whose output
+ * is the input of every AdaLN projection), the mixed-precision note (the
+ * timestep MLP is float32, the block stack bfloat16), `forward` `timestep`
+ * (the distinct timestep values that timestep_indices point at) and the
+ * class description (the modality tag selects the AdaLN modulation). Page
+ * "HyperFlow for MiniMax-H3", How it works: a second embedder for the step
+ * endpoint r is blended with the base one by a fixed gate; conditioning rows
+ * keep r = t. Where the pages leave the form open, the library takes:
+ * s(t) = [cos(t f_j), sin(t f_j)], f_j = max_period^(-j / (freq_dim/2));
+ * E(t) = W2 SiLU(W1 s(t) + b1) + b2; two-time e = (1 - gate) E(t) + gate E'(r);
+ * table row (tag k, value v) = W_k SiLU(e_v) + b_k viewed as [6, D]. */
+typedef struct {
+  int32_t freq_dim;   /* sinusoid width (256); multiple of 32                 */
+  int32_t hidden_dim; /* timestep MLP inner width (5376); multiple of 16      */
+  int32_t embed_dim;  /* timestep MLP output width (2688); multiple of 16     */
+  float max_period;   /* base of the sinusoid frequencies (1e4)               */
+} minih3_time_config;
+
+/* fp32 timestep-MLP weights, row-major [out, in]; a NULL bias is zero. */
+typedef struct {
+  const float* w1; /* [hidden_dim, freq_dim] */
+  const float* b1; /* [hidden_dim]           */
+  const float* w2; /* [embed_dim, hidden_dim] */
+  const float* b2; /* [embed_dim]            */
+} minih3_time_mlp;
+
+/* Bytes of workspace minih3_time_embed needs for num_tvals values. */
+int minih3_time_embed_workspace_bytes(const minih3_time_config* tc, int32_t num_tvals, size_t* bytes);
+
+/* Time embeddings of num_tvals timestep values, fp32 throughout:
+ * emb[v] = E(t[v]), or with `endpoint` non-NULL (two-time conditioning)
+ * emb[v] = (1 - gate) E(t[v]) + gate E'(r[v]), E' the MLP with the endpoint
+ * weights (r NULL: r = t). t, r : [num_tvals] fp32; emb : [num_tvals,
+ * embed_dim] fp32. Split-K partial sums are added in a fixed order, so
+ * repeated calls give identical bits. */
+int minih3_time_embed(const minih3_time_config* tc, const minih3_time_mlp* base, const float* t,
+                      const minih3_time_mlp* endpoint, const float* r, float gate, int32_t num_tvals, float* emb,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace minih3_adaln_table needs (0 for fp32 activations). */
+int minih3_adaln_table_workspace_bytes(const minih3_config* cfg, int32_t embed_dim, size_t* bytes);
+
+/* AdaLN table of one block from the time embeddings:
+ * table[k, v, c, :] = (W_k SiLU(emb[v]) + b_k)[c*D : (c+1)*D], c = shift1,
+ * scale1, gate1, shift2, scale2, gate2 (the layout of
+ * minih3_block_weights.adaln_table). Reads hidden (D), num_tags, num_tvals
+ * and act_dtype of cfg.
+ * emb    : [num_tvals, embed_dim] fp32
+ * w_proj : [num_tags, 6 D, embed_dim] act;  b_proj : [num_tags, 6 D] act or NULL
+ * table  : [num_tags, num_tvals, 6, D] fp32 (output)
+ * bf16: SiLU(emb) is rounded to bf16 for the MFMA product (fp32
+ * accumulation, fp32 output); embed_dim % 32 == 0. fp32: embed_dim % 16 == 0. */
+int minih3_adaln_table(const minih3_config* cfg, const float* emb, int32_t embed_dim, const void* w_proj,
+                       const void* b_proj, float* table, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernel timing under MINIH3_PROFILE. Synchronises the recorded events,
  * writes for each kernel id k < n the summed milliseconds and the number of
  * launches since the last collect, then resets. Returns the number of

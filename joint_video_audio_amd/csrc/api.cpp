@@ -328,6 +328,47 @@ LayoutDev make_layout_dev(const minih3_config* c, const minih3_layout* L) {
   return d;
 }
 
+
+// ---- timestep conditioning ----
+constexpr int kTimeSplits = 8;  // K splits of the timestep MLP's second layer
+
+int check_time_config(const minih3_time_config* tc) {
+  if (!tc) return MINIH3_E_ARG;
+  if (tc->freq_dim < 32 || tc->freq_dim % 32 != 0) return MINIH3_E_UNSUPPORTED;
+  if (tc->hidden_dim < 16 || tc->hidden_dim % 16 != 0) return MINIH3_E_UNSUPPORTED;
+  if (tc->embed_dim < 16 || tc->embed_dim % 16 != 0) return MINIH3_E_UNSUPPORTED;
+  if (!(tc->max_period > 0.f)) return MINIH3_E_ARG;
+  return MINIH3_OK;
+}
+
+struct TimeWorkspace {
+  float *h, *part;
+  size_t total;
+};
+
+TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base) {
+  TimeWorkspace w{};
+  const size_t hb = align_up((size_t)M * tc->hidden_dim * 4);
+  const size_t pb = align_up((size_t)skinny_splits(tc->hidden_dim, kTimeSplits) * M * tc->embed_dim * 4);
+  w.h = base ? (float*)base : nullptr;
+  w.part = base ? (float*)(base + hb) : nullptr;
+  w.total = hb + pb;
+  return w;
+}
+
+// One timestep MLP over M timesteps; emb = its output, or the blend
+// (1 - gate) emb + gate * output when blend is set.
+int time_mlp(const minih3_time_config* tc, const minih3_time_mlp* m, const float* t, int M, float* emb, bool blend,
+             float gate, TimeWorkspace& w, hipStream_t st) {
+  const int F = tc->freq_dim, Hd = tc->hidden_dim, E = tc->embed_dim;
+  HIPCHECK(launch_skinny_f32(kInSinusoid, t, m->w1, m->b1, w.h, M, Hd, F, 1, Hd, 1, tc->max_period, st));
+  const int splits = skinny_splits(Hd, kTimeSplits);  // what the launch below uses
+  HIPCHECK(launch_skinny_f32(kInPlain, w.h, m->w2, nullptr, w.part, M, E, Hd, kTimeSplits, E, 0, tc->max_period,
+                             st));
+  HIPCHECK(launch_rows_finish(w.part, splits, m->b2, emb, M, E, 0, blend ? emb : nullptr, gate, st));
+  return MINIH3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -510,6 +551,61 @@ int minih3_linear(int32_t dtype, const void* a, const void* w, void* c, int32_t 
   }
   return MINIH3_OK;
 }
+
+int minih3_time_embed_workspace_bytes(const minih3_time_config* tc, int32_t num_tvals, size_t* bytes) {
+  int s = check_time_config(tc);
+  if (s) return s;
+  if (num_tvals < 1 || !bytes) return MINIH3_E_ARG;
+  *bytes = carve_time(tc, num_tvals, nullptr).total;
+  return MINIH3_OK;
+}
+
+int minih3_time_embed(const minih3_time_config* tc, const minih3_time_mlp* base, const float* t,
+                      const minih3_time_mlp* endpoint, const float* r, float gate, int32_t num_tvals, float* emb,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int s = check_time_config(tc);
+  if (s) return s;
+  if (num_tvals < 1 || !base || !base->w1 || !base->w2 || !t || !emb) return MINIH3_E_ARG;
+  if (endpoint && (!endpoint->w1 || !endpoint->w2)) return MINIH3_E_ARG;
+  if ((long)num_tvals * tc->hidden_dim > (1L << 28) || (long)num_tvals * tc->embed_dim > (1L << 28))
+    return MINIH3_E_UNSUPPORTED;
+  TimeWorkspace w = carve_time(tc, num_tvals, (char*)workspace);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = time_mlp(tc, base, t, num_tvals, emb, false, 0.f, w, st);
+  if (s || !endpoint) return s;
+  return time_mlp(tc, endpoint, r ? r : t, num_tvals, emb, true, gate, w, st);
+}
+
+int minih3_adaln_table_workspace_bytes(const minih3_config* c, int32_t embed_dim, size_t* bytes) {
+  if (!c || !bytes || c->num_tvals < 1 || embed_dim < 1) return MINIH3_E_ARG;
+  *bytes = c->act_dtype == MINIH3_BF16 ? align_up((size_t)adaln_proj_rows(c->num_tvals) * embed_dim * 2) : 0;
+  return MINIH3_OK;
+}
+
+int minih3_adaln_table(const minih3_config* c, const float* emb, int32_t embed_dim, const void* w_proj,
+                       const void* b_proj, float* table, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!c || (c->act_dtype != MINIH3_BF16 && c->act_dtype != MINIH3_F32)) return MINIH3_E_ARG;
+  if (c->hidden < 256 || c->hidden % 256 != 0) return MINIH3_E_UNSUPPORTED;
+  if (c->num_tags < 1 || c->num_tvals < 1 || embed_dim < 1) return MINIH3_E_ARG;
+  if (!emb || !w_proj || !table) return MINIH3_E_ARG;
+  const long ng = 6L * c->hidden, N = ng * c->num_tags, M = c->num_tvals;
+  if (N * embed_dim > (1L << 31) || M * N > (1L << 31) || M > (1L << 20)) return MINIH3_E_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  if (c->act_dtype == MINIH3_F32) {
+    if (embed_dim % 16 != 0) return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_skinny_f32(kInSilu, emb, (const float*)w_proj, (const float*)b_proj, table, (int)M, (int)N,
+                               embed_dim, 1, (int)ng, 0, 1.f, st));
+    return MINIH3_OK;
+  }
+  if (embed_dim % 32 != 0) return MINIH3_E_UNSUPPORTED;
+  const size_t need = align_up((size_t)adaln_proj_rows((int)M) * embed_dim * 2);
+  if (!workspace || workspace_bytes < need) return MINIH3_E_WORKSPACE;
+  HIPCHECK(launch_adaln_proj(emb, (const bf16_t*)w_proj, (const bf16_t*)b_proj, (bf16_t*)workspace, table, (int)M,
+                             (int)N, embed_dim, (int)ng, st));
+  return MINIH3_OK;
+}
+
 
 int minih3_profile_collect(double* total_ms, int32_t* launches, int32_t n) {
   std::lock_guard<std::mutex> lk(g_prof.mu);

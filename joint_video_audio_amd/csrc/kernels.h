@@ -83,4 +83,26 @@ hipError_t launch_attention(const T* q, const T* k, const T* vt, T* out, const u
                             const int32_t* list_real, const int32_t* list_pad, const int32_t* meta, void* scratch,
                             int B, int S, int H, int stride, float scale, hipStream_t st);
 
+// ---- timestep conditioning (AdaLN table build) ----
+enum InMode { kInPlain = 0, kInSilu = 1, kInSinusoid = 2 };
+// y = in(x)[M, K] . W[N, K]^T in fp32 (N % 16 == 0, K % 16 == 0). in(x): x
+// itself, SiLU(x), or the sinusoid of the M timesteps in x (K = width).
+// splits == 1 (after rounding the K range to multiples of 16): out row
+// (n / ng) * M + m, column n % ng, gets act(y + bias) (ng % 16 == 0, bias may
+// be null). splits > 1: out is the partial-sum buffer [splits][M][N]; the
+// split count actually used is skinny_splits(K, splits).
+hipError_t launch_skinny_f32(int in_mode, const float* x, const float* w, const float* bias, float* out, int M, int N,
+                             int K, int splits, int ng, int act, float period, hipStream_t st);
+int skinny_splits(int K, int splits);
+// out[M, N] = act(sum of `splits` partial sums + bias); with prev the blend
+// (1 - gate) prev + gate * that (prev may equal out). N % 4 == 0.
+hipError_t launch_rows_finish(const float* part, int splits, const float* bias, float* out, int M, int N, int act,
+                              const float* prev, float gate, hipStream_t st);
+// table[(n / ng) * M + m][n % ng] = W[n] . bf16(SiLU(emb[m])) + bias[n] with
+// bf16 W [N, K] and bias [N] (may be null), N % 64 == 0, K % 32 == 0.
+// a_scratch: adaln_proj_rows(M) * K bf16 values.
+int adaln_proj_rows(int M);
+hipError_t launch_adaln_proj(const float* emb, const uint16_t* w, const uint16_t* bias, uint16_t* a_scratch, float* table,
+                             int M, int N, int K, int ng, hipStream_t st);
+
 }  // namespace minih3

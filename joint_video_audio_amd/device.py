@@ -41,3 +41,11 @@ def upload(wl: Workload, device="cuda"):
     """(config, layout, [blocks], x) on the device."""
     return config_for(wl.dims), layout_for(wl, device), [block_for(b, device) for b in wl.blocks], \
         to_device(wl.x, device)
+
+
+def time_config_for(cond, max_period: float = 1.0e4) -> m.TimeConfig:
+    return m.TimeConfig(cond.freq_dim, cond.hidden_dim, cond.embed_dim, float(max_period))
+
+
+def time_mlp_for(te, device="cuda") -> m.DeviceTimeMLP:
+    return m.DeviceTimeMLP(f32(te.w1, device), f32(te.b1, device), f32(te.w2, device), f32(te.b2, device))

@@ -57,6 +57,15 @@ class _Taps(ctypes.Structure):
     _fields_ = [(n, _P) for n in TAP_FLOAT + TAP_INT]
 
 
+class TimeConfig(ctypes.Structure):
+    _fields_ = [("freq_dim", ctypes.c_int32), ("hidden_dim", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
+                ("max_period", ctypes.c_float)]
+
+
+class _TimeMLP(ctypes.Structure):
+    _fields_ = [("w1", _P), ("b1", _P), ("w2", _P), ("b2", _P)]
+
+
 class Minih3Error(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -97,9 +106,19 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_int32, _P]
         L.minih3_linear.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
         L.minih3_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), _I32P, ctypes.c_int32]
+        L.minih3_time_embed_workspace_bytes.argtypes = [ctypes.POINTER(TimeConfig), ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_time_embed.argtypes = [ctypes.POINTER(TimeConfig), ctypes.POINTER(_TimeMLP), _P,
+                                        ctypes.POINTER(_TimeMLP), _P, ctypes.c_float, ctypes.c_int32, _P, _P,
+                                        ctypes.c_size_t, _P]
+        L.minih3_adaln_table_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_adaln_table.argtypes = [ctypes.POINTER(Config), _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t,
+                                         _P]
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
                    "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
-                   "minih3_profile_collect"):
+                   "minih3_profile_collect", "minih3_time_embed_workspace_bytes", "minih3_time_embed",
+                   "minih3_adaln_table_workspace_bytes", "minih3_adaln_table"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -107,7 +126,9 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_workspace_bytes",
             "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
-            "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string")
+            "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
+            "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
+            "minih3_adaln_table")
 
 
 def status_string(s: int) -> str:
@@ -317,6 +338,76 @@ def linear(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None)
         out = torch.empty(M, N, dtype=a.dtype, device=a.device)
     _req(out, a.dtype, "out", M * N)
     _check(lib().minih3_linear(dtc, _ptr(a), _ptr(w), _ptr(out), M, N, K, _stream()), "linear")
+    return out
+
+
+class DeviceTimeMLP:
+    """fp32 device weights of one timestep MLP (w1 [hidden, freq], w2 [embed, hidden])."""
+
+    def __init__(self, w1, b1, w2, b2):
+        self.w1, self.b1, self.w2, self.b2 = w1, b1, w2, b2
+
+    def check(self, tc: TimeConfig):
+        _req(self.w1, torch.float32, "w1", tc.hidden_dim * tc.freq_dim)
+        _req(self.w2, torch.float32, "w2", tc.embed_dim * tc.hidden_dim)
+        if self.b1 is not None:
+            _req(self.b1, torch.float32, "b1", tc.hidden_dim)
+        if self.b2 is not None:
+            _req(self.b2, torch.float32, "b2", tc.embed_dim)
+
+    def c(self) -> _TimeMLP:
+        return _TimeMLP(*(_ptr(t) for t in (self.w1, self.b1, self.w2, self.b2)))
+
+
+def time_embed(tc: TimeConfig, base: DeviceTimeMLP, t: torch.Tensor, endpoint: Optional[DeviceTimeMLP] = None,
+               r: Optional[torch.Tensor] = None, gate: float = 0.0,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """t [n] fp32 -> time embeddings [n, embed_dim] fp32 (two-time blend with an endpoint MLP)."""
+    n = t.numel()
+    _req(t, torch.float32, "t", n)
+    base.check(tc)
+    if endpoint is not None:
+        endpoint.check(tc)
+    if r is not None:
+        _req(r, torch.float32, "r", n)
+    if out is None:
+        out = torch.empty(n, tc.embed_dim, dtype=torch.float32, device=t.device)
+    _req(out, torch.float32, "out", n * tc.embed_dim)
+    nb = ctypes.c_size_t(0)
+    _check(lib().minih3_time_embed_workspace_bytes(ctypes.byref(tc), n, ctypes.byref(nb)), "time_embed")
+    ws = alloc_workspace(int(nb.value), t.device)
+    cb = base.c()
+    ce = endpoint.c() if endpoint is not None else None
+    _check(lib().minih3_time_embed(ctypes.byref(tc), ctypes.byref(cb), _ptr(t),
+                                   ctypes.byref(ce) if ce is not None else None, _ptr(r), float(gate), n, _ptr(out),
+                                   _ptr(ws), ws.numel(), _stream()), "time_embed")
+    return out
+
+
+def adaln_table_workspace_bytes(cfg: Config, embed_dim: int) -> int:
+    nb = ctypes.c_size_t(0)
+    _check(lib().minih3_adaln_table_workspace_bytes(ctypes.byref(cfg), embed_dim, ctypes.byref(nb)),
+           "adaln_table_workspace_bytes")
+    return int(nb.value)
+
+
+def adaln_table(cfg: Config, emb: torch.Tensor, w_proj: torch.Tensor, b_proj: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """emb [num_tvals, E] fp32, w_proj [tags, 6D, E] act -> table [tags, num_tvals, 6, D] fp32."""
+    dt = act_torch_dtype(cfg)
+    T, V, D = cfg.num_tags, cfg.num_tvals, cfg.hidden
+    E = emb.shape[-1]
+    _req(emb, torch.float32, "emb", V * E)
+    _req(w_proj, dt, "w_proj", T * 6 * D * E)
+    if b_proj is not None:
+        _req(b_proj, dt, "b_proj", T * 6 * D)
+    if out is None:
+        out = torch.empty(T, V, 6, D, dtype=torch.float32, device=emb.device)
+    _req(out, torch.float32, "table", T * V * 6 * D)
+    if workspace is None:
+        workspace = alloc_workspace(adaln_table_workspace_bytes(cfg, E), emb.device)
+    _check(lib().minih3_adaln_table(ctypes.byref(cfg), _ptr(emb), E, _ptr(w_proj), _ptr(b_proj), _ptr(out),
+                                    _ptr(workspace), workspace.numel(), _stream()), "adaln_table")
     return out
 
 

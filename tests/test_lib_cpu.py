@@ -63,3 +63,28 @@ def test_host_side_queries_and_argument_errors():
     s = lib.minih3_block_forward(ctypes.byref(cfg), ctypes.byref(L_big), bw, 1, ctypes.c_void_p(16),
                                  ctypes.c_void_p(32), ctypes.c_void_p(64), 10, 0, None, None)
     assert s == m.E_UNSUPPORTED
+
+
+def test_conditioning_host_side_checks():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libminih3.so not built")
+    lib = m.lib()
+    tc = m.TimeConfig(256, 5376, 2688, 1.0e4)
+    n = ctypes.c_size_t(0)
+    assert lib.minih3_time_embed_workspace_bytes(ctypes.byref(tc), 64, ctypes.byref(n)) == m.OK
+    # the hidden activations and eight split-K partial sums, fp32
+    assert n.value >= 64 * 5376 * 4 + 8 * 64 * 2688 * 4
+    bad = m.TimeConfig(200, 5376, 2688, 1.0e4)
+    assert lib.minih3_time_embed_workspace_bytes(ctypes.byref(bad), 64, ctypes.byref(n)) == m.E_UNSUPPORTED
+    mlp = m._TimeMLP(ctypes.c_void_p(16), None, ctypes.c_void_p(16), None)
+    assert lib.minih3_time_embed(ctypes.byref(tc), ctypes.byref(mlp), None, None, None, 0.0, 64,
+                                 ctypes.c_void_p(16), ctypes.c_void_p(16), 1 << 30, None) == m.E_ARG
+    assert lib.minih3_time_embed(ctypes.byref(tc), ctypes.byref(mlp), ctypes.c_void_p(16), None, None, 0.0, 64,
+                                 ctypes.c_void_p(16), ctypes.c_void_p(16), 10, None) == m.E_WORKSPACE
+    cfg = dv.config_for(synth.workload_dims("clip32k"))
+    assert lib.minih3_adaln_table_workspace_bytes(ctypes.byref(cfg), 2688, ctypes.byref(n)) == m.OK
+    assert n.value >= 64 * 2688 * 2
+    p = ctypes.c_void_p(16)
+    assert lib.minih3_adaln_table(ctypes.byref(cfg), p, 2688, p, None, p, p, 10, None) == m.E_WORKSPACE
+    assert lib.minih3_adaln_table(ctypes.byref(cfg), p, 2680, p, None, p, p, 1 << 30, None) == m.E_UNSUPPORTED
+    assert lib.minih3_adaln_table(ctypes.byref(cfg), None, 2688, p, None, p, p, 1 << 30, None) == m.E_ARG
