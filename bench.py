@@ -15,6 +15,9 @@ only (GEMMs on non-padding rows, attention on same-document pairs of
 non-padding rows). The dominant kernel's roofline uses its average launch
 time from HIP events recorded on the launch stream inside the timed region.
 cpu_baseline times the fp64 oracle on a bounded sample of the workload.
+table_build times, apart from the step, the build of one block's AdaLN
+table from the workload's timestep values (time embeddings, then the bf16
+AdaLN projection), with the projection's HBM roofline.
 """
 from __future__ import annotations
 
@@ -97,6 +100,61 @@ def cpu_baseline(wl, rows: int):
                        f"by algorithmic FLOP per row")
 
 
+def table_build(wl, seed: int, reps: int, warmup: int):
+    """Time the AdaLN table build of one block for the workload's timestep
+    values: the time embeddings (two-time on the clip workload, whose values
+    are (sigma_now, sigma_next) pairs) and the bf16 AdaLN projection. HIP
+    events bracket each call on the stream the library launches on."""
+    import torch
+    from joint_video_audio_amd import device as dv
+    from joint_video_audio_amd import minih3 as m
+    from joint_video_audio_amd import synth
+    dims = wl.dims
+    two = wl.name == "clip32k"
+    cond = synth.make_conditioning(dims, two_time=two, seed=seed)
+    cfg = dv.config_for(dims)
+    tc = dv.time_config_for(cond)
+    base = dv.time_mlp_for(cond.base)
+    ep = dv.time_mlp_for(cond.endpoint) if two else None
+    t = dv.f32(cond.t)
+    r = dv.f32(cond.r) if two else None
+    wp, bp = dv.to_device(cond.w_proj[0]), dv.to_device(cond.b_proj[0])
+    n, E, D, T = dims.num_tvals, cond.embed_dim, dims.hidden, dims.num_tags
+    emb = torch.empty(n, E, dtype=torch.float32, device="cuda")
+    table = torch.empty(T, n, 6, D, dtype=torch.float32, device="cuda")
+    ws_t = m.alloc_workspace(m.time_embed_workspace_bytes(tc, n))
+    ws_a = m.alloc_workspace(m.adaln_table_workspace_bytes(cfg, E))
+
+    def run():
+        m.time_embed(tc, base, t, ep, r, cond.gate, out=emb, workspace=ws_t)
+        m.adaln_table(cfg, emb, wp, bp, out=table, workspace=ws_a)
+
+    for _ in range(warmup):
+        run()
+    st = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1, e2 in evs:
+        e0.record(st)
+        m.time_embed(tc, base, t, ep, r, cond.gate, out=emb, workspace=ws_t)
+        e1.record(st)
+        m.adaln_table(cfg, emb, wp, bp, out=table, workspace=ws_a)
+        e2.record(st)
+    torch.cuda.synchronize()
+    te = sum(e0.elapsed_time(e1) for e0, e1, _ in evs) / reps
+    ta = sum(e1.elapsed_time(e2) for _, e1, e2 in evs) / reps
+    # algorithmic HBM bytes of the projection: bf16 weights and biases, fp32
+    # time embeddings in, fp32 table out
+    el = 2 if dims.dtype == "bf16" else 4
+    nbytes = T * 6 * D * E * el + T * 6 * D * el + n * E * 4 + T * n * 6 * D * 4
+    gbs = nbytes / (ta / 1e3) / 1e9
+    return {"timestep_values": n, "two_time": two, "freq_dim": cond.freq_dim, "mlp_hidden": cond.hidden_dim,
+            "embed_dim": E, "reps": reps, "time_embed_ms": round(te, 4), "adaln_table_ms": round(ta, 4),
+            "roofline": {"kernel": "adaln_table", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes": nbytes, "avg_launch_ms": round(ta, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +164,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-table-build", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -197,6 +256,8 @@ def main():
                      "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(a.workload),
                      "avg_launch_ms": round(att_avg, 4)},
     }
+    if not a.no_table_build:
+        res["table_build"] = table_build(wl, a.seed, reps=50, warmup=5)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)

@@ -330,7 +330,7 @@ LayoutDev make_layout_dev(const minih3_config* c, const minih3_layout* L) {
 
 
 // ---- timestep conditioning ----
-constexpr int kTimeSplits = 8;  // K splits of the timestep MLP's second layer
+constexpr int kTimeSplits = 16;  // K splits of the timestep MLP's second layer
 
 int check_time_config(const minih3_time_config* tc) {
   if (!tc) return MINIH3_E_ARG;
@@ -342,17 +342,19 @@ int check_time_config(const minih3_time_config* tc) {
 }
 
 struct TimeWorkspace {
-  float *h, *part;
+  float *s, *h, *part;
   size_t total;
 };
 
 TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base) {
   TimeWorkspace w{};
-  const size_t hb = align_up((size_t)M * tc->hidden_dim * 4);
+  const size_t sb = align_up((size_t)padded_rows(M) * tc->freq_dim * 4);
+  const size_t hb = align_up((size_t)padded_rows(M) * tc->hidden_dim * 4);
   const size_t pb = align_up((size_t)skinny_splits(tc->hidden_dim, kTimeSplits) * M * tc->embed_dim * 4);
-  w.h = base ? (float*)base : nullptr;
-  w.part = base ? (float*)(base + hb) : nullptr;
-  w.total = hb + pb;
+  w.s = base ? (float*)base : nullptr;
+  w.h = base ? (float*)(base + sb) : nullptr;
+  w.part = base ? (float*)(base + sb + hb) : nullptr;
+  w.total = sb + hb + pb;
   return w;
 }
 
@@ -361,10 +363,10 @@ TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base) {
 int time_mlp(const minih3_time_config* tc, const minih3_time_mlp* m, const float* t, int M, float* emb, bool blend,
              float gate, TimeWorkspace& w, hipStream_t st) {
   const int F = tc->freq_dim, Hd = tc->hidden_dim, E = tc->embed_dim;
-  HIPCHECK(launch_skinny_f32(kInSinusoid, t, m->w1, m->b1, w.h, M, Hd, F, 1, Hd, 1, tc->max_period, st));
+  HIPCHECK(launch_sinusoid(t, w.s, M, F, tc->max_period, st));
+  HIPCHECK(launch_skinny_f32(kFragToFrag, w.s, m->w1, m->b1, w.h, M, Hd, F, 1, Hd, 1, st));
   const int splits = skinny_splits(Hd, kTimeSplits);  // what the launch below uses
-  HIPCHECK(launch_skinny_f32(kInPlain, w.h, m->w2, nullptr, w.part, M, E, Hd, kTimeSplits, E, 0, tc->max_period,
-                             st));
+  HIPCHECK(launch_skinny_f32(kFragToRows, w.h, m->w2, nullptr, w.part, M, E, Hd, kTimeSplits, E, 0, st));
   HIPCHECK(launch_rows_finish(w.part, splits, m->b2, emb, M, E, 0, blend ? emb : nullptr, gate, st));
   return MINIH3_OK;
 }
@@ -579,7 +581,7 @@ int minih3_time_embed(const minih3_time_config* tc, const minih3_time_mlp* base,
 
 int minih3_adaln_table_workspace_bytes(const minih3_config* c, int32_t embed_dim, size_t* bytes) {
   if (!c || !bytes || c->num_tvals < 1 || embed_dim < 1) return MINIH3_E_ARG;
-  *bytes = c->act_dtype == MINIH3_BF16 ? align_up((size_t)adaln_proj_rows(c->num_tvals) * embed_dim * 2) : 0;
+  *bytes = c->act_dtype == MINIH3_BF16 ? align_up((size_t)padded_rows(c->num_tvals) * embed_dim * 2) : 0;
   return MINIH3_OK;
 }
 
@@ -594,12 +596,12 @@ int minih3_adaln_table(const minih3_config* c, const float* emb, int32_t embed_d
   hipStream_t st = (hipStream_t)stream;
   if (c->act_dtype == MINIH3_F32) {
     if (embed_dim % 16 != 0) return MINIH3_E_UNSUPPORTED;
-    HIPCHECK(launch_skinny_f32(kInSilu, emb, (const float*)w_proj, (const float*)b_proj, table, (int)M, (int)N,
-                               embed_dim, 1, (int)ng, 0, 1.f, st));
+    HIPCHECK(launch_skinny_f32(kRowsSilu, emb, (const float*)w_proj, (const float*)b_proj, table, (int)M, (int)N,
+                               embed_dim, 1, (int)ng, 0, st));
     return MINIH3_OK;
   }
   if (embed_dim % 32 != 0) return MINIH3_E_UNSUPPORTED;
-  const size_t need = align_up((size_t)adaln_proj_rows((int)M) * embed_dim * 2);
+  const size_t need = align_up((size_t)padded_rows((int)M) * embed_dim * 2);
   if (!workspace || workspace_bytes < need) return MINIH3_E_WORKSPACE;
   HIPCHECK(launch_adaln_proj(emb, (const bf16_t*)w_proj, (const bf16_t*)b_proj, (bf16_t*)workspace, table, (int)M,
                              (int)N, embed_dim, (int)ng, st));

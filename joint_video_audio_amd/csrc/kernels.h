@@ -84,15 +84,26 @@ hipError_t launch_attention(const T* q, const T* k, const T* vt, T* out, const u
                             int B, int S, int H, int stride, float scale, hipStream_t st);
 
 // ---- timestep conditioning (AdaLN table build) ----
-enum InMode { kInPlain = 0, kInSilu = 1, kInSinusoid = 2 };
-// y = in(x)[M, K] . W[N, K]^T in fp32 (N % 16 == 0, K % 16 == 0). in(x): x
-// itself, SiLU(x), or the sinusoid of the M timesteps in x (K = width).
-// splits == 1 (after rounding the K range to multiples of 16): out row
-// (n / ng) * M + m, column n % ng, gets act(y + bias) (ng % 16 == 0, bias may
-// be null). splits > 1: out is the partial-sum buffer [splits][M][N]; the
-// split count actually used is skinny_splits(K, splits).
-hipError_t launch_skinny_f32(int in_mode, const float* x, const float* w, const float* bias, float* out, int M, int N,
-                             int K, int splits, int ng, int act, float period, hipStream_t st);
+enum InMode { kInPlain = 0, kInSilu = 1 };
+// Row count of the padded conditioning operands: M rounded up to the row
+// chunk a launch column covers (16, 32 or 64 rows).
+int padded_rows(int M);
+// Fragment order of an fp32 [Mpad, K] operand: the 16-byte unit
+// (mb * (K / 16) + st) * 64 + lane, lane = r16 + 16 q, holds row 16 mb + r16,
+// columns 16 st + 4q .. +3 (an MFMA 16x16x4 operand / accumulator block).
+// s = [cos(t f_c), sin(t f_c)] over F columns, f_c = period^(-c / (F/2)),
+// in fragment order with padded_rows(M) rows (zero past M); F % 32 == 0.
+hipError_t launch_sinusoid(const float* t, float* s, int M, int F, float period, hipStream_t st);
+// y = x[M, K] . W[N, K]^T in fp32 (N % 16 == 0, K % 16 == 0) in one of three
+// modes: kFragToFrag (x in fragment order; act(y + bias) written in fragment
+// order with padded_rows(M) rows; one split only), kFragToRows (x in
+// fragment order; partial sums [splits][M][N], or with one split act(y +
+// bias) row-major), kRowsSilu (x row-major, input SiLU(x)). Row-major
+// results go to out row (n / ng) * M + m, column n % ng (ng % 16 == 0); bias
+// may be null. The split count actually used is skinny_splits(K, splits).
+enum SkinnyMode { kFragToFrag = 0, kFragToRows = 1, kRowsSilu = 2 };
+hipError_t launch_skinny_f32(int mode, const float* x, const float* w, const float* bias, float* out, int M, int N,
+                             int K, int splits, int ng, int act, hipStream_t st);
 int skinny_splits(int K, int splits);
 // out[M, N] = act(sum of `splits` partial sums + bias); with prev the blend
 // (1 - gate) prev + gate * that (prev may equal out). N % 4 == 0.
@@ -100,8 +111,8 @@ hipError_t launch_rows_finish(const float* part, int splits, const float* bias, 
                               const float* prev, float gate, hipStream_t st);
 // table[(n / ng) * M + m][n % ng] = W[n] . bf16(SiLU(emb[m])) + bias[n] with
 // bf16 W [N, K] and bias [N] (may be null), N % 64 == 0, K % 32 == 0.
-// a_scratch: adaln_proj_rows(M) * K bf16 values.
-int adaln_proj_rows(int M);
+// a_scratch: padded_rows(M) * K bf16 values (SiLU(emb) in bf16, stored in
+// MFMA fragment order).
 hipError_t launch_adaln_proj(const float* emb, const uint16_t* w, const uint16_t* bias, uint16_t* a_scratch, float* table,
                              int M, int N, int K, int ng, hipStream_t st);
 

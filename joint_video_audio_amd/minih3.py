@@ -359,9 +359,16 @@ class DeviceTimeMLP:
         return _TimeMLP(*(_ptr(t) for t in (self.w1, self.b1, self.w2, self.b2)))
 
 
+def time_embed_workspace_bytes(tc: TimeConfig, num_tvals: int) -> int:
+    nb = ctypes.c_size_t(0)
+    _check(lib().minih3_time_embed_workspace_bytes(ctypes.byref(tc), num_tvals, ctypes.byref(nb)),
+           "time_embed_workspace_bytes")
+    return int(nb.value)
+
+
 def time_embed(tc: TimeConfig, base: DeviceTimeMLP, t: torch.Tensor, endpoint: Optional[DeviceTimeMLP] = None,
-               r: Optional[torch.Tensor] = None, gate: float = 0.0,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               r: Optional[torch.Tensor] = None, gate: float = 0.0, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """t [n] fp32 -> time embeddings [n, embed_dim] fp32 (two-time blend with an endpoint MLP)."""
     n = t.numel()
     _req(t, torch.float32, "t", n)
@@ -373,9 +380,7 @@ def time_embed(tc: TimeConfig, base: DeviceTimeMLP, t: torch.Tensor, endpoint: O
     if out is None:
         out = torch.empty(n, tc.embed_dim, dtype=torch.float32, device=t.device)
     _req(out, torch.float32, "out", n * tc.embed_dim)
-    nb = ctypes.c_size_t(0)
-    _check(lib().minih3_time_embed_workspace_bytes(ctypes.byref(tc), n, ctypes.byref(nb)), "time_embed")
-    ws = alloc_workspace(int(nb.value), t.device)
+    ws = workspace if workspace is not None else alloc_workspace(time_embed_workspace_bytes(tc, n), t.device)
     cb = base.c()
     ce = endpoint.c() if endpoint is not None else None
     _check(lib().minih3_time_embed(ctypes.byref(tc), ctypes.byref(cb), _ptr(t),
