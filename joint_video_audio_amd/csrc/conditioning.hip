@@ -18,8 +18,8 @@
 //    partial sums are added in a fixed order by k_rows_finish, which also
 //    applies the bias, the SiLU and the two-time blend.
 //  * k_adaln_proj: the bf16 table projection on v_mfma_f32_16x16x32_bf16;
-//    a wave owns 64 weight rows and keeps four k-steps of weight and
-//    activation fragments in flight.
+//    a wave owns 64 weight rows and streams them through its own LDS ring
+//    in long contiguous runs.
 #include "common.h"
 #include "kernels.h"
 
@@ -213,60 +213,115 @@ __global__ void __launch_bounds__(256) k_silu_bf16(const float* __restrict__ e, 
   *reinterpret_cast<u32x4*>(a + u * 8) = r;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS (buffer form): lane
+// L of the wave lands at dst + 16 L; voff is the lane's byte offset.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, lds_ptr_t dst) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
 // table[(n / ng) * M + m][n % ng] = sum_k a[m, k] W[n, k] + bias[n] with
 // bf16 W and a, fp32 accumulation. One wave per workgroup owns weight rows
 // n0 .. n0+63 (four 16-row blocks) and MB 16-row blocks of a from m0.
-// a has Mpad rows (a multiple of 16 MB, zero past M) in fragment order, so
-// each of its loads is one contiguous 1 KB; K is a multiple of 32.
+//
+// The weights are the only large operand. They are streamed through a
+// three-stage LDS ring private to the wave (no barriers): a stage is 128
+// columns of the 64 rows, moved by 16 buffer-to-LDS instructions that each
+// read 4 rows x 256 contiguous bytes, so every row is fetched in long runs.
+// Row r of a stage sits at r * 256 bytes with 16-byte chunk c stored at c ^
+// (r & 15): the 16 lanes of a fragment read (16 rows, one chunk) hit 16
+// different bank groups. a has Mpad rows (a multiple of 16 MB, zero past M)
+// in fragment order, so each of its loads is one contiguous 1 KB; it is
+// loaded into registers in the same group as the stage's weights, which
+// keeps the in-order load counter exact. K is a multiple of 32; columns past
+// K are clamped on load and their k-steps skipped.
 template <int MB>
 __global__ void __launch_bounds__(64) k_adaln_proj(const bf16_t* __restrict__ w, const bf16_t* __restrict__ bias,
                                                    const bf16_t* __restrict__ a, float* __restrict__ table, int M,
                                                    int K, int ng) {
-  constexpr int NB = 4, PF = 4;
+  constexpr int NB = 4, NS = 3, SPS = 4;         // n-blocks, ring stages, k-steps per stage
+  constexpr int kStageBytes = 64 * SPS * 64;     // 64 rows x 256 bytes
+  constexpr int kOps = 16 + SPS * MB;            // loads issued per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * kStageBytes];
   const int lane = threadIdx.x;
   const int r16 = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * 16 * NB;
   const int m0 = blockIdx.y * 16 * MB;
-  const long kb16 = 16L * K;
-  const bf16_t* wp = w + (long)(n0 + r16) * K + 8 * q;
-  const bf16_t* ap = a + ((long)(m0 / 16) * (K / 32) * 64 + lane) * 8;  // fragment-major
-  const int KT = K / 32;
+  const int KT = K / 32, KG = (KT + SPS - 1) / SPS;
+  const bf16_t* ap = a + ((long)(m0 / 16) * KT * 64 + lane) * 8;  // fragment order
 
   floatx4 acc[NB][MB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  u32x4 wf[PF][NB], af[PF][MB];
+  u32x4 af[NS][SPS][MB];
 
-  // Fragments of k-step s: lane (r16, q) holds W[n0 + 16 i + r16][32 s + 8q .. +7]
-  // (A operand) and a[m0 + 16 j + r16][32 s + 8q .. +7] (B operand). Steps
-  // past the end re-read the last one (and are not accumulated), so every
-  // iteration issues the same loads and the in-order load counter stays exact.
-  auto load = [&](int slot, int s) {
-    s = min(s, KT - 1);
+  // DMA instruction j of a stage: rows 4j .. 4j+3; lane L takes row
+  // 4j + L/16 and logical chunk (L % 16) ^ (row & 15) of the stage's 256 bytes.
+  const int drow0 = lane >> 4, dchunk = lane & 15;
+  // Stage g: weight columns 128 g .. 128 g + 127 into ring slot `slot`, and
+  // the a fragments of k-steps 4 g .. 4 g + 3 (clamped to the last one).
+  auto issue = [&](int slot, int g) {
+    g = min(g, KG - 1);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) wf[slot][i] = *reinterpret_cast<const u32x4*>(wp + i * kb16 + 32 * s);
+    for (int j = 0; j < 16; ++j) {
+      const int row = 4 * j + drow0;
+      const int col = min(128 * g + 8 * (dchunk ^ (row & 15)), K - 8);
+      dma16(w, (uint32_t)(((long)(n0 + row) * K + col) * 2),
+            (lds_ptr_t)(lds + slot * kStageBytes + j * 1024));
+    }
 #pragma unroll
-    for (int j = 0; j < MB; ++j) af[slot][j] = *reinterpret_cast<const u32x4*>(ap + ((long)j * KT + s) * 512);
+    for (int ss = 0; ss < SPS; ++ss) {
+      const int s = min(SPS * g + ss, KT - 1);
+#pragma unroll
+      for (int jm = 0; jm < MB; ++jm) af[slot][ss][jm] = *reinterpret_cast<const u32x4*>(ap + ((long)jm * KT + s) * 512);
+    }
   };
+  auto compute = [&](int slot, int g) {
+    const uint8_t* st = lds + slot * kStageBytes;
 #pragma unroll
-  for (int s = 0; s < PF - 1; ++s) load(s, s);
-  for (int kt = 0; kt < KT; kt += PF) {
+    for (int ss = 0; ss < SPS; ++ss) {
+      if (SPS * g + ss >= KT) break;
+      u32x4 wf[NB];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      load((s + PF - 1) % PF, kt + s + PF - 1);
-      if (kt + s < KT) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int j = 0; j < MB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[s][i]),
-                                                                __builtin_bit_cast(bf16x8, af[s][j]), acc[i][j], 0,
-                                                                0, 0);
+      for (int i = 0; i < NB; ++i) {
+        const int row = 16 * i + r16;
+        wf[i] = *reinterpret_cast<const u32x4*>(st + row * 256 + 16 * ((SPS * ss + q) ^ (row & 15)));
       }
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int jm = 0; jm < MB; ++jm)
+          acc[i][jm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[i]),
+                                                               __builtin_bit_cast(bf16x8, af[slot][ss][jm]),
+                                                               acc[i][jm], 0, 0, 0);
+    }
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  for (int g0 = 0; g0 < KG; g0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int g = g0 + u;
+      // stage g landed once only the group issued after it is outstanding;
+      // its slot's previous contents were consumed by the last iteration
+      wait_vmcnt<kOps>();
+      issue((u + 2) % NS, g + 2);
+      if (g < KG) compute(u, g);
     }
   }
+  wait_vmcnt<0>();
 
   // Lane (r16, q) holds rows n0 + 16 i + 4q .. +3 for input row m0 + 16 j + r16.
 #pragma unroll
