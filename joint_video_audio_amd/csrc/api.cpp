@@ -342,32 +342,45 @@ int check_time_config(const minih3_time_config* tc) {
 }
 
 struct TimeWorkspace {
-  float *s, *h, *part;
+  float *s[2], *h[2], *part[2];
   size_t total;
 };
 
+// Per chain (base, endpoint): the sinusoid and the hidden activations in
+// fragment order, and the split-K partial sums of the second layer.
 TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base) {
   TimeWorkspace w{};
   const size_t sb = align_up((size_t)padded_rows(M) * tc->freq_dim * 4);
   const size_t hb = align_up((size_t)padded_rows(M) * tc->hidden_dim * 4);
   const size_t pb = align_up((size_t)skinny_splits(tc->hidden_dim, kTimeSplits) * M * tc->embed_dim * 4);
-  w.s = base ? (float*)base : nullptr;
-  w.h = base ? (float*)(base + sb) : nullptr;
-  w.part = base ? (float*)(base + sb + hb) : nullptr;
-  w.total = sb + hb + pb;
+  size_t off = 0;
+  for (int c = 0; c < 2; ++c) {
+    w.s[c] = base ? (float*)(base + off) : nullptr;
+    off += sb;
+    w.h[c] = base ? (float*)(base + off) : nullptr;
+    off += hb;
+    w.part[c] = base ? (float*)(base + off) : nullptr;
+    off += pb;
+  }
+  w.total = off;
   return w;
 }
 
-// One timestep MLP over M timesteps; emb = its output, or the blend
-// (1 - gate) emb + gate * output when blend is set.
-int time_mlp(const minih3_time_config* tc, const minih3_time_mlp* m, const float* t, int M, float* emb, bool blend,
-             float gate, TimeWorkspace& w, hipStream_t st) {
+// The timestep MLP over M timesteps, with the endpoint MLP on r alongside it
+// when `ep` is set (one launch per layer for both); emb = E(t), or the blend
+// (1 - gate) E(t) + gate E'(r).
+int time_mlps(const minih3_time_config* tc, const minih3_time_mlp* m, const float* t, const minih3_time_mlp* ep,
+              const float* r, float gate, int M, float* emb, TimeWorkspace& w, hipStream_t st) {
   const int F = tc->freq_dim, Hd = tc->hidden_dim, E = tc->embed_dim;
-  HIPCHECK(launch_sinusoid(t, w.s, M, F, tc->max_period, st));
-  HIPCHECK(launch_skinny_f32(kFragToFrag, w.s, m->w1, m->b1, w.h, M, Hd, F, 1, Hd, 1, st));
+  const int chains = ep ? 2 : 1;
+  HIPCHECK(launch_sinusoid(t, ep ? r : nullptr, w.s[0], w.s[1], M, F, tc->max_period, st));
+  SkinnyArgs l1{{w.s[0], w.s[1]}, {m->w1, ep ? ep->w1 : nullptr}, {m->b1, ep ? ep->b1 : nullptr}, {w.h[0], w.h[1]}};
+  HIPCHECK(launch_skinny_f32(kFragToFrag, l1, chains, M, Hd, F, 1, Hd, 1, st));
   const int splits = skinny_splits(Hd, kTimeSplits);  // what the launch below uses
-  HIPCHECK(launch_skinny_f32(kFragToRows, w.h, m->w2, nullptr, w.part, M, E, Hd, kTimeSplits, E, 0, st));
-  HIPCHECK(launch_rows_finish(w.part, splits, m->b2, emb, M, E, 0, blend ? emb : nullptr, gate, st));
+  SkinnyArgs l2{{w.h[0], w.h[1]}, {m->w2, ep ? ep->w2 : nullptr}, {nullptr, nullptr}, {w.part[0], w.part[1]}};
+  HIPCHECK(launch_skinny_f32(kFragToRows, l2, chains, M, E, Hd, kTimeSplits, E, 0, st));
+  HIPCHECK(launch_rows_finish(w.part[0], ep ? w.part[1] : nullptr, splits, m->b2, ep ? ep->b2 : nullptr, emb, M, E,
+                              0, gate, st));
   return MINIH3_OK;
 }
 
@@ -574,9 +587,7 @@ int minih3_time_embed(const minih3_time_config* tc, const minih3_time_mlp* base,
   TimeWorkspace w = carve_time(tc, num_tvals, (char*)workspace);
   if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  s = time_mlp(tc, base, t, num_tvals, emb, false, 0.f, w, st);
-  if (s || !endpoint) return s;
-  return time_mlp(tc, endpoint, r ? r : t, num_tvals, emb, true, gate, w, st);
+  return time_mlps(tc, base, t, endpoint, r ? r : t, gate, num_tvals, emb, w, st);
 }
 
 int minih3_adaln_table_workspace_bytes(const minih3_config* c, int32_t embed_dim, size_t* bytes) {
@@ -596,8 +607,8 @@ int minih3_adaln_table(const minih3_config* c, const float* emb, int32_t embed_d
   hipStream_t st = (hipStream_t)stream;
   if (c->act_dtype == MINIH3_F32) {
     if (embed_dim % 16 != 0) return MINIH3_E_UNSUPPORTED;
-    HIPCHECK(launch_skinny_f32(kRowsSilu, emb, (const float*)w_proj, (const float*)b_proj, table, (int)M, (int)N,
-                               embed_dim, 1, (int)ng, 0, st));
+    SkinnyArgs g{{emb, nullptr}, {(const float*)w_proj, nullptr}, {(const float*)b_proj, nullptr}, {table, nullptr}};
+    HIPCHECK(launch_skinny_f32(kRowsSilu, g, 1, (int)M, (int)N, embed_dim, 1, (int)ng, 0, st));
     return MINIH3_OK;
   }
   if (embed_dim % 32 != 0) return MINIH3_E_UNSUPPORTED;

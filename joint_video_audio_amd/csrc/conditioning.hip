@@ -29,6 +29,13 @@ namespace {
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.f + expf(-v)); }
 
+// Operands of up to two independent chains (the base timestep MLP and the
+// step-endpoint one) handled by one launch.
+template <typename P>
+struct Pair {
+  P p[2];
+};
+
 // Four consecutive inputs (row m, columns k..k+3) of the skinny product.
 template <int IN>
 __device__ __forceinline__ floatx4 skinny_in(const float* x, int m, int K, int k) {
@@ -48,9 +55,12 @@ __device__ __forceinline__ floatx4 skinny_in(const float* x, int m, int K, int k
 // moves a 16 x 16 block as one contiguous 1 KB.
 
 // s = [cos(t_m f_c), sin(t_m f_c)] over F columns, f_c = period^(-c / (F/2)),
-// in fragment order with Mpad rows (zero past M); one thread a unit.
-__global__ void __launch_bounds__(256) k_sinusoid(const float* __restrict__ t, float* __restrict__ s, int M, int Mpad,
-                                                  int F, float log2_period) {
+// in fragment order with Mpad rows (zero past M); one thread a unit. Grid
+// row y handles the timesteps t[y] into s[y] (base and step endpoint).
+__global__ void __launch_bounds__(256) k_sinusoid(Pair<const float*> tp, Pair<float*> sp, int M, int Mpad, int F,
+                                                  float log2_period) {
+  const float* __restrict__ t = tp.p[blockIdx.y];
+  float* __restrict__ s = sp.p[blockIdx.y];
   const long u = (long)blockIdx.x * 256 + threadIdx.x;
   if (u >= (long)Mpad * F / 4) return;
   const int lane = (int)(u & 63);
@@ -76,22 +86,28 @@ __global__ void __launch_bounds__(256) k_sinusoid(const float* __restrict__ t, f
 }
 
 // y[m, n] = sum_k in(x)[m, k] W[n, k] over k in this split's range.
-// Grid: (ceil(N/64), splits, ceil(M / (16 MB))), 4 waves of 16 weight rows.
+// Grid: (ceil(N/64), splits, chains * ceil(M / (16 MB))), 4 waves of 16
+// weight rows; grid z picks the chain (its x, W, bias, out) and the row chunk.
 // XF: x is in fragment order with Mpad rows (plain input), else row-major.
 // One split: act(y + bias) goes, with OF, to out in fragment order (Mpad
 // rows, zero past M), else to out row (n / ng) * M + m at column n % ng;
 // several splits: the raw partial sum goes to part[split][m][n].
 template <int IN, int XF, int OF, int MB>
-__global__ void __launch_bounds__(256) k_skinny_f32(const float* __restrict__ x, const float* __restrict__ w,
-                                                    const float* __restrict__ bias, float* __restrict__ out,
-                                                    int M, int N, int K, int kchunk, int ng, int act) {
+__global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<const float*> wp,
+                                                    Pair<const float*> bp, Pair<float*> op, int mchunks, int M,
+                                                    int N, int K, int kchunk, int ng, int act) {
   const int lane = threadIdx.x & 63;
   const int nb = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (nb * 16 >= N) return;  // whole wave; no barrier follows
+  const int chain = blockIdx.z / mchunks;
+  const float* __restrict__ x = xp.p[chain];
+  const float* __restrict__ w = wp.p[chain];
+  const float* __restrict__ bias = bp.p[chain];
+  float* __restrict__ out = op.p[chain];
   const int r16 = lane & 15, q = lane >> 4;
   const int k_beg = blockIdx.y * kchunk;
   const int k_end = min(K, k_beg + kchunk);
-  const int m0 = blockIdx.z * 16 * MB;
+  const int m0 = (blockIdx.z - chain * mchunks) * 16 * MB;
   const float* wr = w + (long)(nb * 16 + r16) * K + 4 * q;
 
   constexpr int PF = 4;
@@ -168,25 +184,30 @@ __global__ void __launch_bounds__(256) k_skinny_f32(const float* __restrict__ x,
   }
 }
 
-// out[m, n] = act(sum_s part[s][m][n] + bias[n]); with prev, the blend
-// (1 - gate) prev[m, n] + gate * that (prev may be out). Four columns a thread.
-__global__ void __launch_bounds__(256) k_rows_finish(const float* __restrict__ part, int splits,
-                                                     const float* __restrict__ bias, float* out, int M, int N,
-                                                     int act, const float* prev, float gate) {
+// y_c[m, n] = act(sum_s part_c[s][m][n] + bias_c[n]) for each chain c; out is
+// y_0, or with two chains the blend (1 - gate) y_0 + gate y_1. Four columns
+// a thread; the partial sums are added in split order.
+__global__ void __launch_bounds__(256) k_rows_finish(Pair<const float*> pp, Pair<const float*> bp, int chains,
+                                                     int splits, float* __restrict__ out, int M, int N, int act,
+                                                     float gate) {
   const long i4 = (long)blockIdx.x * 256 + threadIdx.x;
   const long total4 = (long)M * N / 4;
   if (i4 >= total4) return;
   const long e = i4 * 4;
   const int n = (int)(e % N);
-  floatx4 v = *reinterpret_cast<const floatx4*>(part + e);
-  for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const floatx4*>(part + (long)s * M * N + e);
-  if (bias) v += *reinterpret_cast<const floatx4*>(bias + n);
-  if (act) {
+  floatx4 y[2];
+  for (int c = 0; c < chains; ++c) {
+    const float* part = pp.p[c];
+    floatx4 v = *reinterpret_cast<const floatx4*>(part + e);
+    for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const floatx4*>(part + (long)s * M * N + e);
+    if (bp.p[c]) v += *reinterpret_cast<const floatx4*>(bp.p[c] + n);
+    if (act) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = silu_f(v[j]);
+      for (int j = 0; j < 4; ++j) v[j] = silu_f(v[j]);
+    }
+    y[c] = v;
   }
-  if (prev) v = (1.f - gate) * *reinterpret_cast<const floatx4*>(prev + e) + gate * v;
-  *reinterpret_cast<floatx4*>(out + e) = v;
+  *reinterpret_cast<floatx4*>(out + e) = chains == 2 ? (1.f - gate) * y[0] + gate * y[1] : y[0];
 }
 
 // a = bf16(SiLU(e)) for m < M, zero for M <= m < Mpad, stored in MFMA
@@ -350,37 +371,44 @@ int skinny_kchunk(int K, int splits) { return ((K + splits - 1) / splits + 15) /
 }  // namespace
 
 template <int IN, int XF, int OF>
-static void skinny_launch(dim3 grid, int mb, const float* x, const float* w, const float* bias, float* out, int M,
-                          int N, int K, int kchunk, int ng, int act, hipStream_t st) {
+static void skinny_launch(dim3 grid, int mb, const SkinnyArgs& g, int mchunks, int M, int N, int K, int kchunk,
+                          int ng, int act, hipStream_t st) {
+  const Pair<const float*> xp{{g.x[0], g.x[1]}}, wp{{g.w[0], g.w[1]}}, bp{{g.bias[0], g.bias[1]}};
+  const Pair<float*> op{{g.out[0], g.out[1]}};
   if (mb == 4)
-    k_skinny_f32<IN, XF, OF, 4><<<grid, 256, 0, st>>>(x, w, bias, out, M, N, K, kchunk, ng, act);
+    k_skinny_f32<IN, XF, OF, 4><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act);
   else if (mb == 2)
-    k_skinny_f32<IN, XF, OF, 2><<<grid, 256, 0, st>>>(x, w, bias, out, M, N, K, kchunk, ng, act);
+    k_skinny_f32<IN, XF, OF, 2><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act);
   else
-    k_skinny_f32<IN, XF, OF, 1><<<grid, 256, 0, st>>>(x, w, bias, out, M, N, K, kchunk, ng, act);
+    k_skinny_f32<IN, XF, OF, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act);
 }
 
-hipError_t launch_skinny_f32(int mode, const float* x, const float* w, const float* bias, float* out, int M, int N,
-                             int K, int splits, int ng, int act, hipStream_t st) {
+hipError_t launch_skinny_f32(int mode, const SkinnyArgs& g, int chains, int M, int N, int K, int splits, int ng,
+                             int act, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  if (chains < 1 || chains > 2) return hipErrorInvalidValue;
   const int mb = mblocks(M);
   const int kchunk = skinny_kchunk(K, splits);
   splits = (K + kchunk - 1) / kchunk;
   if (mode == kFragToFrag && splits != 1) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)splits, (unsigned)((M + 16 * mb - 1) / (16 * mb)));
+  const int mchunks = (M + 16 * mb - 1) / (16 * mb);
+  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)splits, (unsigned)(chains * mchunks));
   if (mode == kFragToFrag)
-    skinny_launch<kInPlain, 1, 1>(grid, mb, x, w, bias, out, M, N, K, kchunk, ng, act, st);
+    skinny_launch<kInPlain, 1, 1>(grid, mb, g, mchunks, M, N, K, kchunk, ng, act, st);
   else if (mode == kFragToRows)
-    skinny_launch<kInPlain, 1, 0>(grid, mb, x, w, bias, out, M, N, K, kchunk, ng, act, st);
+    skinny_launch<kInPlain, 1, 0>(grid, mb, g, mchunks, M, N, K, kchunk, ng, act, st);
   else
-    skinny_launch<kInSilu, 0, 0>(grid, mb, x, w, bias, out, M, N, K, kchunk, ng, act, st);
+    skinny_launch<kInSilu, 0, 0>(grid, mb, g, mchunks, M, N, K, kchunk, ng, act, st);
   return hipGetLastError();
 }
 
-hipError_t launch_sinusoid(const float* t, float* s, int M, int F, float period, hipStream_t st) {
+hipError_t launch_sinusoid(const float* t0, const float* t1, float* s0, float* s1, int M, int F, float period,
+                           hipStream_t st) {
   const long n = (long)padded_rows(M) * F / 4;
   if (n <= 0) return hipSuccess;
-  k_sinusoid<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(t, s, M, padded_rows(M), F, log2f(period));
+  const int chains = t1 ? 2 : 1;
+  k_sinusoid<<<dim3((unsigned)((n + 255) / 256), (unsigned)chains), 256, 0, st>>>(
+      Pair<const float*>{{t0, t1}}, Pair<float*>{{s0, s1}}, M, padded_rows(M), F, log2f(period));
   return hipGetLastError();
 }
 
@@ -389,11 +417,13 @@ int skinny_splits(int K, int splits) {
   return (K + kchunk - 1) / kchunk;
 }
 
-hipError_t launch_rows_finish(const float* part, int splits, const float* bias, float* out, int M, int N, int act,
-                              const float* prev, float gate, hipStream_t st) {
+hipError_t launch_rows_finish(const float* part0, const float* part1, int splits, const float* bias0,
+                              const float* bias1, float* out, int M, int N, int act, float gate, hipStream_t st) {
   const long n4 = (long)M * N / 4;
   if (n4 <= 0) return hipSuccess;
-  k_rows_finish<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(part, splits, bias, out, M, N, act, prev, gate);
+  k_rows_finish<<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
+      Pair<const float*>{{part0, part1}}, Pair<const float*>{{bias0, bias1}}, part1 ? 2 : 1, splits, out, M, N, act,
+      gate);
   return hipGetLastError();
 }
 

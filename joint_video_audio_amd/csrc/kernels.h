@@ -93,22 +93,33 @@ int padded_rows(int M);
 // columns 16 st + 4q .. +3 (an MFMA 16x16x4 operand / accumulator block).
 // s = [cos(t f_c), sin(t f_c)] over F columns, f_c = period^(-c / (F/2)),
 // in fragment order with padded_rows(M) rows (zero past M); F % 32 == 0.
-hipError_t launch_sinusoid(const float* t, float* s, int M, int F, float period, hipStream_t st);
-// y = x[M, K] . W[N, K]^T in fp32 (N % 16 == 0, K % 16 == 0) in one of three
-// modes: kFragToFrag (x in fragment order; act(y + bias) written in fragment
-// order with padded_rows(M) rows; one split only), kFragToRows (x in
-// fragment order; partial sums [splits][M][N], or with one split act(y +
-// bias) row-major), kRowsSilu (x row-major, input SiLU(x)). Row-major
-// results go to out row (n / ng) * M + m, column n % ng (ng % 16 == 0); bias
-// may be null. The split count actually used is skinny_splits(K, splits).
+// With t1 non-null, s1 gets the embedding of t1 in the same launch.
+hipError_t launch_sinusoid(const float* t0, const float* t1, float* s0, float* s1, int M, int F, float period,
+                           hipStream_t st);
+// y = x[M, K] . W[N, K]^T in fp32 (N % 16 == 0, K % 16 == 0) for one or two
+// independent chains (x, W, bias, out of chain c at index c) in one launch,
+// in one of three modes: kFragToFrag (x in fragment order; act(y + bias)
+// written in fragment order with padded_rows(M) rows; one split only),
+// kFragToRows (x in fragment order; partial sums [splits][M][N], or with
+// one split act(y + bias) row-major), kRowsSilu (x row-major, input
+// SiLU(x)). Row-major results go to out row (n / ng) * M + m, column n % ng
+// (ng % 16 == 0); bias may be null. The split count actually used is
+// skinny_splits(K, splits).
 enum SkinnyMode { kFragToFrag = 0, kFragToRows = 1, kRowsSilu = 2 };
-hipError_t launch_skinny_f32(int mode, const float* x, const float* w, const float* bias, float* out, int M, int N,
-                             int K, int splits, int ng, int act, hipStream_t st);
+struct SkinnyArgs {
+  const float* x[2];
+  const float* w[2];
+  const float* bias[2];
+  float* out[2];
+};
+hipError_t launch_skinny_f32(int mode, const SkinnyArgs& args, int chains, int M, int N, int K, int splits, int ng,
+                             int act, hipStream_t st);
 int skinny_splits(int K, int splits);
-// out[M, N] = act(sum of `splits` partial sums + bias); with prev the blend
-// (1 - gate) prev + gate * that (prev may equal out). N % 4 == 0.
-hipError_t launch_rows_finish(const float* part, int splits, const float* bias, float* out, int M, int N, int act,
-                              const float* prev, float gate, hipStream_t st);
+// y_c = act(sum of the `splits` partial sums [splits][M][N] of chain c +
+// bias_c) (bias may be null); out[M, N] = y_0, or with part1 non-null the
+// blend (1 - gate) y_0 + gate y_1. N % 4 == 0.
+hipError_t launch_rows_finish(const float* part0, const float* part1, int splits, const float* bias0,
+                              const float* bias1, float* out, int M, int N, int act, float gate, hipStream_t st);
 // table[(n / ng) * M + m][n % ng] = W[n] . bf16(SiLU(emb[m])) + bias[n] with
 // bf16 W [N, K] and bias [N] (may be null), N % 64 == 0, K % 32 == 0.
 // a_scratch: padded_rows(M) * K bf16 values (SiLU(emb) in bf16, stored in
