@@ -48,22 +48,24 @@ def flop_counts(dims, layout):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attention_clip32k_traffic.md")
 ATTENTION_SOURCE = os.path.join(ROOT, "joint_video_audio_amd", "csrc", "attention.hip")
+TABLE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "adaln_table_clip32k.md")
+CONDITIONING_SOURCE = os.path.join(ROOT, "joint_video_audio_amd", "csrc", "conditioning.hip")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed FETCH_SIZE / WRITE_SIZE
-    summary, or None when it covers another workload or another version of
-    the kernel source."""
+def measured_traffic(workload: str, summary: str = TRAFFIC_SUMMARY, source: str = ATTENTION_SOURCE):
+    """HBM bytes per launch of a kernel from its committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when the summary covers another workload or
+    another version of the kernel's source file."""
     import hashlib
     import re
-    if workload != "clip32k" or not os.path.exists(TRAFFIC_SUMMARY):
+    if workload != "clip32k" or not os.path.exists(summary):
         return None
-    text = open(TRAFFIC_SUMMARY).read()
-    m_sha = re.search(r"attention\.hip sha256: ([0-9a-f]{64})", text)
+    text = open(summary).read()
+    m_sha = re.search(re.escape(os.path.basename(source)) + r" sha256: ([0-9a-f]{64})", text)
     m_b = re.search(r"traffic_bytes_per_launch: ([0-9]+)", text)
     if not (m_sha and m_b):
         return None
-    sha = hashlib.sha256(open(ATTENTION_SOURCE, "rb").read()).hexdigest()
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
     return int(m_b.group(1)) if sha == m_sha.group(1) else None
 
 
@@ -151,7 +153,8 @@ def table_build(wl, seed: int, reps: int, warmup: int):
     return {"timestep_values": n, "two_time": two, "freq_dim": cond.freq_dim, "mlp_hidden": cond.hidden_dim,
             "embed_dim": E, "reps": reps, "time_embed_ms": round(te, 4), "adaln_table_ms": round(ta, 4),
             "roofline": {"kernel": "adaln_table", "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(wl.name, TABLE_TRAFFIC_SUMMARY, CONDITIONING_SOURCE),
                          "algorithmic_bytes": nbytes, "avg_launch_ms": round(ta, 4)}}
 
 
