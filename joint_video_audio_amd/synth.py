@@ -380,3 +380,55 @@ def make_conditioning(dims: ModelDims, num_blocks: int = 1, two_time: bool = Fal
     return Conditioning(freq_dim, hidden_dim, embed_dim, np.asarray(t, np.float32),
                         None if r is None else np.asarray(r, np.float32), base, endpoint,
                         0.25 if two_time else 0.0, w_proj, b_proj)
+
+
+# --------------------------------------------------------------------------
+# Model edges: latent rows and the input / output projections
+# --------------------------------------------------------------------------
+#
+# Recipe: ``numpy.random.default_rng(seed)``; draw order: video latent rows
+# [B, n_video, 96], audio latent rows [B, n_audio, 32], embedded text rows
+# [B, n_text, D] (activation dtype), then proj_in W [D, 96] and b,
+# audio_proj_in W [D, 32] and b, norm_out weight and bias, proj_out W [96, D]
+# and b, audio_proj_out W [32, D] and b. Latents N(0, 1); projection weights
+# N(0, 1 / fan_in), biases N(0, 0.02); norm_out weight 1 + N(0, 0.02), bias
+# N(0, 0.02). Everything but the text rows is fp32.
+
+@dataclasses.dataclass
+class Edges:
+    video: np.ndarray      # fp32 [B, n_video, C_v]
+    audio: np.ndarray      # fp32 [B, n_audio, C_a]
+    text: Tensor           # [B, n_text, D] activation dtype
+    w_in: np.ndarray       # fp32 [D, C_v]
+    b_in: np.ndarray       # fp32 [D]
+    w_ain: np.ndarray      # fp32 [D, C_a]
+    b_ain: np.ndarray      # fp32 [D]
+    gamma: np.ndarray      # fp32 [D]
+    beta: np.ndarray       # fp32 [D]
+    w_out: np.ndarray      # fp32 [C_v, D]
+    b_out: np.ndarray      # fp32 [C_v]
+    w_aout: np.ndarray     # fp32 [C_a, D]
+    b_aout: np.ndarray     # fp32 [C_a]
+    final_norm_eps: float = 1.0e-5
+
+
+def make_edges(dims: ModelDims, layout: Layout, batch: int = 1, seed: int = 0, video_channels: int = 96,
+               audio_channels: int = 32) -> Edges:
+    rng = np.random.default_rng(seed)
+    D = dims.hidden
+    nv, na, nt = (int(layout.video_indices.shape[0]), int(layout.audio_indices.shape[0]),
+                  int(layout.text_indices.shape[0]))
+    video = _normal(rng, (batch, nv, video_channels), 1.0)
+    audio = _normal(rng, (batch, na, audio_channels), 1.0)
+    text = _store(_normal(rng, (batch, nt, D), 1.0), dims.dtype)
+    w_in = _normal(rng, (D, video_channels), video_channels ** -0.5)
+    b_in = _normal(rng, (D,), 0.02)
+    w_ain = _normal(rng, (D, audio_channels), audio_channels ** -0.5)
+    b_ain = _normal(rng, (D,), 0.02)
+    gamma = _normal(rng, (D,), 0.02, 1.0)
+    beta = _normal(rng, (D,), 0.02)
+    w_out = _normal(rng, (video_channels, D), D ** -0.5)
+    b_out = _normal(rng, (video_channels,), 0.02)
+    w_aout = _normal(rng, (audio_channels, D), D ** -0.5)
+    b_aout = _normal(rng, (audio_channels,), 0.02)
+    return Edges(video, audio, text, w_in, b_in, w_ain, b_ain, gamma, beta, w_out, b_out, w_aout, b_aout)
