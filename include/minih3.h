@@ -243,6 +243,60 @@ int minih3_adaln_table_workspace_bytes(const minih3_config* cfg, int32_t embed_d
 int minih3_adaln_table(const minih3_config* cfg, const float* emb, int32_t embed_dim, const void* w_proj,
                        const void* b_proj, float* table, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Model edges: the packed sequence in, the velocities out ----
+ * Page "MiniMaxH3Transformer3DModel": Parameters in_channels, patch_size,
+ * audio_in_channels, final_norm_eps; the mixed-precision note (the input
+ * patch projections and the output heads are float32); `forward`
+ * (hidden_states: patchified video rows in the order of video_indices;
+ * audio_hidden_states in the order of audio_indices; the returned video and
+ * audio velocities in those orders). Where the pages leave the form open the
+ * library takes: proj_in / audio_proj_in are Linear layers with bias;
+ * text rows arrive already embedded (the text refiner is not part of this
+ * library); norm_out is a LayerNorm with weight and bias shared by the video
+ * and audio rows; proj_out / audio_proj_out are Linear layers with bias. */
+typedef struct {
+  int32_t video_channels;  /* in_channels * prod(patch_size) (24 * 1*2*2 = 96); one of 16, 32, 48, 64, 96, 128 */
+  int32_t audio_channels;  /* audio_in_channels (32); one of 16, 32, 48, 64, 96, 128 */
+  float final_norm_eps;    /* eps of norm_out (1e-5) */
+  const float* w_in;        /* proj_in weight [D, video_channels] fp32        */
+  const float* b_in;        /* proj_in bias [D]                               */
+  const float* w_audio_in;  /* audio_proj_in weight [D, audio_channels]       */
+  const float* b_audio_in;  /* audio_proj_in bias [D]                         */
+  const float* norm_w;      /* norm_out weight [D]                            */
+  const float* norm_b;      /* norm_out bias [D]                              */
+  const float* w_out;       /* proj_out weight [video_channels, D]            */
+  const float* b_out;       /* proj_out bias [video_channels] (NULL = zero)   */
+  const float* w_audio_out; /* audio_proj_out weight [audio_channels, D]      */
+  const float* b_audio_out; /* audio_proj_out bias [audio_channels] (NULL = zero) */
+} minih3_edges;
+
+/* Bytes of workspace minih3_embed_inputs / minih3_output_heads need. */
+int minih3_edges_workspace_bytes(const minih3_config* cfg, const minih3_edges* edges, int32_t seq_len, size_t* bytes);
+
+/* The packed sequence x [B, S, D] act from the model inputs:
+ * x[b, video_indices[i]] = proj_in(video[b, i]), x[b, audio_indices[j]] =
+ * audio_proj_in(audio[b, j]) (fp32 arithmetic, rounded to act),
+ * x[b, text_indices[k]] = text[b, k] (copied), and zero on padding rows.
+ * video : [B, num_video, video_channels] fp32;  audio : [B, num_audio,
+ * audio_channels] fp32;  text : [B, num_text, D] act. Rows that no index
+ * tensor addresses and that are not padding rows (only in an invalid
+ * layout) are left as they were; MINIH3_VALIDATE checks the layout first.
+ * Reads hidden and act_dtype of cfg (and the layout fields under
+ * MINIH3_VALIDATE). */
+int minih3_embed_inputs(const minih3_config* cfg, const minih3_layout* layout, const minih3_edges* edges,
+                        const float* video, const float* audio, const void* text, void* x, void* workspace,
+                        size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* The velocities from the final hidden states x [B, S, D] act:
+ * video_out[b, i] = proj_out(norm_out(x[b, video_indices[i]])) and
+ * audio_out[b, j] = audio_proj_out(norm_out(x[b, audio_indices[j]])), fp32.
+ * video_out : [B, num_video, video_channels];  audio_out : [B, num_audio,
+ * audio_channels]. norm_out is applied as W diag(w) (x - mean) / sd + (W b +
+ * bias) with the statistics of each row. */
+int minih3_output_heads(const minih3_config* cfg, const minih3_layout* layout, const minih3_edges* edges,
+                        const void* x, float* video_out, float* audio_out, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream);
+
 /* Kernel timing under MINIH3_PROFILE. Synchronises the recorded events,
  * writes for each kernel id k < n the summed milliseconds and the number of
  * launches since the last collect, then resets. Returns the number of

@@ -384,6 +384,59 @@ int time_mlps(const minih3_time_config* tc, const minih3_time_mlp* m, const floa
   return MINIH3_OK;
 }
 
+
+// ---- model edges ----
+int check_edges(const minih3_config* c, const minih3_edges* e) {
+  if (!c || !e) return MINIH3_E_ARG;
+  if (c->act_dtype != MINIH3_BF16 && c->act_dtype != MINIH3_F32) return MINIH3_E_ARG;
+  if (c->hidden < 256 || c->hidden % 256 != 0) return MINIH3_E_UNSUPPORTED;
+  for (int ch : {e->video_channels, e->audio_channels})
+    if (ch < 16 || ch > 128 || ch % 16 != 0 || ch == 80 || ch == 112) return MINIH3_E_UNSUPPORTED;
+  if (!(e->final_norm_eps >= 0.f)) return MINIH3_E_ARG;
+  if (!e->w_in || !e->b_in || !e->w_audio_in || !e->b_audio_in || !e->norm_w || !e->norm_b || !e->w_out ||
+      !e->w_audio_out)
+    return MINIH3_E_ARG;
+  return MINIH3_OK;
+}
+
+struct EdgeWorkspace {
+  int32_t *counts, *npad;
+  uint32_t* err;
+  float *wf, *s, *cv;  // folded heads: video rows first, then audio
+  size_t total;
+};
+
+EdgeWorkspace carve_edges(const minih3_config* c, const minih3_edges* e, int S, char* base) {
+  EdgeWorkspace w{};
+  const size_t C = (size_t)e->video_channels + e->audio_channels;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off += align_up(n);
+    return base ? base + o : nullptr;
+  };
+  w.counts = (int32_t*)take(4 * (size_t)S);
+  w.npad = (int32_t*)take(4);
+  w.err = (uint32_t*)take(4);
+  w.wf = (float*)take(4 * C * c->hidden);
+  w.s = (float*)take(4 * C);
+  w.cv = (float*)take(4 * C);
+  w.total = off;
+  return w;
+}
+
+// Layout validation on the device, reported after one stream synchronisation.
+int validate_layout(const minih3_config* c, const minih3_layout* L, uint32_t flags, EdgeWorkspace& w,
+                    hipStream_t st) {
+  LayoutDev ld = make_layout_dev(c, L);
+  HIPCHECK(launch_layout_validate(ld, (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0, w.counts, w.err, w.npad, nullptr,
+                                  nullptr, nullptr, st));
+  uint32_t err = 0;
+  HIPCHECK(hipMemcpyAsync(&err, w.err, 4, hipMemcpyDeviceToHost, st));
+  HIPCHECK(hipStreamSynchronize(st));
+  return status_from_err(err);
+}
+
 }  // namespace
 
 extern "C" {
@@ -619,6 +672,85 @@ int minih3_adaln_table(const minih3_config* c, const float* emb, int32_t embed_d
   return MINIH3_OK;
 }
 
+
+int minih3_edges_workspace_bytes(const minih3_config* c, const minih3_edges* e, int32_t seq_len, size_t* bytes) {
+  int s = check_edges(c, e);
+  if (s) return s;
+  if (seq_len < 1 || !bytes) return MINIH3_E_ARG;
+  *bytes = carve_edges(c, e, seq_len, nullptr).total;
+  return MINIH3_OK;
+}
+
+int minih3_embed_inputs(const minih3_config* c, const minih3_layout* L, const minih3_edges* e, const float* video,
+                        const float* audio, const void* text, void* x, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream) {
+  int s = check_edges(c, e);
+  if (s) return s;
+  s = check_layout(L, true);
+  if (s) return s;
+  if (!x || (L->num_video && !video) || (L->num_audio && !audio) || (L->num_text && !text)) return MINIH3_E_ARG;
+  EdgeWorkspace w = carve_edges(c, e, L->seq_len, (char*)workspace);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (flags & MINIH3_VALIDATE) {
+    s = validate_layout(c, L, flags, w, st);
+    if (s) return s;
+  }
+  const int B = L->batch, S = L->seq_len, D = c->hidden;
+  if (c->act_dtype == MINIH3_BF16) {
+    bf16_t* xo = (bf16_t*)x;
+    HIPCHECK(launch_edge_in<bf16_t>(video, L->num_video, e->video_channels, e->w_in, e->b_in, L->video_indices, B, S,
+                                    D, xo, st));
+    HIPCHECK(launch_edge_in<bf16_t>(audio, L->num_audio, e->audio_channels, e->w_audio_in, e->b_audio_in,
+                                    L->audio_indices, B, S, D, xo, st));
+    HIPCHECK(launch_edge_rows<bf16_t>((const bf16_t*)text, L->text_indices, L->num_text, L->token_tags, B, S, D, xo,
+                                      st));
+  } else {
+    float* xo = (float*)x;
+    HIPCHECK(launch_edge_in<float>(video, L->num_video, e->video_channels, e->w_in, e->b_in, L->video_indices, B, S,
+                                   D, xo, st));
+    HIPCHECK(launch_edge_in<float>(audio, L->num_audio, e->audio_channels, e->w_audio_in, e->b_audio_in,
+                                   L->audio_indices, B, S, D, xo, st));
+    HIPCHECK(launch_edge_rows<float>((const float*)text, L->text_indices, L->num_text, L->token_tags, B, S, D, xo,
+                                     st));
+  }
+  return MINIH3_OK;
+}
+
+int minih3_output_heads(const minih3_config* c, const minih3_layout* L, const minih3_edges* e, const void* x,
+                        float* video_out, float* audio_out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                        void* stream) {
+  int s = check_edges(c, e);
+  if (s) return s;
+  s = check_layout(L, true);
+  if (s) return s;
+  if (!x || (L->num_video && !video_out) || (L->num_audio && !audio_out)) return MINIH3_E_ARG;
+  EdgeWorkspace w = carve_edges(c, e, L->seq_len, (char*)workspace);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (flags & MINIH3_VALIDATE) {
+    s = validate_layout(c, L, flags, w, st);
+    if (s) return s;
+  }
+  const int B = L->batch, S = L->seq_len, D = c->hidden, Cv = e->video_channels, Ca = e->audio_channels;
+  float* wf_a = w.wf + (size_t)Cv * D;
+  HIPCHECK(launch_edge_fold(e->w_out, e->b_out, e->norm_w, e->norm_b, Cv, D, w.wf, w.s, w.cv, st));
+  HIPCHECK(launch_edge_fold(e->w_audio_out, e->b_audio_out, e->norm_w, e->norm_b, Ca, D, wf_a, w.s + Cv, w.cv + Cv,
+                            st));
+  const float eps = e->final_norm_eps;
+  if (c->act_dtype == MINIH3_BF16) {
+    HIPCHECK(launch_edge_out<bf16_t>((const bf16_t*)x, L->video_indices, L->num_video, B, S, D, w.wf, w.s, w.cv, Cv,
+                                     eps, video_out, st));
+    HIPCHECK(launch_edge_out<bf16_t>((const bf16_t*)x, L->audio_indices, L->num_audio, B, S, D, wf_a, w.s + Cv,
+                                     w.cv + Cv, Ca, eps, audio_out, st));
+  } else {
+    HIPCHECK(launch_edge_out<float>((const float*)x, L->video_indices, L->num_video, B, S, D, w.wf, w.s, w.cv, Cv,
+                                    eps, video_out, st));
+    HIPCHECK(launch_edge_out<float>((const float*)x, L->audio_indices, L->num_audio, B, S, D, wf_a, w.s + Cv,
+                                    w.cv + Cv, Ca, eps, audio_out, st));
+  }
+  return MINIH3_OK;
+}
 
 int minih3_profile_collect(double* total_ms, int32_t* launches, int32_t n) {
   std::lock_guard<std::mutex> lk(g_prof.mu);

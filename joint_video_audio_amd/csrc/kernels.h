@@ -127,4 +127,24 @@ hipError_t launch_rows_finish(const float* part0, const float* part1, int splits
 hipError_t launch_adaln_proj(const float* emb, const uint16_t* w, const uint16_t* bias, uint16_t* a_scratch, float* table,
                              int M, int N, int K, int ng, hipStream_t st);
 
+// ---- model edges (input projections, output heads) ----
+// x[b, idx[r]] = W h[b, r] + bias (h [B, nrows, C] fp32, W [D, C] fp32,
+// C % 16 == 0, D % 256 == 0); indices clamped into [0, S).
+template <typename T>
+hipError_t launch_edge_in(const float* h, int nrows, int C, const float* W, const float* bias, const int32_t* idx,
+                          int B, int S, int D, T* x, hipStream_t st);
+// x[b, idx[k]] = text[b, k] for k < ntext, then x[b, r] = 0 where tags[r] == -1.
+template <typename T>
+hipError_t launch_edge_rows(const T* text, const int32_t* idx, int ntext, const int32_t* tags, int B, int S, int D,
+                            T* x, hipStream_t st);
+// W' = W diag(gamma) [C, D], s = W' 1, cv = W beta + b (b may be null).
+hipError_t launch_edge_fold(const float* W, const float* b, const float* gamma, const float* beta, int C, int D,
+                            float* Wf, float* s, float* cv, hipStream_t st);
+// y[b, r] = (W' x_r - mu_r s) / sigma_r + cv, x_r = x[b, idx[r]], for the
+// LayerNorm statistics of x_r (eps inside the root); C in {16, 32, 48, 64,
+// 96, 128}, D % 64 == 0; y [B, nrows, C] fp32.
+template <typename T>
+hipError_t launch_edge_out(const T* x, const int32_t* idx, int nrows, int B, int S, int D, const float* Wf,
+                           const float* s, const float* cv, int C, float eps, float* y, hipStream_t st);
+
 }  // namespace minih3

@@ -49,3 +49,12 @@ def time_config_for(cond, max_period: float = 1.0e4) -> m.TimeConfig:
 
 def time_mlp_for(te, device="cuda") -> m.DeviceTimeMLP:
     return m.DeviceTimeMLP(f32(te.w1, device), f32(te.b1, device), f32(te.w2, device), f32(te.b2, device))
+
+
+def edges_for(e, device="cuda") -> m.DeviceEdges:
+    """Device copies of synthetic edge weights (synth.Edges)."""
+    return m.DeviceEdges(e.w_in.shape[1], e.w_ain.shape[1], e.final_norm_eps,
+                         **{n: f32(getattr(e, a), device) for n, a in (
+                             ("w_in", "w_in"), ("b_in", "b_in"), ("w_audio_in", "w_ain"), ("b_audio_in", "b_ain"),
+                             ("norm_w", "gamma"), ("norm_b", "beta"), ("w_out", "w_out"), ("b_out", "b_out"),
+                             ("w_audio_out", "w_aout"), ("b_audio_out", "b_aout"))})

@@ -66,6 +66,13 @@ class _TimeMLP(ctypes.Structure):
     _fields_ = [("w1", _P), ("b1", _P), ("w2", _P), ("b2", _P)]
 
 
+class _Edges(ctypes.Structure):
+    _fields_ = [("video_channels", ctypes.c_int32), ("audio_channels", ctypes.c_int32),
+                ("final_norm_eps", ctypes.c_float)] + [(n, _P) for n in (
+                    "w_in", "b_in", "w_audio_in", "b_audio_in", "norm_w", "norm_b", "w_out", "b_out", "w_audio_out",
+                    "b_audio_out")]
+
+
 class Minih3Error(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
@@ -115,6 +122,14 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(ctypes.c_size_t)]
         L.minih3_adaln_table.argtypes = [ctypes.POINTER(Config), _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t,
                                          _P]
+        L.minih3_edges_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Edges), ctypes.c_int32,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_embed_inputs.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), ctypes.POINTER(_Edges), _P,
+                                          _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_uint32, _P]
+        L.minih3_output_heads.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), ctypes.POINTER(_Edges), _P,
+                                          _P, _P, _P, ctypes.c_size_t, ctypes.c_uint32, _P]
+        for fn in ("minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads"):
+            getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
                    "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
                    "minih3_profile_collect", "minih3_time_embed_workspace_bytes", "minih3_time_embed",
@@ -128,7 +143,7 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
             "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
             "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
-            "minih3_adaln_table")
+            "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads")
 
 
 def status_string(s: int) -> str:
@@ -414,6 +429,79 @@ def adaln_table(cfg: Config, emb: torch.Tensor, w_proj: torch.Tensor, b_proj: Op
     _check(lib().minih3_adaln_table(ctypes.byref(cfg), _ptr(emb), E, _ptr(w_proj), _ptr(b_proj), _ptr(out),
                                     _ptr(workspace), workspace.numel(), _stream()), "adaln_table")
     return out
+
+
+class DeviceEdges:
+    """fp32 device weights of the model edges (proj_in, audio_proj_in, norm_out,
+    proj_out, audio_proj_out)."""
+
+    NAMES = ("w_in", "b_in", "w_audio_in", "b_audio_in", "norm_w", "norm_b", "w_out", "b_out", "w_audio_out",
+             "b_audio_out")
+
+    def __init__(self, video_channels: int, audio_channels: int, final_norm_eps: float, **tensors):
+        self.video_channels, self.audio_channels = int(video_channels), int(audio_channels)
+        self.final_norm_eps = float(final_norm_eps)
+        self.t = {n: tensors.get(n) for n in self.NAMES}
+
+    def check(self, cfg: Config):
+        D, Cv, Ca = cfg.hidden, self.video_channels, self.audio_channels
+        shapes = dict(w_in=D * Cv, b_in=D, w_audio_in=D * Ca, b_audio_in=D, norm_w=D, norm_b=D, w_out=Cv * D,
+                      b_out=Cv, w_audio_out=Ca * D, b_audio_out=Ca)
+        for n, k in shapes.items():
+            if self.t[n] is None and n in ("b_out", "b_audio_out"):
+                continue
+            _req(self.t[n], torch.float32, n, k)
+
+    def c(self) -> _Edges:
+        return _Edges(self.video_channels, self.audio_channels, self.final_norm_eps,
+                      *(_ptr(self.t[n]) for n in self.NAMES))
+
+
+def edges_workspace_bytes(cfg: Config, edges: DeviceEdges, seq_len: int) -> int:
+    nb = ctypes.c_size_t(0)
+    ce = edges.c()
+    _check(lib().minih3_edges_workspace_bytes(ctypes.byref(cfg), ctypes.byref(ce), seq_len, ctypes.byref(nb)),
+           "edges_workspace_bytes")
+    return int(nb.value)
+
+
+def embed_inputs(cfg: Config, layout: DeviceLayout, edges: DeviceEdges, video: torch.Tensor, audio: torch.Tensor,
+                 text: torch.Tensor, x: Optional[torch.Tensor] = None, flags: int = 0,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """video [B, n_video, Cv] fp32, audio [B, n_audio, Ca] fp32, text [B, n_text, D] act -> x [B, S, D] act."""
+    dt = act_torch_dtype(cfg)
+    B, S, D = layout.batch, layout.seq_len, cfg.hidden
+    edges.check(cfg)
+    _req(video, torch.float32, "video", B * layout.video_indices.numel() * edges.video_channels)
+    _req(audio, torch.float32, "audio", B * layout.audio_indices.numel() * edges.audio_channels)
+    _req(text, dt, "text", B * layout.text_indices.numel() * D)
+    if x is None:
+        x = torch.empty(B, S, D, dtype=dt, device=video.device)
+    _req(x, dt, "x", B * S * D)
+    if workspace is None:
+        workspace = alloc_workspace(edges_workspace_bytes(cfg, edges, S), video.device)
+    L, ce = layout.c(), edges.c()
+    _check(lib().minih3_embed_inputs(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(ce), _ptr(video), _ptr(audio),
+                                     _ptr(text), _ptr(x), _ptr(workspace), workspace.numel(), flags, _stream()),
+           "embed_inputs")
+    return x
+
+
+def output_heads(cfg: Config, layout: DeviceLayout, edges: DeviceEdges, x: torch.Tensor, flags: int = 0,
+                 workspace: Optional[torch.Tensor] = None):
+    """x [B, S, D] act -> (video velocity [B, n_video, Cv], audio velocity [B, n_audio, Ca]) fp32."""
+    dt = act_torch_dtype(cfg)
+    B, S, D = layout.batch, layout.seq_len, cfg.hidden
+    edges.check(cfg)
+    _req(x, dt, "x", B * S * D)
+    v = torch.empty(B, layout.video_indices.numel(), edges.video_channels, dtype=torch.float32, device=x.device)
+    a = torch.empty(B, layout.audio_indices.numel(), edges.audio_channels, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(edges_workspace_bytes(cfg, edges, S), x.device)
+    L, ce = layout.c(), edges.c()
+    _check(lib().minih3_output_heads(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(ce), _ptr(x), _ptr(v), _ptr(a),
+                                     _ptr(workspace), workspace.numel(), flags, _stream()), "output_heads")
+    return v, a
 
 
 def profile_collect() -> dict:

@@ -88,3 +88,27 @@ def test_conditioning_host_side_checks():
     assert lib.minih3_adaln_table(ctypes.byref(cfg), p, 2688, p, None, p, p, 10, None) == m.E_WORKSPACE
     assert lib.minih3_adaln_table(ctypes.byref(cfg), p, 2680, p, None, p, p, 1 << 30, None) == m.E_UNSUPPORTED
     assert lib.minih3_adaln_table(ctypes.byref(cfg), None, 2688, p, None, p, p, 1 << 30, None) == m.E_ARG
+
+
+def test_edges_host_side_checks():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libminih3.so not built")
+    lib = m.lib()
+    cfg = dv.config_for(synth.workload_dims("clip32k"))
+    p = ctypes.c_void_p(16)
+    e = m._Edges(96, 32, 1e-5, *([p] * 10))
+    n = ctypes.c_size_t(0)
+    assert lib.minih3_edges_workspace_bytes(ctypes.byref(cfg), ctypes.byref(e), 32768, ctypes.byref(n)) == m.OK
+    # validation scratch plus the folded heads (128 x 5376 fp32)
+    assert n.value >= 32768 * 4 + 128 * 5376 * 4
+    bad = m._Edges(90, 32, 1e-5, *([p] * 10))
+    assert lib.minih3_edges_workspace_bytes(ctypes.byref(cfg), ctypes.byref(bad), 32768, ctypes.byref(n)) == \
+        m.E_UNSUPPORTED
+    L = m._Layout(1, 8, p, p, p, p, 4, p, 2, p, 2)
+    assert lib.minih3_embed_inputs(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(e), p, p, p, p, p, 10, 0,
+                                   None) == m.E_WORKSPACE
+    assert lib.minih3_output_heads(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(e), None, p, p, p, 1 << 30, 0,
+                                   None) == m.E_ARG
+    no_w = m._Edges(96, 32, 1e-5, None, *([p] * 9))
+    assert lib.minih3_output_heads(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(no_w), p, p, p, p, 1 << 30, 0,
+                                   None) == m.E_ARG
