@@ -17,7 +17,8 @@ time from HIP events recorded on the launch stream inside the timed region.
 cpu_baseline times the fp64 oracle on a bounded sample of the workload.
 table_build times, apart from the step, the build of one block's AdaLN
 table from the workload's timestep values (time embeddings, then the bf16
-AdaLN projection), with the projection's HBM roofline.
+AdaLN projection), with the projection's HBM roofline; edges times the
+input projections into the packed sequence and the output heads (fp32).
 """
 from __future__ import annotations
 
@@ -158,6 +159,54 @@ def table_build(wl, seed: int, reps: int, warmup: int):
                          "algorithmic_bytes": nbytes, "avg_launch_ms": round(ta, 4)}}
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def edges(wl, seed: int, reps: int, warmup: int):
+    """Time the model edges on the workload's layout: the input projections
+    with the scatter into the packed sequence (minih3_embed_inputs) and
+    norm_out with the output heads on the gathered rows (minih3_output_heads).
+    Both are fp32 contractions; HIP events bracket each call."""
+    import torch
+    from joint_video_audio_amd import device as dv
+    from joint_video_audio_amd import minih3 as m
+    from joint_video_audio_amd import synth
+    L = wl.layout
+    e = synth.make_edges(wl.dims, L, seed=seed)
+    cfg = dv.config_for(wl.dims)
+    lay = dv.layout_for(wl, batch=1)
+    de = dv.edges_for(e)
+    video, audio, text = dv.f32(e.video), dv.f32(e.audio), dv.to_device(e.text)
+    x = torch.empty(1, L.seq_len, wl.dims.hidden, dtype=m.act_torch_dtype(cfg), device="cuda")
+    ws = m.alloc_workspace(m.edges_workspace_bytes(cfg, de, L.seq_len))
+    for _ in range(warmup):
+        m.embed_inputs(cfg, lay, de, video, audio, text, x=x, workspace=ws)
+        m.output_heads(cfg, lay, de, x, workspace=ws)
+    st = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1, e2 in evs:
+        e0.record(st)
+        m.embed_inputs(cfg, lay, de, video, audio, text, x=x, workspace=ws)
+        e1.record(st)
+        m.output_heads(cfg, lay, de, x, workspace=ws)
+        e2.record(st)
+    torch.cuda.synchronize()
+    t_in = sum(a.elapsed_time(b) for a, b, _ in evs) / reps
+    t_out = sum(b.elapsed_time(c) for _, b, c in evs) / reps
+    D, Cv, Ca = wl.dims.hidden, e.w_in.shape[1], e.w_ain.shape[1]
+    nv, na = len(L.video_indices), len(L.audio_indices)
+    flop = 2.0 * (nv * Cv + na * Ca) * D  # each direction
+    tf_in, tf_out = flop / (t_in / 1e3) / 1e12, flop / (t_out / 1e3) / 1e12
+    return {"video_rows": nv, "audio_rows": na, "video_channels": Cv, "audio_channels": Ca, "reps": reps,
+            "embed_inputs_ms": round(t_in, 4), "output_heads_ms": round(t_out, 4),
+            "roofline": {"kernel": "output_heads", "bound": "mfma", "achieved": round(tf_out, 1),
+                         "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_out / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "avg_launch_ms": round(t_out, 4)},
+            "embed_inputs_tflops": round(tf_in, 1), "embed_inputs_frac": round(tf_in / FP32_MFMA_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +217,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table-build", action="store_true")
+    ap.add_argument("--no-edges", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -261,6 +311,8 @@ def main():
     }
     if not a.no_table_build:
         res["table_build"] = table_build(wl, a.seed, reps=50, warmup=5)
+    if not a.no_edges:
+        res["edges"] = edges(wl, a.seed, reps=20, warmup=3)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)

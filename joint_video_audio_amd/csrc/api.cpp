@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "../../include/minih3.h"
@@ -737,18 +738,37 @@ int minih3_output_heads(const minih3_config* c, const minih3_layout* L, const mi
   HIPCHECK(launch_edge_fold(e->w_out, e->b_out, e->norm_w, e->norm_b, Cv, D, w.wf, w.s, w.cv, st));
   HIPCHECK(launch_edge_fold(e->w_audio_out, e->b_audio_out, e->norm_w, e->norm_b, Ca, D, wf_a, w.s + Cv, w.cv + Cv,
                             st));
-  const float eps = e->final_norm_eps;
-  if (c->act_dtype == MINIH3_BF16) {
-    HIPCHECK(launch_edge_out<bf16_t>((const bf16_t*)x, L->video_indices, L->num_video, B, S, D, w.wf, w.s, w.cv, Cv,
-                                     eps, video_out, st));
-    HIPCHECK(launch_edge_out<bf16_t>((const bf16_t*)x, L->audio_indices, L->num_audio, B, S, D, wf_a, w.s + Cv,
-                                     w.cv + Cv, Ca, eps, audio_out, st));
-  } else {
-    HIPCHECK(launch_edge_out<float>((const float*)x, L->video_indices, L->num_video, B, S, D, w.wf, w.s, w.cv, Cv,
-                                    eps, video_out, st));
-    HIPCHECK(launch_edge_out<float>((const float*)x, L->audio_indices, L->num_audio, B, S, D, wf_a, w.s + Cv,
-                                    w.cv + Cv, Ca, eps, audio_out, st));
+  // the wider head first (the kernel sizes its LDS ring by head 0)
+  const int wide = Ca > Cv ? 1 : 0;
+  EdgeHeads hd{};
+  const int32_t* idxs[2] = {L->video_indices, L->audio_indices};
+  const int nr[2] = {L->num_video, L->num_audio}, Cs[2] = {Cv, Ca};
+  float* Wfs[2] = {w.wf, wf_a};
+  float* outs[2] = {video_out, audio_out};
+  for (int k = 0; k < 2; ++k) {
+    const int h = wide ? 1 - k : k;
+    hd.idx[k] = idxs[h];
+    hd.nrows[k] = nr[h];
+    hd.C[k] = Cs[h];
+    hd.Wf[k] = Wfs[h];
+    hd.s[k] = w.s + (h ? Cv : 0);
+    hd.cv[k] = w.cv + (h ? Cv : 0);
+    hd.y[k] = outs[h];
   }
+  if (hd.nrows[0] == 0) {  // only the narrower head has rows: run it alone
+    std::swap(hd.idx[0], hd.idx[1]);
+    std::swap(hd.nrows[0], hd.nrows[1]);
+    std::swap(hd.C[0], hd.C[1]);
+    std::swap(hd.Wf[0], hd.Wf[1]);
+    std::swap(hd.s[0], hd.s[1]);
+    std::swap(hd.cv[0], hd.cv[1]);
+    std::swap(hd.y[0], hd.y[1]);
+  }
+  const float eps = e->final_norm_eps;
+  if (c->act_dtype == MINIH3_BF16)
+    HIPCHECK(launch_edge_out<bf16_t>((const bf16_t*)x, hd, B, S, D, eps, st));
+  else
+    HIPCHECK(launch_edge_out<float>((const float*)x, hd, B, S, D, eps, st));
   return MINIH3_OK;
 }
 

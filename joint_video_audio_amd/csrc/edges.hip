@@ -17,9 +17,11 @@
 //    zeroed.
 //  * k_edge_fold: norm_out folded into the head: W' = W diag(gamma),
 //    s = W' 1, c = W beta + b, so head(LN(x)) = (W' x - mu s) / sigma + c.
-//  * k_edge_out: the head on gathered rows. A wave owns 16 rows and all
-//    output channels over the full hidden width; the four waves of a
-//    workgroup share 64-column chunks of W' in a double-buffered LDS ring.
+//  * k_edge_out: both heads on gathered rows in one launch. A wave owns 16
+//    rows and all output channels of its head over the full hidden width;
+//    the four waves of a workgroup share 64-column chunks of W' in a
+//    double-buffered LDS ring, with the next chunk's weights and activations
+//    in flight while one is used.
 //    Row sums of x - x_0 (x_0 the row's first value) and of its square ride
 //    along, so the LayerNorm statistics come from the same pass.
 #include "common.h"
@@ -175,20 +177,25 @@ __global__ void __launch_bounds__(256) k_edge_fold(const float* __restrict__ W, 
 }
 
 // y[b, r, :] = (W' x_r - mu_r s) / sigma_r + cv with x_r = x[b, idx[r]],
-// mu_r, sigma_r its LayerNorm mean and deviation (eps inside), for r < nrows.
-// NB = C / 16 output blocks; D % 64 == 0. Grid (ceil(nrows / 64), B).
+// mu_r, sigma_r its LayerNorm mean and deviation (eps inside), for r < nrows,
+// for two heads in one launch: workgroups [0, blocks0) serve head 0, the
+// rest head 1, so the small audio head runs beside the video one. NB = the
+// larger head's C / 16; a head with fewer output blocks skips the others.
+// D % 64 == 0. Grid (blocks0 + blocks1, B), blocks_h = ceil(nrows_h / 64).
 template <typename T, int NB>
-__global__ void __launch_bounds__(256) k_edge_out(const T* __restrict__ x, const int32_t* __restrict__ idx, int nrows,
-                                                  int S, int D, const float* __restrict__ Wf,
-                                                  const float* __restrict__ s, const float* __restrict__ cv, float eps,
-                                                  float* __restrict__ y) {
-  constexpr int C = 16 * NB, KC = 64, kLd = KC + 4;  // a 64-column chunk of W', rows padded by 16 bytes
-  constexpr int kLoads = C * KC / 4 / 256;            // float4 loads per thread per chunk
-  static_assert(C * KC / 4 % 256 == 0, "chunk split");
-  __shared__ __attribute__((aligned(16))) float wl[2][C][kLd];
+__global__ void __launch_bounds__(256) k_edge_out(const T* __restrict__ x, EdgeHeads hd, int blocks0, int S, int D,
+                                                  float eps) {
+  constexpr int Cmax = 16 * NB, KC = 64, kLd = KC + 4;  // 64-column chunks of W', rows padded by 16 bytes
+  constexpr int kLoads = (Cmax * KC / 4 + 255) / 256;  // float4 loads per thread per chunk (at most)
+  __shared__ __attribute__((aligned(16))) float wl[2][Cmax][kLd];
+  const int h = blockIdx.x < blocks0 ? 0 : 1;
+  const int blk = h ? blockIdx.x - blocks0 : blockIdx.x;
+  const int32_t* __restrict__ idx = hd.idx[h];
+  const int nrows = hd.nrows[h], C = hd.C[h], nbh = C / 16;
+  const float* __restrict__ Wf = hd.Wf[h];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
-  const int m = blockIdx.x * 64 + 16 * wid + r16;  // the lane's row
+  const int m = blk * 64 + 16 * wid + r16;  // the lane's row
   const bool live = m < nrows;
   const int row = clamp_row(idx[live ? m : nrows - 1], S);
   const T* xr = x + ((long)blockIdx.y * S + row) * D;
@@ -204,50 +211,70 @@ __global__ void __launch_bounds__(256) k_edge_out(const T* __restrict__ x, const
   for (int i = 0; i < NB; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float s1 = 0.f, s2 = 0.f;
   floatx4 stage[kLoads];
+  const int nld = C * KC / 4;  // float4 pieces of a chunk of this head
   auto fetch = [&](int kc) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
-      const int e = threadIdx.x + 256 * l;  // float4 index within the chunk
-      const int c = e / (KC / 4), k4 = e % (KC / 4);
-      stage[l] = *reinterpret_cast<const floatx4*>(Wf + (long)c * D + kc * KC + 4 * k4);
+      const int e = threadIdx.x + 256 * l;
+      if (e < nld) {
+        const int c = e / (KC / 4), k4 = e % (KC / 4);
+        stage[l] = *reinterpret_cast<const floatx4*>(Wf + (long)c * D + kc * KC + 4 * k4);
+      }
     }
   };
   auto put = [&](int buf) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
       const int e = threadIdx.x + 256 * l;
-      const int c = e / (KC / 4), k4 = e % (KC / 4);
-      *reinterpret_cast<floatx4*>(&wl[buf][c][4 * k4]) = stage[l];
+      if (e < nld) {
+        const int c = e / (KC / 4), k4 = e % (KC / 4);
+        *reinterpret_cast<floatx4*>(&wl[buf][c][4 * k4]) = stage[l];
+      }
     }
+  };
+  // The lane's 16 activations of a chunk: columns 32 st + 8q .. +7, st = 0, 1.
+  float xa[2][8];
+  auto fetch_x = [&](int kc) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) load8<T>(xr + kc * KC + 32 * st + 8 * q, xa[st]);
   };
   const int nk = D / KC;
   fetch(0);
+  fetch_x(0);
   put(0);
   __syncthreads();
   for (int kc = 0; kc < nk; ++kc) {
     const int buf = kc & 1;
-    if (kc + 1 < nk) fetch(kc + 1);
+    float xv[2][8];
 #pragma unroll
-    for (int st = 0; st < KC / 32; ++st) {
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xv[st][t] = xa[st][t];
+    if (kc + 1 < nk) {  // next chunk's weights and activations in flight during this one
+      fetch(kc + 1);
+      fetch_x(kc + 1);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
       // Lane (r16, q) holds x_r[32 st + 8q + t] - x_0 and W'[16 i + r16][same
       // column]; MFMA t contracts k slot q of both (eight MFMAs a block).
-      float xv[8];
-      load8<T>(xr + kc * KC + 32 * st + 8 * q, xv);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        xv[t] = live ? xv[t] - x0 : 0.f;
-        s1 += xv[t];
-        s2 += xv[t] * xv[t];
+        xv[st][t] = live ? xv[st][t] - x0 : 0.f;
+        s1 += xv[st][t];
+        s2 += xv[st][t] * xv[st][t];
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
+        if (i >= nbh) break;  // uniform: the head's output blocks
         const float* wrow = &wl[buf][16 * i + r16][32 * st + 8 * q];
         const floatx4 wa = *reinterpret_cast<const floatx4*>(wrow);
         const floatx4 wb = *reinterpret_cast<const floatx4*>(wrow + 4);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t], xv[t], acc[i], 0, 0, 0);
+        for (int t = 0; t < 4; ++t) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t], xv[st][t], acc[i], 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(wb[t], xv[4 + t], acc[i], 0, 0, 0);
+        for (int t = 0; t < 4; ++t)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(wb[t], xv[st][4 + t], acc[i], 0, 0, 0);
       }
     }
     if (kc + 1 < nk) put(buf ^ 1);
@@ -264,12 +291,13 @@ __global__ void __launch_bounds__(256) k_edge_out(const T* __restrict__ x, const
   const float rs = rsqrtf(var + eps);
   if (!live) return;
   // Lane (r16, q) holds output channels 16 i + 4q .. +3 of its row.
-  float* yr = y + ((long)blockIdx.y * nrows + m) * C;
+  float* yr = hd.y[h] + ((long)blockIdx.y * nrows + m) * C;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
+    if (i >= nbh) break;
     const int c = 16 * i + 4 * q;
-    const floatx4 sv = *reinterpret_cast<const floatx4*>(s + c);
-    const floatx4 cvv = *reinterpret_cast<const floatx4*>(cv + c);
+    const floatx4 sv = *reinterpret_cast<const floatx4*>(hd.s[h] + c);
+    const floatx4 cvv = *reinterpret_cast<const floatx4*>(hd.cv[h] + c);
     floatx4 o;
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t] = (acc[i][t] - mu * sv[t]) * rs + cvv[t];
@@ -308,25 +336,20 @@ hipError_t launch_edge_fold(const float* W, const float* b, const float* gamma, 
   return hipGetLastError();
 }
 
-template <typename T, int NB>
-static void edge_out_nb(dim3 g, const T* x, const int32_t* idx, int nrows, int S, int D, const float* Wf,
-                        const float* s, const float* cv, float eps, float* y, hipStream_t st) {
-  k_edge_out<T, NB><<<g, 256, 0, st>>>(x, idx, nrows, S, D, Wf, s, cv, eps, y);
-}
-
 template <typename T>
-hipError_t launch_edge_out(const T* x, const int32_t* idx, int nrows, int B, int S, int D, const float* Wf,
-                           const float* s, const float* cv, int C, float eps, float* y, hipStream_t st) {
-  if (nrows <= 0) return hipSuccess;
+hipError_t launch_edge_out(const T* x, const EdgeHeads& hd, int B, int S, int D, float eps, hipStream_t st) {
   if (D % 64 != 0) return hipErrorInvalidValue;
-  dim3 g((unsigned)((nrows + 63) / 64), (unsigned)B);
-  switch (C) {
-    case 16: edge_out_nb<T, 1>(g, x, idx, nrows, S, D, Wf, s, cv, eps, y, st); break;
-    case 32: edge_out_nb<T, 2>(g, x, idx, nrows, S, D, Wf, s, cv, eps, y, st); break;
-    case 48: edge_out_nb<T, 3>(g, x, idx, nrows, S, D, Wf, s, cv, eps, y, st); break;
-    case 64: edge_out_nb<T, 4>(g, x, idx, nrows, S, D, Wf, s, cv, eps, y, st); break;
-    case 96: edge_out_nb<T, 6>(g, x, idx, nrows, S, D, Wf, s, cv, eps, y, st); break;
-    case 128: edge_out_nb<T, 8>(g, x, idx, nrows, S, D, Wf, s, cv, eps, y, st); break;
+  const int b0 = (hd.nrows[0] + 63) / 64, b1 = (hd.nrows[1] + 63) / 64;
+  if (b0 + b1 == 0) return hipSuccess;
+  if (hd.nrows[1] > 0 && hd.C[1] > hd.C[0]) return hipErrorInvalidValue;  // head 0 is the wider one
+  dim3 g((unsigned)(b0 + b1), (unsigned)B);
+  switch (hd.C[0]) {
+    case 16: k_edge_out<T, 1><<<g, 256, 0, st>>>(x, hd, b0, S, D, eps); break;
+    case 32: k_edge_out<T, 2><<<g, 256, 0, st>>>(x, hd, b0, S, D, eps); break;
+    case 48: k_edge_out<T, 3><<<g, 256, 0, st>>>(x, hd, b0, S, D, eps); break;
+    case 64: k_edge_out<T, 4><<<g, 256, 0, st>>>(x, hd, b0, S, D, eps); break;
+    case 96: k_edge_out<T, 6><<<g, 256, 0, st>>>(x, hd, b0, S, D, eps); break;
+    case 128: k_edge_out<T, 8><<<g, 256, 0, st>>>(x, hd, b0, S, D, eps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -340,9 +363,7 @@ template hipError_t launch_edge_rows<bf16_t>(const bf16_t*, const int32_t*, int,
                                              bf16_t*, hipStream_t);
 template hipError_t launch_edge_rows<float>(const float*, const int32_t*, int, const int32_t*, int, int, int, float*,
                                             hipStream_t);
-template hipError_t launch_edge_out<bf16_t>(const bf16_t*, const int32_t*, int, int, int, int, const float*,
-                                            const float*, const float*, int, float, float*, hipStream_t);
-template hipError_t launch_edge_out<float>(const float*, const int32_t*, int, int, int, int, const float*,
-                                           const float*, const float*, int, float, float*, hipStream_t);
+template hipError_t launch_edge_out<bf16_t>(const bf16_t*, const EdgeHeads&, int, int, int, float, hipStream_t);
+template hipError_t launch_edge_out<float>(const float*, const EdgeHeads&, int, int, int, float, hipStream_t);
 
 }  // namespace minih3

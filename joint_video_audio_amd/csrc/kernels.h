@@ -140,11 +140,19 @@ hipError_t launch_edge_rows(const T* text, const int32_t* idx, int ntext, const 
 // W' = W diag(gamma) [C, D], s = W' 1, cv = W beta + b (b may be null).
 hipError_t launch_edge_fold(const float* W, const float* b, const float* gamma, const float* beta, int C, int D,
                             float* Wf, float* s, float* cv, hipStream_t st);
-// y[b, r] = (W' x_r - mu_r s) / sigma_r + cv, x_r = x[b, idx[r]], for the
-// LayerNorm statistics of x_r (eps inside the root); C in {16, 32, 48, 64,
-// 96, 128}, D % 64 == 0; y [B, nrows, C] fp32.
+// Two output heads in one launch: for head h, y_h[b, r] = (W'_h x_r - mu_r
+// s_h) / sigma_r + cv_h, x_r = x[b, idx_h[r]], with the LayerNorm statistics
+// of x_r (eps inside the root); C_h in {16, 32, 48, 64, 96, 128} with C_1 <=
+// C_0 (head 1 may have no rows), D % 64 == 0; y_h [B, nrows_h, C_h] fp32.
+struct EdgeHeads {
+  const int32_t* idx[2];
+  int nrows[2], C[2];
+  const float* Wf[2];
+  const float* s[2];
+  const float* cv[2];
+  float* y[2];
+};
 template <typename T>
-hipError_t launch_edge_out(const T* x, const int32_t* idx, int nrows, int B, int S, int D, const float* Wf,
-                           const float* s, const float* cv, int C, float eps, float* y, hipStream_t st);
+hipError_t launch_edge_out(const T* x, const EdgeHeads& heads, int B, int S, int D, float eps, hipStream_t st);
 
 }  // namespace minih3
