@@ -1,0 +1,85 @@
+"""CPU oracle of the rotated W8A8 INT8 linear layer (TEST INFRASTRUCTURE
+ONLY).
+
+Only tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this module. It shares no code with the HIP path.
+
+Source: page "HyperFlow H3 Flash Brings MiniMax H3 Video to One GPU", How it
+got smaller and faster: rotated W8A8 INT8 quantization of 180 linear layers
+(8-bit integer weights and activations). The page names the technique, not
+its form. Readings:
+  a. rotation: the block-diagonal normalised Hadamard transform over the
+     input dimension in blocks of 128, applied to the activations and to the
+     weight rows alike, so that (x H)(W H)^T = x W^T (H H^T = I);
+  b. quantization: symmetric int8 per row (per token for activations, per
+     output channel for weights): amax = max |v|, code = rint(v * (127 /
+     amax)) in [-127, 127], scale = amax / 127; an all-zero row has codes 0
+     and scale 0;
+  c. the product: exact int32 accumulation of the codes, then
+     y = acc * scale_x * scale_w.
+The codes are integers decided by floating point, so the rotation and the
+quantization are computed in float32, in the order stated at each function
+(the GPU path takes the same decisions in the same precision); the product
+is exact in integers and its dequantization is evaluated in float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128
+# 1 / sqrt(128) rounded to float32
+INV_SQRT_BLOCK = np.float32(1.0 / np.sqrt(128.0))
+
+
+def fwht_blocks_f32(x) -> np.ndarray:
+    """Normalised Hadamard transform of every 128-wide block of the last axis
+    (reading a), in float32: butterfly stages h = 1, 2, 4, ..., 64, each
+    mapping the pair (i, i + h) (bit h of i clear) to (x_i + x_{i+h},
+    x_i - x_{i+h}), then one multiplication by 1/sqrt(128)."""
+    v = np.array(x, dtype=np.float32, copy=True)
+    K = v.shape[-1]
+    assert K % BLOCK == 0
+    lead = v.shape[:-1]
+    v = v.reshape(-1, K // BLOCK, BLOCK)
+    h = 1
+    while h < BLOCK:
+        w = v.reshape(v.shape[0], v.shape[1], BLOCK // (2 * h), 2, h)
+        a = w[:, :, :, 0, :].copy()
+        b = w[:, :, :, 1, :].copy()
+        w[:, :, :, 0, :] = a + b
+        w[:, :, :, 1, :] = a - b
+        h *= 2
+    v = v * INV_SQRT_BLOCK
+    return v.reshape(*lead, K)
+
+
+def quantize_rows_f32(v):
+    """Symmetric per-row int8 quantization (reading b) of float32 rows:
+    returns (codes int8, scale float32)."""
+    v = np.asarray(v, np.float32)
+    amax = np.abs(v).max(axis=-1)
+    safe = np.where(amax > 0, amax, np.float32(1.0)).astype(np.float32)
+    inv = (np.float32(127.0) / safe).astype(np.float32)
+    q = np.rint(v * inv[..., None]).astype(np.float32)
+    q = np.clip(q, -127, 127)
+    q = np.where(amax[..., None] > 0, q, 0).astype(np.int8)
+    scale = np.where(amax > 0, amax / np.float32(127.0), np.float32(0.0)).astype(np.float32)
+    return q, scale
+
+
+def rotate_quantize(x):
+    """Rotation then quantization of rows (activations or weight rows)."""
+    return quantize_rows_f32(fwht_blocks_f32(np.asarray(x, np.float32)))
+
+
+def int_matmul(qa, qw) -> np.ndarray:
+    """Exact integer product qa [M, K] . qw [N, K]^T (reading c)."""
+    return np.asarray(qa, np.int64) @ np.asarray(qw, np.int64).T
+
+
+def linear_w8a8(x, w) -> np.ndarray:
+    """y = x W^T through the rotated W8A8 path, dequantized in float64."""
+    qx, sx = rotate_quantize(x)
+    qw, sw = rotate_quantize(w)
+    acc = int_matmul(qx, qw).astype(np.float64)
+    return acc * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]

@@ -1,0 +1,99 @@
+"""Pins of the rotated W8A8 oracle against the Hadamard matrix of a library,
+orthogonality, exact integer arithmetic, the quantization error bound and
+hand-worked values (CPU only).
+
+A wrong butterfly, a missing normalisation, a rotation applied to one
+operand only, a wrong rounding or clamp, or a scale from the wrong axis each
+fail at least one of these.
+"""
+import itertools
+
+import numpy as np
+from scipy.linalg import hadamard
+
+from oracle import w8a8 as ow
+
+
+def test_fwht_equals_scipy_hadamard_blockwise():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 384)).astype(np.float32)
+    H = hadamard(128).astype(np.float64) / np.sqrt(128.0)
+    ref = np.concatenate([x[:, 128 * b:128 * (b + 1)].astype(np.float64) @ H for b in range(3)], axis=1)
+    got = ow.fwht_blocks_f32(x).astype(np.float64)
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_fwht_of_unit_vectors_is_a_signed_column_exactly():
+    # e_k maps to column k of H / sqrt(128): every entry is +-1/sqrt(128) in float32
+    for k in (0, 1, 77, 127):
+        e = np.zeros((1, 128), np.float32)
+        e[0, k] = 1.0
+        got = ow.fwht_blocks_f32(e)[0]
+        col = hadamard(128)[:, k].astype(np.float32) * ow.INV_SQRT_BLOCK
+        assert np.array_equal(got, col)
+
+
+def test_fwht_is_orthogonal_and_an_involution():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 256)).astype(np.float32)
+    y = ow.fwht_blocks_f32(x)
+    # Parseval per 128-block, and H H = I
+    for b in range(2):
+        sl = slice(128 * b, 128 * (b + 1))
+        assert np.allclose((y[:, sl].astype(np.float64) ** 2).sum(1), (x[:, sl].astype(np.float64) ** 2).sum(1),
+                           rtol=1e-5)
+    assert np.abs(ow.fwht_blocks_f32(y) - x).max() <= 1e-5
+
+
+def test_rotation_preserves_products():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 384))
+    w = rng.standard_normal((6, 384))
+    lhs = ow.fwht_blocks_f32(x).astype(np.float64) @ ow.fwht_blocks_f32(w).astype(np.float64).T
+    assert np.abs(lhs - x @ w.T).max() <= 1e-4 * np.abs(x @ w.T).max()
+
+
+def test_quantize_hand_worked_and_bounds():
+    # amax = 2.54 (float32): 127 / 2.54 rounds to exactly 50 in float32; then 1.0 -> 50, -2.54 -> -127,
+    # 0.01 * 50 rounds to 0.5 -> 0 (ties to even), 0.03 * 50 rounds to 1.5 -> 2 (ties to even)
+    v = np.array([[1.0, -2.54, 0.01, 0.03]], np.float32)
+    q, s = ow.quantize_rows_f32(v)
+    assert np.float32(127.0) / np.float32(2.54) == np.float32(50.0)
+    assert q[0].tolist() == [50, -127, 0, 2]
+    assert s[0] == np.float32(2.54) / np.float32(127.0)
+    # the round-trip error is at most half a step, and zero rows stay zero
+    rng = np.random.default_rng(3)
+    r = rng.standard_normal((20, 128)).astype(np.float32) * 3
+    q, s = ow.quantize_rows_f32(r)
+    assert np.all(np.abs(q.astype(np.float64) * s[:, None] - r) <= 0.5 * s[:, None] * (1 + 1e-5) + 1e-7)
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    qz, sz = ow.quantize_rows_f32(np.zeros((2, 128), np.float32))
+    assert np.all(qz == 0) and np.all(sz == 0)
+
+
+def test_int_matmul_brute_force():
+    rng = np.random.default_rng(4)
+    a = rng.integers(-127, 128, (3, 5)).astype(np.int8)
+    b = rng.integers(-127, 128, (4, 5)).astype(np.int8)
+    got = ow.int_matmul(a, b)
+    for i, j in itertools.product(range(3), range(4)):
+        assert got[i, j] == sum(int(a[i, k]) * int(b[j, k]) for k in range(5))
+    # the worst case of a 14336-deep product stays inside int32
+    assert 14336 * 127 * 127 < 2 ** 31
+
+
+def test_linear_w8a8_within_the_quantization_bound():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((8, 512))
+    w = rng.standard_normal((16, 512)) * 0.02
+    y = ow.linear_w8a8(x, w)
+    ref = x @ w.T
+    xr, wr = ow.fwht_blocks_f32(x).astype(np.float64), ow.fwht_blocks_f32(w).astype(np.float64)
+    _, sx = ow.rotate_quantize(x)
+    _, sw = ow.rotate_quantize(w)
+    ex, ew = 0.5 * sx.astype(np.float64), 0.5 * sw.astype(np.float64)
+    bound = (np.abs(xr).sum(1)[:, None] * ew[None, :] + ex[:, None] * np.abs(wr).sum(1)[None, :]
+             + 512 * ex[:, None] * ew[None, :]) * (1 + 1e-3) + 1e-6
+    assert np.all(np.abs(y - ref) <= bound)
+    # and the error is small in the usual sense
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 2e-2
