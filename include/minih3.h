@@ -297,6 +297,33 @@ int minih3_output_heads(const minih3_config* cfg, const minih3_layout* layout, c
                         const void* x, float* video_out, float* audio_out, void* workspace, size_t workspace_bytes,
                         uint32_t flags, void* stream);
 
+/* ---- Rotated W8A8 INT8 linear layers ----
+ * Page "HyperFlow H3 Flash Brings MiniMax H3 Video to One GPU", How it got
+ * smaller and faster: rotated W8A8 INT8 quantization of the linear layers.
+ * The library takes: the rotation is the normalised Hadamard transform of
+ * every 128-wide block of a row, applied alike to activation rows and
+ * weight rows (so x W^T is unchanged); quantization is symmetric int8 per
+ * row, code = rint(v * (127 / amax)) in [-127, 127], scale = amax / 127
+ * (all-zero rows: codes 0, scale 0); the product accumulates the codes
+ * exactly in int32 and dequantizes with the two scales. The butterflies run
+ * in stages 1, 2, 4, ..., 64 in fp32 followed by one multiplication by
+ * fp32(1/sqrt(128)), and both divisions are correctly rounded fp32, so the
+ * codes are reproducible from that definition. */
+
+/* Rotate and quantize the rows of x [M, K] (dtype MINIH3_BF16 or
+ * MINIH3_F32; K a multiple of 128, at most 16384): q [M, K] int8 codes,
+ * scale [M] fp32. Weight rows [N, K] are prepared the same way, once. */
+int minih3_rotate_quantize(int32_t dtype, const void* x, int32_t M, int32_t K, int8_t* q, float* scale,
+                           void* stream);
+
+/* c[M, N] = bf16((qa . qw^T) * sa[m] * sw[n]): int8 codes qa [M, K] and
+ * qw [N, K] with their row scales sa [M], sw [N] (from
+ * minih3_rotate_quantize), exact int32 accumulation on int8 MFMAs, fp32
+ * dequantization, bf16 output. N % 256 == 0, K % 128 == 0; M*K and N*K
+ * below 4 GiB. */
+int minih3_linear_w8a8(const int8_t* qa, const float* sa, const int8_t* qw, const float* sw, void* c, int32_t M,
+                       int32_t N, int32_t K, void* stream);
+
 /* Kernel timing under MINIH3_PROFILE. Synchronises the recorded events,
  * writes for each kernel id k < n the summed milliseconds and the number of
  * launches since the last collect, then resets. Returns the number of

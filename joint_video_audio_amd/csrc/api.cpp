@@ -772,6 +772,32 @@ int minih3_output_heads(const minih3_config* c, const minih3_layout* L, const mi
   return MINIH3_OK;
 }
 
+int minih3_rotate_quantize(int32_t dtype, const void* x, int32_t M, int32_t K, int8_t* q, float* scale,
+                           void* stream) {
+  if (!x || !q || !scale || M < 1 || K < 1) return MINIH3_E_ARG;
+  if (K % 128 != 0 || K > 16384 || (long)M * K > (1L << 40)) return MINIH3_E_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == MINIH3_BF16)
+    HIPCHECK(launch_rot_quant<bf16_t>((const bf16_t*)x, M, K, q, scale, st));
+  else if (dtype == MINIH3_F32)
+    HIPCHECK(launch_rot_quant<float>((const float*)x, M, K, q, scale, st));
+  else
+    return MINIH3_E_ARG;
+  return MINIH3_OK;
+}
+
+int minih3_linear_w8a8(const int8_t* qa, const float* sa, const int8_t* qw, const float* sw, void* c, int32_t M,
+                       int32_t N, int32_t K, void* stream) {
+  if (!qa || !sa || !qw || !sw || !c || M < 1 || N < 1 || K < 1) return MINIH3_E_ARG;
+  if (N % 256 != 0 || K % 128 != 0 || (long)M * K > 0xFFFFFFFFL || (long)N * K > 0xFFFFFFFFL)
+    return MINIH3_E_UNSUPPORTED;
+  EpiArgs ea{};
+  ea.row_scale = sa;
+  ea.col_scale = sw;
+  HIPCHECK(launch_gemm_i8(kEpiStore, qa, qw, c, M, N, K, ea, (hipStream_t)stream));
+  return MINIH3_OK;
+}
+
 int minih3_profile_collect(double* total_ms, int32_t* launches, int32_t n) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   for (int i = 0; i < n; ++i) {

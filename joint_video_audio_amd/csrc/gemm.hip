@@ -129,11 +129,17 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // step k + 1 and one barrier publishes it and frees A_k's and W_k's slots;
 // the second half loads W_{k+2} into A_k's slot. A_k has about two K steps
 // to arrive, W_k one.
-template <int EPI>
-__global__ void __launch_bounds__(64 * kWaves, 1)
-    k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
-                int K, EpiArgs ea) {
+//
+// I8: the same kernel on int8 operands (v_mfma_i32_16x16x64_i8): a K step is
+// 128 bytes of a row either way, so the LDS ring, the swizzle and the
+// fragment reads are unchanged; a step covers 128 int8 columns instead of
+// 64 bf16 ones. The int32 accumulators are turned into fp32
+// acc * row_scale[m] * col_scale[W row] before the epilogue.
+template <int EPI, int I8>
+__device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
+                                          void* __restrict__ Cv, int M, int N, int K, const EpiArgs& ea) {
   constexpr int WTM = 128, WTN = 128, MI = WTM / 16, NI = WTN / 16;
+  constexpr int kEs = I8 ? 1 : 2;  // bytes per element
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -174,10 +180,10 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
     } else {
       wr = tn * BN + row;
     }
-    voff_a[j] = (uint32_t)(((long)am * K + c * 8) * 2);
-    voff_w[j] = (uint32_t)(((long)wr * K + c * 8) * 2);
+    voff_a[j] = (uint32_t)((long)am * K * kEs + c * 16);
+    voff_w[j] = (uint32_t)((long)wr * K * kEs + c * 16);
   }
-  const int KT = K / BK;
+  const int KT = K / (kRowBytes / kEs);
   auto slot_ptr = [&](int s) { return lds + s * kSlotBytes; };
   // DMA instruction j of operand A (or W) of K step k into its ring slot;
   // past the end of K the last step is loaded again (the slot is free).
@@ -227,7 +233,10 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   // registers are rewritten no sooner than 12 MFMAs after their last use.
   auto mfma1 = [&](int set, int i) {
     const int mi = i / NI, ni = i % NI;
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(fw[set][ni]), "v"(fa[set][mi]));
+    if constexpr (I8)
+      asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(fw[set][ni]), "v"(fa[set][mi]));
+    else
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(fw[set][ni]), "v"(fa[set][mi]));
   };
   // One half K step (64 MFMAs) in a fixed issue order: MFMA i, then after
   // every fourth MFMA one fragment of the next half, after every eighth one
@@ -305,6 +314,28 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
 
   // ---- epilogue. A lane's accumulators hold row m = tile row
   // (wm*128 + mi*16 + (lane & 15)), columns wn*128 + ni*16 + 4*(lane>>4) + e.
+  // Accumulator block (mi, ni) as fp32; with int8 operands the int32 sums
+  // times the row's scale and the scale of the W row each column came from.
+  auto deq = [&](int mi, int ni) -> floatx4 {
+    if constexpr (I8) {
+      int m = m0 + wm * WTM + mi * 16 + fr_row;
+      m = m < M ? m : M - 1;
+      int wrow;
+      if constexpr (EPI == kEpiSwiGLU)
+        wrow = (ni < NI / 2 ? 0 : ea.ffn_dim) + 128 * tn + (WTN / 2) * wn + (ni % (NI / 2)) * 16 + 4 * fr_q;
+      else
+        wrow = tn * BN + wn * WTN + ni * 16 + 4 * fr_q;
+      const float rs = ea.row_scale[m];
+      const floatx4 cs = *reinterpret_cast<const floatx4*>(ea.col_scale + wrow);
+      const intx4 ai = __builtin_bit_cast(intx4, acc[mi][ni]);
+      floatx4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (float)ai[e] * rs * cs[e];
+      return r;
+    } else {
+      return acc[mi][ni];
+    }
+  };
   if constexpr (EPI == kEpiGatedResid) {
     // gated residual straight from the accumulators (staging through LDS
     // measured slower, as did staging the SwiGLU output). Per lane row: its
@@ -341,8 +372,9 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           const int n = tn * BN + wn * WTN + ni * 16 + 4 * fr_q;
+          const floatx4 a = deq(mi, ni);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[ni][e] += (tr >= 0 ? g[ni][e] : 0.f) * acc[mi][ni][e];
+          for (int e = 0; e < 4; ++e) r[ni][e] += (tr >= 0 ? g[ni][e] : 0.f) * a[e];
           store4<TO>(out + (long)m * N + n, r[ni]);
         }
       }
@@ -368,8 +400,9 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
 #pragma unroll
       for (int ni = 0; ni < NI / 2; ++ni) {
         float v[4];
+        const floatx4 g = deq(mi, ni), u = deq(mi, ni + NI / 2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = silu(acc[mi][ni][e]) * acc[mi][ni + NI / 2][e];
+        for (int e = 0; e < 4; ++e) v[e] = silu(g[e]) * u[e];
         const int f = 128 * tn + (WTN / 2) * wn + ni * 16 + 4 * fr_q;
         store4<bf16_t>(static_cast<bf16_t*>(Cv) + (long)m * F + f, v);
       }
@@ -385,8 +418,9 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
       for (int ni = 0; ni < NI; ++ni) {
         const int r = wm * WTM + mi * 16 + fr_row, c = wn * WTN + ni * 16 + 4 * fr_q;
         u32x2 pk;
-        pk[0] = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
-        pk[1] = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+        const floatx4 a = deq(mi, ni);
+        pk[0] = pack_bf16x2(a[0], a[1]);
+        pk[1] = pack_bf16x2(a[2], a[3]);
         *reinterpret_cast<u32x2*>(lds + r * RB + c * 2) = pk;
       }
     __syncthreads();
@@ -398,6 +432,20 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
             *reinterpret_cast<const u32x2*>(lds + rr * RB + lane * 8);
     }
   }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(64 * kWaves, 1)
+    k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
+                int K, EpiArgs ea) {
+  gemm_body<EPI, 0>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(64 * kWaves, 1)
+    k_gemm_i8(const int8_t* __restrict__ A, const int8_t* __restrict__ W, void* __restrict__ Cv, int M, int N, int K,
+              EpiArgs ea) {
+  gemm_body<EPI, 1>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea);
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -478,6 +526,20 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* 
     case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* W, void* C, int M, int N, int K, const EpiArgs& ea,
+                          hipStream_t st) {
+  if (M <= 0 || N % BN != 0 || K % 128 != 0 || !ea.row_scale || !ea.col_scale) return hipErrorInvalidValue;
+  if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
+  if ((unsigned long)M * K > 0xFFFFFFFFul || (unsigned long)N * K > 0xFFFFFFFFul) return hipErrorInvalidValue;
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  dim3 grid((unsigned)tiles);
+  // only the plain store is served with int8 operands (the fused epilogues
+  // are used with bf16 operands only)
+  if (epi != kEpiStore) return hipErrorInvalidValue;
+  k_gemm_i8<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea);
   return hipGetLastError();
 }
 

@@ -65,7 +65,13 @@ struct EpiArgs {
   int num_tags, num_tvals;
   int gate_slot;         // 2 (attention gate) or 5 (FFN gate)
   int ffn_dim;           // SwiGLU: F (W rows [0,F) gate, [F,2F) up)
+  const float* row_scale;  // int8 kernel: per A row
+  const float* col_scale;  // int8 kernel: per W row
 };
+// int8 operands (K % 128 == 0), int32 accumulation, dequantized with
+// ea.row_scale[m] * ea.col_scale[n]; plain store epilogue only (bf16 C).
+hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* W, void* C, int M, int N, int K, const EpiArgs& ea,
+                          hipStream_t st);
 template <typename T>
 hipError_t launch_gemm(int epi, const T* A, const T* W, void* C, int M, int N, int K, const EpiArgs& ea,
                        hipStream_t st);
@@ -154,5 +160,11 @@ struct EdgeHeads {
 };
 template <typename T>
 hipError_t launch_edge_out(const T* x, const EdgeHeads& heads, int B, int S, int D, float eps, hipStream_t st);
+
+// ---- rotated W8A8 ----
+// Rows of x [M, K] (K % 128 == 0, K <= 16384): blockwise normalised Hadamard
+// rotation (128 wide), then symmetric int8 codes q [M, K] and fp32 scales [M].
+template <typename T>
+hipError_t launch_rot_quant(const T* x, int M, int K, int8_t* q, float* scale, hipStream_t st);
 
 }  // namespace minih3

@@ -128,7 +128,10 @@ def lib() -> ctypes.CDLL:
                                           _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_uint32, _P]
         L.minih3_output_heads.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), ctypes.POINTER(_Edges), _P,
                                           _P, _P, _P, ctypes.c_size_t, ctypes.c_uint32, _P]
-        for fn in ("minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads"):
+        L.minih3_rotate_quantize.argtypes = [ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+        L.minih3_linear_w8a8.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
+        for fn in ("minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
+                   "minih3_rotate_quantize", "minih3_linear_w8a8"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
                    "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
@@ -143,7 +146,8 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
             "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
             "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
-            "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads")
+            "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
+            "minih3_rotate_quantize", "minih3_linear_w8a8")
 
 
 def status_string(s: int) -> str:
@@ -502,6 +506,40 @@ def output_heads(cfg: Config, layout: DeviceLayout, edges: DeviceEdges, x: torch
     _check(lib().minih3_output_heads(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(ce), _ptr(x), _ptr(v), _ptr(a),
                                      _ptr(workspace), workspace.numel(), flags, _stream()), "output_heads")
     return v, a
+
+
+def rotate_quantize(x: torch.Tensor):
+    """Rows of x [M, K] (bf16 or fp32) -> (int8 codes [M, K], fp32 scales [M]) after the blockwise
+    Hadamard rotation."""
+    if x.dtype == torch.bfloat16:
+        dtc = BF16
+    elif x.dtype == torch.float32:
+        dtc = F32
+    else:
+        raise ValueError("x must be bf16 or fp32")
+    M, K = x.shape
+    _req(x, x.dtype, "x")
+    q = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    sc = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib().minih3_rotate_quantize(dtc, _ptr(x), M, K, _ptr(q), _ptr(sc), _stream()), "rotate_quantize")
+    return q, sc
+
+
+def linear_w8a8(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 out[M, N] = (qa . qw^T) * sa[m] * sw[n] from int8 codes and fp32 row scales."""
+    M, K = qa.shape
+    N = qw.shape[0]
+    _req(qa, torch.int8, "qa")
+    _req(qw, torch.int8, "qw", N * K)
+    _req(sa, torch.float32, "sa", M)
+    _req(sw, torch.float32, "sw", N)
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=qa.device)
+    _req(out, torch.bfloat16, "out", M * N)
+    _check(lib().minih3_linear_w8a8(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(out), M, N, K, _stream()),
+           "linear_w8a8")
+    return out
 
 
 def profile_collect() -> dict:

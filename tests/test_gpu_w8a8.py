@@ -1,0 +1,101 @@
+"""Parity of the rotated W8A8 INT8 path against the oracle (GPU).
+
+The int8 codes and their scales are integers / float32 values decided by
+float32 arithmetic in a fixed order, so they are compared bit-exactly; the
+product accumulates exactly in int32, so the bf16 output is checked element
+by element against the exact dequantized value (one fp32 dequantization and
+one bf16 rounding apart).
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import gpu_available
+from joint_video_audio_amd import device as dv
+from joint_video_audio_amd import minih3 as m
+from joint_video_audio_amd import synth
+from oracle import w8a8 as ow
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def bf16_pair(a: np.ndarray):
+    t = synth.Tensor(synth.round_to_bf16_bits(a.astype(np.float32)), "bf16")
+    return dv.to_device(t), synth.bf16_bits_to_f32(t.data)
+
+
+def rows(M, K, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((M, K)) * scale).astype(np.float32)
+    if M > 3:
+        x[1] = 0.0                 # all-zero row: codes 0, scale 0
+        x[2] = 0.0
+        x[2, K // 3] = -7.5        # one large value
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(5, 128), (33, 384), (300, 5376), (17, 7168), (9, 14336)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rotate_quantize_bit_exact(M, K, dtype):
+    print(f"rotate_quantize {dtype} M={M} K={K}", flush=True)
+    x = rows(M, K, M + K, scale=2.0)
+    if dtype == "bf16":
+        xd, xv = bf16_pair(x)
+    else:
+        xd, xv = torch.from_numpy(x).cuda(), x
+    q, sc = m.rotate_quantize(xd)
+    torch.cuda.synchronize()
+    rq, rs = ow.rotate_quantize(xv)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.all(q[1].cpu().numpy() == 0) and sc[1].item() == 0.0
+
+
+def check_linear(qa, sa, qw, sw, out):
+    acc = ow.int_matmul(qa, qw).astype(np.float64)
+    ref = acc * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+    got = out.float().cpu().numpy().astype(np.float64)
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max()
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (int(bad.sum()), float(np.abs(got - ref).max()))
+
+
+# K steps of 128: one, two, five, eight; ragged M
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (300, 512, 256), (513, 768, 640), (2048, 1024, 1024)])
+def test_linear_w8a8(M, N, K):
+    print(f"linear_w8a8 M={M} N={N} K={K}", flush=True)
+    xd, xv = bf16_pair(rows(M, K, 1))
+    wd, wv = bf16_pair(rows(N, K, 2, scale=0.02))
+    qa, sa = m.rotate_quantize(xd)
+    qw, sw = m.rotate_quantize(wd)
+    out = m.linear_w8a8(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    # the codes are the oracle's (bit-exact above); the product is checked against their exact value
+    rqa, rsa = ow.rotate_quantize(xv)
+    rqw, rsw = ow.rotate_quantize(wv)
+    assert np.array_equal(qa.cpu().numpy(), rqa) and np.array_equal(qw.cpu().numpy(), rqw)
+    check_linear(rqa, rsa, rqw, rsw, out)
+    # and the W8A8 result tracks the bf16 product within the quantization error
+    ref = xv.astype(np.float64) @ wv.astype(np.float64).T
+    got = out.float().cpu().numpy()
+    assert np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30) < 3e-2
+
+
+def test_linear_w8a8_full_qkv_shape_sampled_rows():
+    # the QKV projection of the clip-scale block: 32768 x 21504 x 5376
+    print("linear_w8a8 full QKV shape", flush=True)
+    M, N, K = 32768, 21504, 5376
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    qa, sa = m.rotate_quantize(x)
+    qw, sw = m.rotate_quantize(w)
+    out = m.linear_w8a8(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 255, 256, 4097, 20000, 32766, 32767])
+    xs = x[sel].float().cpu().numpy()
+    rqa, rsa = ow.rotate_quantize(xs)
+    assert np.array_equal(qa[sel].cpu().numpy(), rqa)
+    rqw, rsw = ow.rotate_quantize(w.float().cpu().numpy())
+    assert np.array_equal(qw.cpu().numpy(), rqw)
+    check_linear(rqa, rsa, rqw, rsw, out[sel])
