@@ -18,7 +18,9 @@ cpu_baseline times the fp64 oracle on a bounded sample of the workload.
 table_build times, apart from the step, the build of one block's AdaLN
 table from the workload's timestep values (time embeddings, then the bf16
 AdaLN projection), with the projection's HBM roofline; edges times the
-input projections into the packed sequence and the output heads (fp32).
+input projections into the packed sequence and the output heads (fp32);
+w8a8 times the rotated W8A8 INT8 variant of the four projections beside the
+bf16 ones (a separate variant: the headline step is bf16).
 """
 from __future__ import annotations
 
@@ -207,6 +209,65 @@ def edges(wl, seed: int, reps: int, warmup: int):
             "embed_inputs_tflops": round(tf_in, 1), "embed_inputs_frac": round(tf_in / FP32_MFMA_PEAK_TFLOPS, 4)}
 
 
+INT8_MFMA_PEAK_TOPS = 5033.2  # 256 CU x 2.4 GHz x 8192 int8 ops/clk (dense)
+
+
+def w8a8(reps: int, warmup: int, M: int = 32768):
+    """Time the rotated W8A8 linear layer on the four projection shapes of the
+    block at M packed rows (QKV, output, gate/up, down) beside the bf16
+    projection on the same shapes, and the rotation + quantization of the
+    activations. Synthetic N(0,1) activations and N(0,0.02) weights; HIP
+    events bracket each call."""
+    import torch
+    from joint_video_audio_amd import minih3 as m
+    shapes = {"qkv": (21504, 5376), "out": (5376, 7168), "gate_up": (28672, 5376), "down": (5376, 14336)}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {}
+    tot_i8 = tot_bf = tot_q = 0.0
+    flop_all = 0.0
+    for name, (N, K) in shapes.items():
+        x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        qw, sw = m.rotate_quantize(w)
+        qa, sa = m.rotate_quantize(x)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        t_i8 = timed(lambda: m.linear_w8a8(qa, sa, qw, sw, out=out))
+        t_bf = timed(lambda: m.linear(x, w, out=out))
+        t_q = timed(lambda: m.rotate_quantize(x))
+        flop = 2.0 * M * N * K
+        res[name] = {"N": N, "K": K, "int8_ms": round(t_i8, 4), "bf16_ms": round(t_bf, 4),
+                     "rotate_quantize_ms": round(t_q, 4), "int8_tops": round(flop / (t_i8 / 1e3) / 1e12, 1),
+                     "bf16_tflops": round(flop / (t_bf / 1e3) / 1e12, 1)}
+        tot_i8 += t_i8
+        tot_bf += t_bf
+        tot_q += t_q
+        flop_all += flop
+        del x, w, qw, qa, out
+    tops = flop_all / (tot_i8 / 1e3) / 1e12
+    res["rows"] = M
+    res["total_int8_ms"] = round(tot_i8, 4)
+    res["total_bf16_ms"] = round(tot_bf, 4)
+    res["total_rotate_quantize_ms"] = round(tot_q, 4)
+    res["roofline"] = {"kernel": "linear_w8a8", "bound": "mfma", "achieved": round(tops, 1),
+                       "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOP/s", "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
+                       "traffic": None, "avg_launch_ms": round(tot_i8 / 4, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +279,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table-build", action="store_true")
     ap.add_argument("--no-edges", action="store_true")
+    ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -313,6 +375,8 @@ def main():
         res["table_build"] = table_build(wl, a.seed, reps=50, warmup=5)
     if not a.no_edges:
         res["edges"] = edges(wl, a.seed, reps=20, warmup=3)
+    if not a.no_w8a8 and a.workload == "clip32k":
+        res["w8a8"] = w8a8(reps=10, warmup=2)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)
