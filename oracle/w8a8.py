@@ -73,8 +73,14 @@ def rotate_quantize(x):
 
 
 def int_matmul(qa, qw) -> np.ndarray:
-    """Exact integer product qa [M, K] . qw [N, K]^T (reading c)."""
-    return np.asarray(qa, np.int64) @ np.asarray(qw, np.int64).T
+    """Exact integer product qa [M, K] . qw [N, K]^T (reading c), int64.
+
+    Evaluated as a float64 product: every term is at most 127^2 and every
+    partial sum at most K * 127^2 < 2^53, so each float64 operation is exact.
+    """
+    qa, qw = np.asarray(qa), np.asarray(qw)
+    assert qa.shape[-1] * 127 * 127 < 2 ** 53
+    return (qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
 
 
 def linear_w8a8(x, w) -> np.ndarray:
@@ -83,3 +89,51 @@ def linear_w8a8(x, w) -> np.ndarray:
     qw, sw = rotate_quantize(w)
     acc = int_matmul(qx, qw).astype(np.float64)
     return acc * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+
+
+# --------------------------------------------------------------------------
+# A block with every projection on rotated W8A8
+# --------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> float32 -> bfloat16 (round to nearest even) -> float64: the
+    value a bf16 activation tensor holds."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def block_forward_w8a8(x, layout, w, dims) -> np.ndarray:
+    """One block (the steps of oracle.block.block_forward) with each of the
+    four projections on rotated W8A8. A bf16 block feeds its projections
+    bf16 tensors, so each input (the AdaLN outputs, the attention output, the
+    SwiGLU output) is rounded to bf16 before it is rotated and quantized;
+    the weights are the block's bf16 matrices, rotated and quantized per row."""
+    from . import block as ob
+    tags = np.asarray(layout.token_tags)
+    tidx = np.asarray(layout.timestep_indices)
+    pos = np.asarray(layout.position_ids)
+    S, D = x.shape
+    H, hd, F = dims.num_heads, dims.head_dim, dims.ffn_dim
+    W = H * hd
+    table = w["adaln_table"]
+
+    def lin(inp, wm):
+        return linear_w8a8(round_bf16(inp), wm)
+
+    a = ob.adaln(x, table, tags, tidx, 0, dims.norm_eps)
+    qkv = lin(a, w["w_qkv"])
+    q = qkv[:, :W].reshape(S, H, hd)
+    k = qkv[:, W:2 * W].reshape(S, H, hd)
+    v = qkv[:, 2 * W:].reshape(S, H, hd)
+    qn = ob.rope_3d(ob.rms_norm_heads(q, w["q_norm"], dims.qk_norm_eps), pos, dims.rope_freq_dim, dims.rope_theta)
+    kn = ob.rope_3d(ob.rms_norm_heads(k, w["k_norm"], dims.qk_norm_eps), pos, dims.rope_freq_dim, dims.rope_theta)
+    o = ob.attention_doc_masked(qn, kn, v, ob.doc_ids(tags), 1.0 / np.sqrt(hd)).reshape(S, W)
+    _, _, gate1 = ob.modulation(table, tags, tidx, 0)
+    x_mid = x + gate1 * lin(o, w["w_out"])
+    b = ob.adaln(x_mid, table, tags, tidx, 1, dims.norm_eps)
+    gu = lin(b, w["w_gate_up"])
+    h = ob.silu(gu[:, :F]) * gu[:, F:]
+    _, _, gate2 = ob.modulation(table, tags, tidx, 1)
+    return x_mid + gate2 * lin(h, w["w_down"])

@@ -97,3 +97,33 @@ def test_linear_w8a8_within_the_quantization_bound():
     assert np.all(np.abs(y - ref) <= bound)
     # and the error is small in the usual sense
     assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 2e-2
+
+
+def test_round_bf16_values():
+    # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1;
+    # 1 + 3 * 2^-8 ties up to 1 + 2^-6 (even mantissa); 3.0 is exact
+    got = ow.round_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 3.0, -1.5]))
+    assert got.tolist() == [1.0, 1 + 2.0 ** -6, 3.0, -1.5]
+
+
+def test_w8a8_block_tracks_the_plain_block():
+    # the W8A8 block differs from the plain block only by the quantization of
+    # the four projections: with gate 0 both are the identity, and otherwise
+    # they agree to the quantization error
+    from oracle import block as ob
+    from oracle import weights_f64
+    from joint_video_audio_amd import synth
+    dims = synth.ModelDims(hidden=256, num_heads=2, head_dim=128, ffn_dim=384, num_tvals=4, dtype="bf16")
+    segs = [("text", 7), ("audio", 5), ("video", 24, (2, 3, 4))]
+    wl = synth.make_custom(dims, segs, (2, 3, 4), 3, seed=0)
+    w = weights_f64(wl.blocks[0])
+    x = wl.x.values()[0]
+    y8 = ow.block_forward_w8a8(x, wl.layout, w, dims)
+    y = ob.block_forward(x, wl.layout, w, dims)
+    rel = np.linalg.norm(y8 - y) / np.linalg.norm(y - x)
+    assert rel < 5e-2, rel  # relative to the block's own change of x
+    w0 = dict(w)
+    w0["adaln_table"] = w["adaln_table"].copy()
+    w0["adaln_table"][:, :, 2] = 0.0
+    w0["adaln_table"][:, :, 5] = 0.0
+    assert np.array_equal(ow.block_forward_w8a8(x, wl.layout, w0, dims), x)
