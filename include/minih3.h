@@ -316,6 +316,34 @@ int minih3_output_heads(const minih3_config* cfg, const minih3_layout* layout, c
 int minih3_rotate_quantize(int32_t dtype, const void* x, int32_t M, int32_t K, int8_t* q, float* scale,
                            void* stream);
 
+/* Weights of one block for the rotated W8A8 forward: each projection's
+ * weight rows as int8 codes with per-row fp32 scales, as
+ * minih3_rotate_quantize returns them for the bf16 matrices of
+ * minih3_block_weights (same shapes and row order); norms and table as there. */
+typedef struct {
+  const int8_t* q_qkv;     const float* s_qkv;     /* [3W, D], [3W] */
+  const int8_t* q_out;     const float* s_out;     /* [D, W],  [D]  */
+  const int8_t* q_gate_up; const float* s_gate_up; /* [2F, D], [2F] */
+  const int8_t* q_down;    const float* s_down;    /* [D, F],  [D]  */
+  const float* q_norm;
+  const float* k_norm;
+  const float* adaln_table;
+} minih3_block_weights_w8a8;
+
+/* Bytes of workspace minih3_block_forward_w8a8 needs (bf16 configs only). */
+int minih3_workspace_bytes_w8a8(const minih3_config* cfg, int32_t batch, int32_t seq_len, size_t* bytes);
+
+/* minih3_block_forward with every projection on rotated W8A8: the bf16 input
+ * rows of each projection are rotated and quantized per row, multiplied with
+ * the int8 weight codes on int8 MFMAs and dequantized into the same fused
+ * epilogues (store, gated residual, SwiGLU). bf16 activations only; D, H*hd
+ * and ffn_dim multiples of 128 and at most 16384. Taps as in
+ * minih3_block_forward (attn_proj and ffn_out are the W8A8 products). */
+int minih3_block_forward_w8a8(const minih3_config* cfg, const minih3_layout* layout,
+                              const minih3_block_weights_w8a8* blocks, int32_t num_blocks, const void* x_in,
+                              void* x_out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                              minih3_taps* taps, void* stream);
+
 /* c[M, N] = bf16((qa . qw^T) * sa[m] * sw[n]): int8 codes qa [M, K] and
  * qw [N, K] with their row scales sa [M], sw [N] (from
  * minih3_rotate_quantize), exact int32 accumulation on int8 MFMAs, fp32

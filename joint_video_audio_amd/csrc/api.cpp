@@ -123,6 +123,8 @@ int check_layout(const minih3_layout* L, bool need_indices) {
 
 struct Workspace {
   void *a, *qkvh, *qn, *kn, *vt, *o, *xmid, *xping;
+  int8_t* qx;     // rotated W8A8: int8 codes of a projection's input rows
+  float* sx;      // and their scales
   uint64_t* masks;
   void* attn_scratch;
   int32_t *list_real, *list_pad, *meta, *counts, *npad;
@@ -154,7 +156,7 @@ size_t tiles_bytes(int B, int S, int H, int32_t** list_real, int32_t** list_pad,
   return off;
 }
 
-Workspace carve(const minih3_config* c, int B, int S, char* base) {
+Workspace carve(const minih3_config* c, int B, int S, char* base, bool w8a8 = false) {
   Workspace w{};
   const size_t e = act_size(c->act_dtype);
   const size_t D = c->hidden, H = c->num_heads, hd = c->head_dim, F = c->ffn_dim;
@@ -180,6 +182,11 @@ Workspace carve(const minih3_config* c, int B, int S, char* base) {
   w.counts = (int32_t*)take(4 * (size_t)S);
   w.npad = (int32_t*)take(4);
   w.err = (uint32_t*)take(4);
+  if (w8a8) {
+    const size_t kmax = D > Wd ? (D > F ? D : F) : (Wd > F ? Wd : F);
+    w.qx = (int8_t*)take(M * kmax);
+    w.sx = (float*)take(4 * M);
+  }
   w.total = off;
   return w;
 }
@@ -198,9 +205,13 @@ int status_from_err(uint32_t err) {
     if ((x) != hipSuccess) return MINIH3_E_HIP;   \
   } while (0)
 
+// One block after another. With qblocks (bf16 only) every projection runs on
+// rotated W8A8: its bf16 input rows are rotated and quantized into w.qx /
+// w.sx, and the int8 kernel applies the same fused epilogue.
 template <typename T>
 int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks, int nb,
-               const T* x_in, T* x_out, Workspace& w, uint32_t flags, minih3_taps* taps, hipStream_t st) {
+               const T* x_in, T* x_out, Workspace& w, uint32_t flags, minih3_taps* taps, hipStream_t st,
+               const minih3_block_weights_w8a8* qblocks = nullptr) {
   const int B = L->batch, S = L->seq_len;
   const int D = c->hidden, H = c->num_heads, hd = c->head_dim, F = c->ffn_dim;
   const int Wd = H * hd;
@@ -227,7 +238,31 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
   const void* src = x_in;
   bool src_f32 = sizeof(T) == 4;
   for (int i = 0; i < nb; ++i) {
-    const minih3_block_weights& bw = blocks[i];
+    minih3_block_weights bw{};
+    if (qblocks) {
+      bw.q_norm = qblocks[i].q_norm;
+      bw.k_norm = qblocks[i].k_norm;
+      bw.adaln_table = qblocks[i].adaln_table;
+    } else {
+      bw = blocks[i];
+    }
+    // C = A . W^T with epilogue `epi`; `which` picks the weight (0 qkv, 1 out, 2 gate/up, 3 down)
+    auto proj = [&](int epi, const T* A, int which, void* C, int N, int K, EpiArgs& ea) -> hipError_t {
+      if (!qblocks) {
+        const void* W = which == 0 ? bw.w_qkv : which == 1 ? bw.w_out : which == 2 ? bw.w_gate_up : bw.w_down;
+        return launch_gemm<T>(epi, A, (const T*)W, C, M, N, K, ea, st);
+      }
+      const minih3_block_weights_w8a8& qb = qblocks[i];
+      const int8_t* QW = which == 0 ? qb.q_qkv : which == 1 ? qb.q_out : which == 2 ? qb.q_gate_up : qb.q_down;
+      const float* SW = which == 0 ? qb.s_qkv : which == 1 ? qb.s_out : which == 2 ? qb.s_gate_up : qb.s_down;
+      hipError_t r = launch_rot_quant<bf16_t>(reinterpret_cast<const bf16_t*>(A), M, K, w.qx, w.sx, st);
+      if (r != hipSuccess) return r;
+      ea.row_scale = w.sx;
+      ea.col_scale = SW;
+      r = launch_gemm_i8(epi, w.qx, QW, C, M, N, K, ea, st);
+      ea.row_scale = ea.col_scale = nullptr;
+      return r;
+    };
     const bool last = i == nb - 1;
     void* dst = last ? (void*)x_out : (void*)ping;  // ping may be src: src is consumed before dst is written
     const bool tap = taps && i == 0;
@@ -248,7 +283,7 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
     if (tap && taps->adaln1) HIPCHECK(hipMemcpyAsync(taps->adaln1, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
     {
       Timed tm(prof, kKQKV, st);
-      HIPCHECK(launch_gemm<T>(kEpiStore, a, (const T*)bw.w_qkv, qkv, M, 3 * Wd, D, ea, st));
+      HIPCHECK(proj(kEpiStore, a, 0, qkv, 3 * Wd, D, ea));
     }
     {
       // bf16: the same pass records the key norms the attention kernel needs
@@ -273,14 +308,14 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
                                    Sp, scale, st));
     }
     if (tap && taps->attn_o) HIPCHECK(hipMemcpyAsync(taps->attn_o, o, (size_t)M * Wd * e, hipMemcpyDeviceToDevice, st));
-    if (tap && taps->attn_proj) HIPCHECK(launch_gemm<T>(kEpiStore, o, (const T*)bw.w_out, taps->attn_proj, M, D, Wd, ea, st));
+    if (tap && taps->attn_proj) HIPCHECK(proj(kEpiStore, o, 1, taps->attn_proj, D, Wd, ea));
     {
       Timed tm(prof, kKOutProj, st);
       ea.resid = src;
       ea.resid_f32 = src_f32;
       ea.out_f32 = 1;
       ea.gate_slot = 2;
-      HIPCHECK(launch_gemm<T>(kEpiGatedResid, o, (const T*)bw.w_out, xmid, M, D, Wd, ea, st));
+      HIPCHECK(proj(kEpiGatedResid, o, 1, xmid, D, Wd, ea));
     }
     if (tap && taps->x_mid) HIPCHECK(launch_cast_f32<T>(xmid, (T*)taps->x_mid, (long)M * D, st));
     {
@@ -291,17 +326,17 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
     if (tap && taps->adaln2) HIPCHECK(hipMemcpyAsync(taps->adaln2, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
     {
       Timed tm(prof, kKGateUp, st);
-      HIPCHECK(launch_gemm<T>(kEpiSwiGLU, a, (const T*)bw.w_gate_up, hbuf, M, 2 * F, D, ea, st));
+      HIPCHECK(proj(kEpiSwiGLU, a, 2, hbuf, 2 * F, D, ea));
     }
     if (tap && taps->ffn_h) HIPCHECK(hipMemcpyAsync(taps->ffn_h, hbuf, (size_t)M * F * e, hipMemcpyDeviceToDevice, st));
-    if (tap && taps->ffn_out) HIPCHECK(launch_gemm<T>(kEpiStore, hbuf, (const T*)bw.w_down, taps->ffn_out, M, D, F, ea, st));
+    if (tap && taps->ffn_out) HIPCHECK(proj(kEpiStore, hbuf, 3, taps->ffn_out, D, F, ea));
     {
       Timed tm(prof, kKDown, st);
       ea.resid = xmid;
       ea.resid_f32 = 1;
       ea.out_f32 = last ? (sizeof(T) == 4) : 1;
       ea.gate_slot = 5;
-      HIPCHECK(launch_gemm<T>(kEpiGatedResid, hbuf, (const T*)bw.w_down, dst, M, D, F, ea, st));
+      HIPCHECK(proj(kEpiGatedResid, hbuf, 3, dst, D, F, ea));
     }
     src = dst;
     src_f32 = !last || sizeof(T) == 4;
@@ -438,6 +473,72 @@ int validate_layout(const minih3_config* c, const minih3_layout* L, uint32_t fla
   return status_from_err(err);
 }
 
+int block_forward(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks,
+                  const minih3_block_weights_w8a8* qblocks, int32_t num_blocks, const void* x_in, void* x_out,
+                  void* workspace, size_t workspace_bytes, uint32_t flags, minih3_taps* taps, void* stream) {
+  int s = check_config(c);
+  if (s) return s;
+  const bool validate = flags & MINIH3_VALIDATE;
+  s = check_layout(L, validate);
+  if (s) return s;
+  if (num_blocks < 1 || (!blocks && !qblocks) || !x_in || !x_out || x_in == x_out) return MINIH3_E_ARG;
+  for (int i = 0; i < num_blocks; ++i) {
+    if (qblocks) {
+      const minih3_block_weights_w8a8& b = qblocks[i];
+      if (!b.q_qkv || !b.s_qkv || !b.q_out || !b.s_out || !b.q_gate_up || !b.s_gate_up || !b.q_down || !b.s_down ||
+          !b.q_norm || !b.k_norm || !b.adaln_table)
+        return MINIH3_E_ARG;
+    } else {
+      const minih3_block_weights& b = blocks[i];
+      if (!b.w_qkv || !b.w_out || !b.w_gate_up || !b.w_down || !b.q_norm || !b.k_norm || !b.adaln_table)
+        return MINIH3_E_ARG;
+    }
+  }
+  if (qblocks) {
+    if (c->act_dtype != MINIH3_BF16) return MINIH3_E_UNSUPPORTED;
+    const long Wq = (long)c->num_heads * c->head_dim;
+    if (c->hidden % 128 != 0 || Wq % 128 != 0 || c->ffn_dim % 128 != 0 || c->ffn_dim > 16384 ||
+        c->hidden > 16384 || Wq > 16384)
+      return MINIH3_E_UNSUPPORTED;
+  }
+  if (c->act_dtype == MINIH3_BF16) {
+    const long rows = (long)L->batch * L->seq_len, D = c->hidden, W = (long)c->num_heads * c->head_dim;
+    const long F = c->ffn_dim;
+    if (!gemm_fits(rows, 3 * W, D) || !gemm_fits(rows, D, W) || !gemm_fits(rows, 2 * F, D) || !gemm_fits(rows, D, F))
+      return MINIH3_E_UNSUPPORTED;
+  }
+  Workspace w = carve(c, L->batch, L->seq_len, (char*)workspace, qblocks != nullptr);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const bool prof = flags & MINIH3_PROFILE;
+
+  const bool int_taps = taps && (taps->table_row || taps->doc_id || taps->tile_flags || taps->num_pad);
+  if (validate || int_taps) {
+    LayoutDev ld = make_layout_dev(c, L);
+    if (!validate) ld.n_idx[0] = ld.n_idx[1] = ld.n_idx[2] = 0;
+    {
+      Timed tm(prof, kKLayout, st);
+      if (launch_layout_validate(ld, (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0, w.counts, w.err, w.npad,
+                                 taps ? taps->table_row : nullptr, taps ? taps->doc_id : nullptr,
+                                 taps ? taps->tile_flags : nullptr, st) != hipSuccess)
+        return MINIH3_E_HIP;
+    }
+    if (taps && taps->num_pad)
+      HIPCHECK(hipMemcpyAsync(taps->num_pad, w.npad, 4, hipMemcpyDeviceToDevice, st));
+    if (validate) {
+      uint32_t err = 0;
+      HIPCHECK(hipMemcpyAsync(&err, w.err, 4, hipMemcpyDeviceToHost, st));
+      HIPCHECK(hipStreamSynchronize(st));
+      s = status_from_err(err);
+      if (s) return s;
+    }
+  }
+  if (c->act_dtype == MINIH3_BF16)
+    return run_blocks<bf16_t>(c, L, blocks, num_blocks, (const bf16_t*)x_in, (bf16_t*)x_out, w, flags, taps, st,
+                              qblocks);
+  return run_blocks<float>(c, L, blocks, num_blocks, (const float*)x_in, (float*)x_out, w, flags, taps, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -479,52 +580,24 @@ int minih3_attention_workspace_bytes(const minih3_config* c, int32_t batch, int3
 int minih3_block_forward(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks,
                          int32_t num_blocks, const void* x_in, void* x_out, void* workspace, size_t workspace_bytes,
                          uint32_t flags, minih3_taps* taps, void* stream) {
+  return block_forward(c, L, blocks, nullptr, num_blocks, x_in, x_out, workspace, workspace_bytes, flags, taps,
+                       stream);
+}
+
+int minih3_workspace_bytes_w8a8(const minih3_config* c, int32_t batch, int32_t seq_len, size_t* bytes) {
   int s = check_config(c);
   if (s) return s;
-  const bool validate = flags & MINIH3_VALIDATE;
-  s = check_layout(L, validate);
-  if (s) return s;
-  if (num_blocks < 1 || !blocks || !x_in || !x_out || x_in == x_out) return MINIH3_E_ARG;
-  for (int i = 0; i < num_blocks; ++i) {
-    const minih3_block_weights& b = blocks[i];
-    if (!b.w_qkv || !b.w_out || !b.w_gate_up || !b.w_down || !b.q_norm || !b.k_norm || !b.adaln_table)
-      return MINIH3_E_ARG;
-  }
-  if (c->act_dtype == MINIH3_BF16) {
-    const long rows = (long)L->batch * L->seq_len, D = c->hidden, W = (long)c->num_heads * c->head_dim;
-    const long F = c->ffn_dim;
-    if (!gemm_fits(rows, 3 * W, D) || !gemm_fits(rows, D, W) || !gemm_fits(rows, 2 * F, D) || !gemm_fits(rows, D, F))
-      return MINIH3_E_UNSUPPORTED;
-  }
-  Workspace w = carve(c, L->batch, L->seq_len, (char*)workspace);
-  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  const bool prof = flags & MINIH3_PROFILE;
+  if (c->act_dtype != MINIH3_BF16) return MINIH3_E_UNSUPPORTED;
+  if (!bytes || batch < 1 || seq_len < 1) return MINIH3_E_ARG;
+  *bytes = carve(c, batch, seq_len, nullptr, true).total;
+  return MINIH3_OK;
+}
 
-  const bool int_taps = taps && (taps->table_row || taps->doc_id || taps->tile_flags || taps->num_pad);
-  if (validate || int_taps) {
-    LayoutDev ld = make_layout_dev(c, L);
-    if (!validate) ld.n_idx[0] = ld.n_idx[1] = ld.n_idx[2] = 0;
-    {
-      Timed tm(prof, kKLayout, st);
-      if (launch_layout_validate(ld, (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0, w.counts, w.err, w.npad,
-                                 taps ? taps->table_row : nullptr, taps ? taps->doc_id : nullptr,
-                                 taps ? taps->tile_flags : nullptr, st) != hipSuccess)
-        return MINIH3_E_HIP;
-    }
-    if (taps && taps->num_pad)
-      HIPCHECK(hipMemcpyAsync(taps->num_pad, w.npad, 4, hipMemcpyDeviceToDevice, st));
-    if (validate) {
-      uint32_t err = 0;
-      HIPCHECK(hipMemcpyAsync(&err, w.err, 4, hipMemcpyDeviceToHost, st));
-      HIPCHECK(hipStreamSynchronize(st));
-      s = status_from_err(err);
-      if (s) return s;
-    }
-  }
-  if (c->act_dtype == MINIH3_BF16)
-    return run_blocks<bf16_t>(c, L, blocks, num_blocks, (const bf16_t*)x_in, (bf16_t*)x_out, w, flags, taps, st);
-  return run_blocks<float>(c, L, blocks, num_blocks, (const float*)x_in, (float*)x_out, w, flags, taps, st);
+int minih3_block_forward_w8a8(const minih3_config* c, const minih3_layout* L, const minih3_block_weights_w8a8* blocks,
+                              int32_t num_blocks, const void* x_in, void* x_out, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, minih3_taps* taps, void* stream) {
+  return block_forward(c, L, nullptr, blocks, num_blocks, x_in, x_out, workspace, workspace_bytes, flags, taps,
+                       stream);
 }
 
 int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, const void* q, const void* k,

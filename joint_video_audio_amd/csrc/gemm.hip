@@ -536,10 +536,12 @@ hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* W, void* C, in
   if ((unsigned long)M * K > 0xFFFFFFFFul || (unsigned long)N * K > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
-  // only the plain store is served with int8 operands (the fused epilogues
-  // are used with bf16 operands only)
-  if (epi != kEpiStore) return hipErrorInvalidValue;
-  k_gemm_i8<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea);
+  switch (epi) {
+    case kEpiStore: k_gemm_i8<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiGatedResid: k_gemm_i8<kEpiGatedResid><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiSwiGLU: k_gemm_i8<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

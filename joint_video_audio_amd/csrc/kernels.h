@@ -69,7 +69,8 @@ struct EpiArgs {
   const float* col_scale;  // int8 kernel: per W row
 };
 // int8 operands (K % 128 == 0), int32 accumulation, dequantized with
-// ea.row_scale[m] * ea.col_scale[n]; plain store epilogue only (bf16 C).
+// ea.row_scale[m] * ea.col_scale[W row] ahead of the epilogue (store,
+// gated residual or SwiGLU, as with bf16 operands).
 hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* W, void* C, int M, int N, int K, const EpiArgs& ea,
                           hipStream_t st);
 template <typename T>

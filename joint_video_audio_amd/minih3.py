@@ -49,6 +49,11 @@ class _BlockWeights(ctypes.Structure):
                 ("adaln_table", _P)]
 
 
+class _BlockWeightsW8A8(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("q_qkv", "s_qkv", "q_out", "s_out", "q_gate_up", "s_gate_up", "q_down", "s_down",
+                                  "q_norm", "k_norm", "adaln_table")]
+
+
 TAP_FLOAT = ("adaln1", "q_rot", "k_rot", "v_t", "attn_o", "attn_proj", "x_mid", "adaln2", "ffn_h", "ffn_out")
 TAP_INT = ("table_row", "doc_id", "tile_flags", "num_pad")
 
@@ -129,9 +134,15 @@ def lib() -> ctypes.CDLL:
         L.minih3_output_heads.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), ctypes.POINTER(_Edges), _P,
                                           _P, _P, _P, ctypes.c_size_t, ctypes.c_uint32, _P]
         L.minih3_rotate_quantize.argtypes = [ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+        L.minih3_workspace_bytes_w8a8.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_block_forward_w8a8.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
+                                                ctypes.POINTER(_BlockWeightsW8A8), ctypes.c_int32, _P, _P, _P,
+                                                ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
         L.minih3_linear_w8a8.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
         for fn in ("minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
-                   "minih3_rotate_quantize", "minih3_linear_w8a8"):
+                   "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
+                   "minih3_block_forward_w8a8"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
                    "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
@@ -147,7 +158,8 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
             "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
             "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
-            "minih3_rotate_quantize", "minih3_linear_w8a8")
+            "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
+            "minih3_block_forward_w8a8")
 
 
 def status_string(s: int) -> str:
@@ -539,6 +551,60 @@ def linear_w8a8(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.
     _req(out, torch.bfloat16, "out", M * N)
     _check(lib().minih3_linear_w8a8(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(out), M, N, K, _stream()),
            "linear_w8a8")
+    return out
+
+
+class DeviceBlockW8A8:
+    """Weights of one block for the rotated W8A8 forward: int8 codes and fp32
+    row scales of the four matrices (from rotate_quantize), norms and table."""
+
+    NAMES = ("qkv", "out", "gate_up", "down")
+
+    def __init__(self, codes: dict, scales: dict, q_norm, k_norm, adaln_table):
+        self.codes, self.scales = codes, scales
+        self.q_norm, self.k_norm, self.adaln_table = q_norm, k_norm, adaln_table
+
+    @classmethod
+    def from_block(cls, b: DeviceBlock) -> "DeviceBlockW8A8":
+        codes, scales = {}, {}
+        for n, w in zip(cls.NAMES, (b.w_qkv, b.w_out, b.w_gate_up, b.w_down)):
+            codes[n], scales[n] = rotate_quantize(w)
+        return cls(codes, scales, b.q_norm, b.k_norm, b.adaln_table)
+
+    def c(self) -> _BlockWeightsW8A8:
+        ptrs = []
+        for n in self.NAMES:
+            ptrs += [_ptr(self.codes[n]), _ptr(self.scales[n])]
+        return _BlockWeightsW8A8(*ptrs, _ptr(self.q_norm), _ptr(self.k_norm), _ptr(self.adaln_table))
+
+
+def workspace_bytes_w8a8(cfg: Config, batch: int, seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().minih3_workspace_bytes_w8a8(ctypes.byref(cfg), batch, seq_len, ctypes.byref(n)),
+           "workspace_bytes_w8a8")
+    return int(n.value)
+
+
+def block_forward_w8a8(cfg: Config, layout: DeviceLayout, blocks: Sequence[DeviceBlockW8A8], x: torch.Tensor,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                       taps: Optional[dict] = None) -> torch.Tensor:
+    """x [B, S, D] bf16 -> out [B, S, D] through the blocks with rotated W8A8 projections."""
+    B, S, D = layout.batch, layout.seq_len, cfg.hidden
+    _req(x, torch.bfloat16, "x", B * S * D)
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, torch.bfloat16, "out", B * S * D)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes_w8a8(cfg, B, S), x.device)
+    arr = (_BlockWeightsW8A8 * len(blocks))(*[b.c() for b in blocks])
+    ct = None
+    if taps:
+        ct = _Taps(**{k: (ctypes.c_void_p(v.data_ptr()) if v is not None else None) for k, v in taps.items()})
+    L = layout.c()
+    s = lib().minih3_block_forward_w8a8(ctypes.byref(cfg), ctypes.byref(L), arr, len(blocks), _ptr(x), _ptr(out),
+                                        _ptr(workspace), workspace.numel(), flags,
+                                        ctypes.byref(ct) if ct is not None else None, _stream())
+    _check(s, "block_forward_w8a8")
     return out
 
 

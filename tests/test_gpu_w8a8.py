@@ -99,3 +99,67 @@ def test_linear_w8a8_full_qkv_shape_sampled_rows():
     rqw, rsw = ow.rotate_quantize(w.float().cpu().numpy())
     assert np.array_equal(qw.cpu().numpy(), rqw)
     check_linear(rqa, rsa, rqw, rsw, out[sel])
+
+
+# ---------------------------------------------------------------- the W8A8 block
+#
+# The block's W8A8 results are compared with the W8A8 oracle at relative L2
+# <= 1e-2 (the bf16 bar) and max-abs <= 0.1: the int8 codes of a projection
+# are decided by its bf16 input, and where the GPU's and the oracle's bf16
+# activations differ by one ulp (different summation orders upstream) a code
+# can move by one step, amax / 127 -- about eight times the ulp that caused
+# it -- so single output elements may differ by a few bf16 ulps where the
+# plain block's differ by one. The integer product itself is checked exactly
+# by the tests above.
+W8A8_BLOCK_MAX_ABS = 0.1
+
+def w8a8_block_case(dims, segs, grid, pads, seed, batch):
+    wl = synth.make_custom(dims, segs, grid, pads, seed=seed, batch=batch)
+    cfg, lay, blocks, x = dv.upload(wl)
+    qb = [m.DeviceBlockW8A8.from_block(b) for b in blocks]
+    out = m.block_forward_w8a8(cfg, lay, qb, x, flags=m.VALIDATE)
+    torch.cuda.synchronize()
+    return wl, x, out
+
+
+@pytest.mark.parametrize("pads", [0, 13])
+def test_block_w8a8_small(pads):
+    print(f"block w8a8 small pads={pads}", flush=True)
+    from oracle import weights_f64
+    from helpers import assert_close, to_np64
+    dims = synth.ModelDims(hidden=512, num_heads=4, head_dim=128, ffn_dim=768, num_tvals=8, dtype="bf16")
+    segs = [("text", 37), ("cond", 20, (1, 4, 5)), ("audio", 29), ("video", 105, (3, 5, 7))]
+    wl, x, out = w8a8_block_case(dims, segs, (3, 5, 7), pads, seed=pads, batch=2)
+    w = weights_f64(wl.blocks[0])
+    got = to_np64(out)
+    for b in range(2):
+        ref = ow.block_forward_w8a8(wl.x.values()[b], wl.layout, w, dims)
+        assert_close(got[b], ref, f"w8a8 block, item {b}", mabs=W8A8_BLOCK_MAX_ABS)
+    # padding rows leave the block bit for bit
+    pad = wl.layout.token_tags == -1
+    assert np.array_equal(got[:, pad], wl.x.values()[:, pad])
+
+
+def test_block_w8a8_gate_zero_is_identity():
+    dims = synth.ModelDims(hidden=512, num_heads=4, head_dim=128, ffn_dim=768, num_tvals=8, dtype="bf16")
+    wl = synth.make_custom(dims, [("text", 40), ("video", 90, (2, 5, 9))], (2, 5, 9), 6, seed=3)
+    wl.blocks[0].adaln_table[:, :, 2] = 0.0
+    wl.blocks[0].adaln_table[:, :, 5] = 0.0
+    cfg, lay, blocks, x = dv.upload(wl)
+    qb = [m.DeviceBlockW8A8.from_block(b) for b in blocks]
+    out = m.block_forward_w8a8(cfg, lay, qb, x)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x)
+
+
+def test_block_w8a8_full_width():
+    # the clip-scale block's widths (hidden 5376, 56 x 128 heads, FFN 14336) on 300 rows
+    print("block w8a8 full width", flush=True)
+    from oracle import weights_f64
+    from helpers import assert_close, to_np64
+    dims = synth.ModelDims(num_tvals=8)
+    segs = [("text", 40), ("audio", 36), ("video", 216, (2, 9, 12))]
+    wl, x, out = w8a8_block_case(dims, segs, (2, 9, 12), 8, seed=5, batch=1)
+    ref = ow.block_forward_w8a8(wl.x.values()[0], wl.layout, weights_f64(wl.blocks[0]), dims)
+    r, mx = assert_close(to_np64(out)[0], ref, "w8a8 block, full width", mabs=W8A8_BLOCK_MAX_ABS)
+    print(f"w8a8 block full width: rel_l2={r:.3e} max_abs={mx:.3e}", flush=True)
