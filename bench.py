@@ -268,6 +268,36 @@ def w8a8(reps: int, warmup: int, M: int = 32768):
     return res
 
 
+def w8a8_block(wl, cfg, lay, blocks, x, steps: int, warmup: int):
+    """The block forward with rotated W8A8 projections on the same workload
+    and inputs as the headline step (a separate variant: the headline step is
+    bf16). The weights are rotated and quantized once, outside the timing."""
+    import torch
+    from joint_video_audio_amd import minih3 as m
+    qb = [m.DeviceBlockW8A8.from_block(b) for b in blocks]
+    out = torch.empty_like(x)
+    ws = m.alloc_workspace(m.workspace_bytes_w8a8(cfg, lay.batch, lay.seq_len))
+    for _ in range(warmup):
+        m.block_forward_w8a8(cfg, lay, qb, x, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    m.profile_collect()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(steps):
+        m.block_forward_w8a8(cfg, lay, qb, x, out=out, workspace=ws, flags=m.PROFILE)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps / len(blocks)
+    kern = {k: round(v[0] / max(v[1], 1), 4) for k, v in m.profile_collect().items() if v[1]}
+    gemm, attn = flop_counts(wl.dims, wl.layout)
+    return {"ms_per_block": round(ms, 4), "rows_per_s": round(lay.seq_len / (ms / 1e3), 1),
+            "tflops_equivalent": round((gemm + attn) / (ms / 1e3) / 1e12, 1), "steps": steps,
+            "kernel_avg_ms": kern,
+            "note": "projection times include rotating and quantizing their input rows"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +310,7 @@ def main():
     ap.add_argument("--no-table-build", action="store_true")
     ap.add_argument("--no-edges", action="store_true")
     ap.add_argument("--no-w8a8", action="store_true")
+    ap.add_argument("--no-w8a8-block", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -375,6 +406,8 @@ def main():
         res["table_build"] = table_build(wl, a.seed, reps=50, warmup=5)
     if not a.no_edges:
         res["edges"] = edges(wl, a.seed, reps=20, warmup=3)
+    if not a.no_w8a8_block and wl.dims.dtype == "bf16":
+        res["w8a8_block"] = w8a8_block(wl, cfg, lay, blocks, x, steps=10, warmup=2)
     if not a.no_w8a8 and a.workload == "clip32k":
         res["w8a8"] = w8a8(reps=10, warmup=2)
     if not a.no_cpu_baseline:
