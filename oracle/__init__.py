@@ -4,7 +4,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import it. It shares no code with the HIP path and the HIP
 path never imports it.
 """
-from . import block, conditioning, edges, layout, w8a8  # noqa: F401
+from . import block, conditioning, edges, layout, step, w8a8  # noqa: F401
 from .block import block_forward, chain_forward  # noqa: F401
 
 
