@@ -352,6 +352,43 @@ int minih3_block_forward_w8a8(const minih3_config* cfg, const minih3_layout* lay
 int minih3_linear_w8a8(const int8_t* qa, const float* sa, const int8_t* qw, const float* sw, void* c, int32_t M,
                        int32_t N, int32_t K, void* stream);
 
+/* ---- Denoising step around the blocks: unmerged LoRA, Euler update ----
+ * Page "HyperFlow for MiniMax-H3", header table: a PEFT LoRA (rank 256,
+ * alpha 256) on the attention and feed-forward layers; sampling on a fixed
+ * sigma grid (video shift 12, audio shift 3). Page
+ * "MiniMaxH3Transformer3DModel", `forward`: a scale may be applied to the
+ * LoRA layers; the model returns the velocities. The library takes the PEFT
+ * form y = x W^T + scale * (alpha / rank) * (x A^T) B^T (A [rank, in], B
+ * [out, rank]), and the Euler step of the flow x' = x + (sigma_next -
+ * sigma_now) * v. */
+
+/* packed [N, K + rank] = [W | B] for minih3_linear_lora (once per layer);
+ * dtype MINIH3_BF16 or MINIH3_F32; w [N, K], lora_b [N, rank]. */
+int minih3_lora_pack_weight(int32_t dtype, const void* w, const void* lora_b, void* packed, int32_t N, int32_t K,
+                            int32_t rank, void* stream);
+
+/* Bytes of workspace minih3_linear_lora needs. */
+int minih3_linear_lora_workspace_bytes(int32_t dtype, int32_t M, int32_t K, int32_t rank, size_t* bytes);
+
+/* c[M, N] = a W^T + lora_scale * (a A^T) B^T with lora_scale = scale *
+ * alpha / rank, the base weight left unmerged: t = a A^T (rounded to dtype),
+ * then one projection over [a | lora_scale * t] and packed = [W | B].
+ * a [M, K], lora_a [rank, K], packed [N, K + rank], c [M, N], all dtype.
+ * bf16: rank and N multiples of 256, K of 64; fp32: rank and N of 64, K of 16. */
+int minih3_linear_lora(int32_t dtype, const void* a, const void* lora_a, const void* packed, float lora_scale,
+                       void* c, int32_t M, int32_t N, int32_t K, int32_t rank, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* x_next[b, i] = x[b, i] + (sigma_next[v] - sigma_now[v]) * velocity[b, i]
+ * for the rows i < num_rows of one modality (x, velocity, x_next [batch,
+ * num_rows, channels] fp32, in the order of `indices`), v =
+ * timestep_indices[indices[i]] (indices clamped into range). Rows whose
+ * timestep value has sigma_next == sigma_now (conditioning rows, r = t)
+ * stay as they are. x_next may alias x. */
+int minih3_euler_step(const float* x, const float* velocity, float* x_next, int32_t batch, int32_t num_rows,
+                      int32_t channels, const int32_t* indices, const int32_t* timestep_indices, int32_t seq_len,
+                      const float* sigma_now, const float* sigma_next, int32_t num_tvals, void* stream);
+
 /* Kernel timing under MINIH3_PROFILE. Synchronises the recorded events,
  * writes for each kernel id k < n the summed milliseconds and the number of
  * launches since the last collect, then resets. Returns the number of

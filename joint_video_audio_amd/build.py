@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libminih3.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "layout.hip", "adaln.hip", "qknorm_rope.hip", "gemm.hip", "attention.hip", "conditioning.hip", "edges.hip", "quant.hip"]
+SOURCES = ["api.cpp", "layout.hip", "adaln.hip", "qknorm_rope.hip", "gemm.hip", "attention.hip", "conditioning.hip", "edges.hip", "quant.hip", "step.hip"]
 
 
 def hipcc() -> str:

@@ -871,6 +871,70 @@ int minih3_linear_w8a8(const int8_t* qa, const float* sa, const int8_t* qw, cons
   return MINIH3_OK;
 }
 
+int minih3_lora_pack_weight(int32_t dtype, const void* w, const void* lora_b, void* packed, int32_t N, int32_t K,
+                            int32_t rank, void* stream) {
+  if (!w || !lora_b || !packed || N < 1 || K < 1 || rank < 1) return MINIH3_E_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == MINIH3_BF16) {
+    if (K % 8 != 0 || rank % 8 != 0) return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_concat_rows<bf16_t>((const bf16_t*)w, (const bf16_t*)lora_b, 1.f, (bf16_t*)packed, N, K, rank,
+                                        st));
+  } else if (dtype == MINIH3_F32) {
+    if (K % 4 != 0 || rank % 4 != 0) return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_concat_rows<float>((const float*)w, (const float*)lora_b, 1.f, (float*)packed, N, K, rank, st));
+  } else {
+    return MINIH3_E_ARG;
+  }
+  return MINIH3_OK;
+}
+
+int minih3_linear_lora_workspace_bytes(int32_t dtype, int32_t M, int32_t K, int32_t rank, size_t* bytes) {
+  if (!bytes || M < 1 || K < 1 || rank < 1 || (dtype != MINIH3_BF16 && dtype != MINIH3_F32)) return MINIH3_E_ARG;
+  const size_t e = act_size(dtype);
+  *bytes = align_up((size_t)M * rank * e) + align_up((size_t)M * (K + rank) * e);
+  return MINIH3_OK;
+}
+
+int minih3_linear_lora(int32_t dtype, const void* a, const void* lora_a, const void* packed, float lora_scale,
+                       void* c, int32_t M, int32_t N, int32_t K, int32_t rank, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!a || !lora_a || !packed || !c || M < 1 || N < 1 || K < 1 || rank < 1) return MINIH3_E_ARG;
+  if (dtype != MINIH3_BF16 && dtype != MINIH3_F32) return MINIH3_E_ARG;
+  const size_t e = act_size(dtype);
+  const size_t tb = align_up((size_t)M * rank * e);
+  if (!workspace || workspace_bytes < tb + align_up((size_t)M * (K + rank) * e)) return MINIH3_E_WORKSPACE;
+  void* t = workspace;
+  void* xcat = (char*)workspace + tb;
+  hipStream_t st = (hipStream_t)stream;
+  EpiArgs ea{};
+  const int Kc = K + rank;
+  if (dtype == MINIH3_BF16) {
+    if (rank % 256 != 0 || N % 256 != 0 || K % 64 != 0 || !gemm_fits(M, rank, K) || !gemm_fits(M, N, Kc))
+      return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)a, (const bf16_t*)lora_a, t, M, rank, K, ea, st));
+    HIPCHECK(launch_concat_rows<bf16_t>((const bf16_t*)a, (const bf16_t*)t, lora_scale, (bf16_t*)xcat, M, K, rank,
+                                        st));
+    HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)xcat, (const bf16_t*)packed, c, M, N, Kc, ea, st));
+  } else {
+    if (rank % 64 != 0 || N % 64 != 0 || K % 16 != 0) return MINIH3_E_UNSUPPORTED;
+    HIPCHECK(launch_gemm<float>(kEpiStore, (const float*)a, (const float*)lora_a, t, M, rank, K, ea, st));
+    HIPCHECK(launch_concat_rows<float>((const float*)a, (const float*)t, lora_scale, (float*)xcat, M, K, rank, st));
+    HIPCHECK(launch_gemm<float>(kEpiStore, (const float*)xcat, (const float*)packed, c, M, N, Kc, ea, st));
+  }
+  return MINIH3_OK;
+}
+
+int minih3_euler_step(const float* x, const float* velocity, float* x_next, int32_t batch, int32_t num_rows,
+                      int32_t channels, const int32_t* indices, const int32_t* timestep_indices, int32_t seq_len,
+                      const float* sigma_now, const float* sigma_next, int32_t num_tvals, void* stream) {
+  if (batch < 1 || num_rows < 0 || channels < 1 || seq_len < 1 || num_tvals < 1) return MINIH3_E_ARG;
+  if (num_rows == 0) return MINIH3_OK;
+  if (!x || !velocity || !x_next || !indices || !timestep_indices || !sigma_now || !sigma_next) return MINIH3_E_ARG;
+  HIPCHECK(launch_euler(x, velocity, x_next, batch, num_rows, channels, indices, timestep_indices, seq_len, sigma_now,
+                        sigma_next, num_tvals, (hipStream_t)stream));
+  return MINIH3_OK;
+}
+
 int minih3_profile_collect(double* total_ms, int32_t* launches, int32_t n) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   for (int i = 0; i < n; ++i) {

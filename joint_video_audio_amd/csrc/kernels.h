@@ -168,4 +168,14 @@ hipError_t launch_edge_out(const T* x, const EdgeHeads& heads, int B, int S, int
 template <typename T>
 hipError_t launch_rot_quant(const T* x, int M, int K, int8_t* q, float* scale, hipStream_t st);
 
+// ---- denoising step: unmerged LoRA, Euler update ----
+// out[m] = [x[m, 0:K] | s * t[m, 0:R]] (rows of K + R), 16-byte pieces.
+template <typename T>
+hipError_t launch_concat_rows(const T* x, const T* t, float s, T* out, long M, int K, int R, hipStream_t st);
+// x_next[b, i] = x[b, i] + (sig_next[v] - sig_now[v]) * vel[b, i], v =
+// tidx[idx[i]] (indices clamped); x_next may alias x.
+hipError_t launch_euler(const float* x, const float* vel, float* x_next, int B, int nrows, int C,
+                        const int32_t* idx, const int32_t* tidx, int S, const float* sig_now, const float* sig_next,
+                        int ntv, hipStream_t st);
+
 }  // namespace minih3

@@ -140,9 +140,21 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(_BlockWeightsW8A8), ctypes.c_int32, _P, _P, _P,
                                                 ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
         L.minih3_linear_w8a8.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
+        L.minih3_lora_pack_weight.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, _P]
+        L.minih3_linear_lora_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                         ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_linear_lora.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_float, _P, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]
+        L.minih3_euler_step.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                        ctypes.c_int32, _P, _P, ctypes.c_int32, _P]
+        for fn in ("minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes", "minih3_linear_lora",
+                   "minih3_euler_step"):
+            getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
                    "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
-                   "minih3_block_forward_w8a8"):
+                   "minih3_block_forward_w8a8", "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
+            "minih3_linear_lora", "minih3_euler_step"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
                    "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
@@ -159,7 +171,8 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
             "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
             "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
-            "minih3_block_forward_w8a8")
+            "minih3_block_forward_w8a8", "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
+            "minih3_linear_lora", "minih3_euler_step")
 
 
 def status_string(s: int) -> str:
@@ -605,6 +618,67 @@ def block_forward_w8a8(cfg: Config, layout: DeviceLayout, blocks: Sequence[Devic
                                         _ptr(workspace), workspace.numel(), flags,
                                         ctypes.byref(ct) if ct is not None else None, _stream())
     _check(s, "block_forward_w8a8")
+    return out
+
+
+def _dtc(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError("bf16 or fp32 expected")
+
+
+def lora_pack_weight(w: torch.Tensor, lora_b: torch.Tensor) -> torch.Tensor:
+    """[W | B]: w [N, K], lora_b [N, rank] -> [N, K + rank] (same dtype)."""
+    N, K = w.shape
+    r = lora_b.shape[1]
+    _req(w, w.dtype, "w")
+    _req(lora_b, w.dtype, "lora_b", N * r)
+    out = torch.empty(N, K + r, dtype=w.dtype, device=w.device)
+    _check(lib().minih3_lora_pack_weight(_dtc(w), _ptr(w), _ptr(lora_b), _ptr(out), N, K, r, _stream()),
+           "lora_pack_weight")
+    return out
+
+
+def linear_lora(a: torch.Tensor, lora_a: torch.Tensor, packed: torch.Tensor, lora_scale: float,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[M, N] = a W^T + lora_scale (a A^T) B^T with packed = [W | B] (unmerged LoRA)."""
+    M, K = a.shape
+    r = lora_a.shape[0]
+    N = packed.shape[0]
+    dt = a.dtype
+    _req(a, dt, "a")
+    _req(lora_a, dt, "lora_a", r * K)
+    _req(packed, dt, "packed", N * (K + r))
+    if out is None:
+        out = torch.empty(M, N, dtype=dt, device=a.device)
+    _req(out, dt, "out", M * N)
+    if workspace is None:
+        nb = ctypes.c_size_t(0)
+        _check(lib().minih3_linear_lora_workspace_bytes(_dtc(a), M, K, r, ctypes.byref(nb)), "linear_lora")
+        workspace = alloc_workspace(int(nb.value), a.device)
+    _check(lib().minih3_linear_lora(_dtc(a), _ptr(a), _ptr(lora_a), _ptr(packed), float(lora_scale), _ptr(out), M, N,
+                                    K, r, _ptr(workspace), workspace.numel(), _stream()), "linear_lora")
+    return out
+
+
+def euler_step(x: torch.Tensor, velocity: torch.Tensor, indices: torch.Tensor, timestep_indices: torch.Tensor,
+               sigma_now: torch.Tensor, sigma_next: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x, velocity [B, n, C] fp32 (rows in the order of indices) -> x + (sigma_next - sigma_now)[row] * velocity."""
+    B, n, C = x.shape
+    _req(x, torch.float32, "x")
+    _req(velocity, torch.float32, "velocity", B * n * C)
+    _req(indices, torch.int32, "indices", n)
+    _req(timestep_indices, torch.int32, "timestep_indices")
+    _req(sigma_now, torch.float32, "sigma_now")
+    _req(sigma_next, torch.float32, "sigma_next", sigma_now.numel())
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, torch.float32, "out", B * n * C)
+    _check(lib().minih3_euler_step(_ptr(x), _ptr(velocity), _ptr(out), B, n, C, _ptr(indices),
+                                   _ptr(timestep_indices), timestep_indices.numel(), _ptr(sigma_now),
+                                   _ptr(sigma_next), sigma_now.numel(), _stream()), "euler_step")
     return out
 
 
