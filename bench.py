@@ -298,6 +298,52 @@ def w8a8_block(wl, cfg, lay, blocks, x, steps: int, warmup: int):
             "note": "projection times include rotating and quantizing their input rows"}
 
 
+def lora(reps: int, warmup: int, M: int = 32768, rank: int = 256):
+    """Time the unmerged LoRA projection (rank 256) on the block's four
+    projection shapes beside the plain projection: the low-rank part is
+    rank / K more work plus building [x | s x A^T]."""
+    import torch
+    from joint_video_audio_amd import minih3 as m
+    shapes = {"qkv": (21504, 5376), "out": (5376, 7168), "gate_up": (28672, 5376), "down": (5376, 14336)}
+    g = torch.Generator(device="cuda").manual_seed(1)
+    res = {}
+    tot_l = tot_p = 0.0
+    for name, (N, K) in shapes.items():
+        a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        la = (torch.randn(rank, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        lb = (torch.randn(N, rank, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        packed = m.lora_pack_weight(w, lb)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        ws = m.alloc_workspace((M * rank + M * (K + rank)) * 2 + 1024)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        t_l = timed(lambda: m.linear_lora(a, la, packed, 1.0, out=out, workspace=ws))
+        t_p = timed(lambda: m.linear(a, w, out=out))
+        res[name] = {"N": N, "K": K, "lora_ms": round(t_l, 4), "plain_ms": round(t_p, 4),
+                     "overhead": round(t_l / t_p - 1.0, 4)}
+        tot_l += t_l
+        tot_p += t_p
+        del a, w, la, lb, packed, out, ws
+    res["rank"] = rank
+    res["rows"] = M
+    res["total_lora_ms"] = round(tot_l, 4)
+    res["total_plain_ms"] = round(tot_p, 4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +357,7 @@ def main():
     ap.add_argument("--no-edges", action="store_true")
     ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--no-w8a8-block", action="store_true")
+    ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -410,6 +457,8 @@ def main():
         res["w8a8_block"] = w8a8_block(wl, cfg, lay, blocks, x, steps=10, warmup=2)
     if not a.no_w8a8 and a.workload == "clip32k":
         res["w8a8"] = w8a8(reps=10, warmup=2)
+    if not a.no_lora and a.workload == "clip32k":
+        res["lora"] = lora(reps=5, warmup=1)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)
