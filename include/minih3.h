@@ -389,6 +389,35 @@ int minih3_euler_step(const float* x, const float* velocity, float* x_next, int3
                       int32_t channels, const int32_t* indices, const int32_t* timestep_indices, int32_t seq_len,
                       const float* sigma_now, const float* sigma_next, int32_t num_tvals, void* stream);
 
+/* One denoising step of the model on the packed layout: the input
+ * projections build x from the video / audio latents and the embedded text
+ * rows (minih3_embed_inputs), the block chain runs on it
+ * (minih3_block_forward, or minih3_block_forward_w8a8 when qblocks is set),
+ * the heads give the velocities (minih3_output_heads), and the Euler update
+ * moves the latents in place (minih3_euler_step with sigma_now /
+ * sigma_next, the pair of each row's timestep value; conditioning rows carry
+ * r = t and stay). The AdaLN tables inside the block weights are built by
+ * the caller for this step's timestep values (minih3_time_embed,
+ * minih3_adaln_table). video [B, num_video, video_channels] and audio
+ * [B, num_audio, audio_channels] fp32 are read and overwritten; text
+ * [B, num_text, D] act. */
+typedef struct {
+  int32_t num_blocks;
+  const minih3_block_weights* blocks;        /* bf16 / fp32 blocks, or NULL  */
+  const minih3_block_weights_w8a8* qblocks;  /* W8A8 blocks (bf16 only), or NULL; exactly one of the two */
+  const minih3_edges* edges;
+  const float* sigma_now;                    /* [num_tvals] */
+  const float* sigma_next;                   /* [num_tvals] */
+} minih3_step_weights;
+
+/* Bytes of workspace minih3_denoise_step needs. */
+int minih3_denoise_step_workspace_bytes(const minih3_config* cfg, const minih3_step_weights* weights, int32_t batch,
+                                        int32_t seq_len, int32_t num_video, int32_t num_audio, size_t* bytes);
+
+int minih3_denoise_step(const minih3_config* cfg, const minih3_layout* layout, const minih3_step_weights* weights,
+                        float* video, float* audio, const void* text, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream);
+
 /* Kernel timing under MINIH3_PROFILE. Synchronises the recorded events,
  * writes for each kernel id k < n the summed milliseconds and the number of
  * launches since the last collect, then resets. Returns the number of

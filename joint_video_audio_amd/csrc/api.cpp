@@ -539,6 +539,42 @@ int block_forward(const minih3_config* c, const minih3_layout* L, const minih3_b
   return run_blocks<float>(c, L, blocks, num_blocks, (const float*)x_in, (float*)x_out, w, flags, taps, st);
 }
 
+// Workspace of a denoising step: the packed sequence twice (input and
+// output of the chain), the velocities, the edges' and the chain's workspaces.
+struct StepWorkspace {
+  char *x0, *x1, *vel_v, *vel_a, *edges, *blocks;
+  size_t edges_bytes, blocks_bytes, total;
+};
+
+int carve_step(const minih3_config* c, const minih3_step_weights* sw, int B, int S, int nv, int na, char* base,
+               StepWorkspace& w) {
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t o = off;
+    off += align_up(n);
+    return base ? base + o : nullptr;
+  };
+  const size_t xb = (size_t)B * S * c->hidden * act_size(c->act_dtype);
+  w.x0 = take(xb);
+  w.x1 = take(xb);
+  w.vel_v = take((size_t)B * nv * sw->edges->video_channels * 4);
+  w.vel_a = take((size_t)B * na * sw->edges->audio_channels * 4);
+  w.edges_bytes = carve_edges(c, sw->edges, S, nullptr).total;
+  w.edges = take(w.edges_bytes);
+  w.blocks_bytes = carve(c, B, S, nullptr, sw->qblocks != nullptr).total;
+  w.blocks = take(w.blocks_bytes);
+  w.total = off;
+  return MINIH3_OK;
+}
+
+int check_step(const minih3_config* c, const minih3_step_weights* sw) {
+  if (!c || !sw || !sw->edges || !sw->sigma_now || !sw->sigma_next || sw->num_blocks < 1) return MINIH3_E_ARG;
+  if ((sw->blocks == nullptr) == (sw->qblocks == nullptr)) return MINIH3_E_ARG;
+  int s = check_config(c);
+  if (s) return s;
+  return check_edges(c, sw->edges);
+}
+
 }  // namespace
 
 extern "C" {
@@ -932,6 +968,45 @@ int minih3_euler_step(const float* x, const float* velocity, float* x_next, int3
   if (!x || !velocity || !x_next || !indices || !timestep_indices || !sigma_now || !sigma_next) return MINIH3_E_ARG;
   HIPCHECK(launch_euler(x, velocity, x_next, batch, num_rows, channels, indices, timestep_indices, seq_len, sigma_now,
                         sigma_next, num_tvals, (hipStream_t)stream));
+  return MINIH3_OK;
+}
+
+int minih3_denoise_step_workspace_bytes(const minih3_config* c, const minih3_step_weights* sw, int32_t batch,
+                                        int32_t seq_len, int32_t num_video, int32_t num_audio, size_t* bytes) {
+  int s = check_step(c, sw);
+  if (s) return s;
+  if (!bytes || batch < 1 || seq_len < 1 || num_video < 0 || num_audio < 0) return MINIH3_E_ARG;
+  StepWorkspace w{};
+  carve_step(c, sw, batch, seq_len, num_video, num_audio, nullptr, w);
+  *bytes = w.total;
+  return MINIH3_OK;
+}
+
+int minih3_denoise_step(const minih3_config* c, const minih3_layout* L, const minih3_step_weights* sw, float* video,
+                        float* audio, const void* text, void* workspace, size_t workspace_bytes, uint32_t flags,
+                        void* stream) {
+  int s = check_step(c, sw);
+  if (s) return s;
+  s = check_layout(L, true);
+  if (s) return s;
+  if ((L->num_video && !video) || (L->num_audio && !audio) || (L->num_text && !text)) return MINIH3_E_ARG;
+  StepWorkspace w{};
+  carve_step(c, sw, L->batch, L->seq_len, L->num_video, L->num_audio, (char*)workspace, w);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  s = minih3_embed_inputs(c, L, sw->edges, video, audio, text, w.x0, w.edges, w.edges_bytes, flags, stream);
+  if (s) return s;
+  const uint32_t bflags = flags & ~(uint32_t)MINIH3_VALIDATE;  // validated once above
+  s = block_forward(c, L, sw->blocks, sw->qblocks, sw->num_blocks, w.x0, w.x1, w.blocks, w.blocks_bytes, bflags,
+                    nullptr, stream);
+  if (s) return s;
+  s = minih3_output_heads(c, L, sw->edges, w.x1, (float*)w.vel_v, (float*)w.vel_a, w.edges, w.edges_bytes, 0, stream);
+  if (s) return s;
+  const int B = L->batch, S = L->seq_len;
+  HIPCHECK(launch_euler(video, (const float*)w.vel_v, video, B, L->num_video, sw->edges->video_channels,
+                        L->video_indices, L->timestep_indices, S, sw->sigma_now, sw->sigma_next, c->num_tvals, st));
+  HIPCHECK(launch_euler(audio, (const float*)w.vel_a, audio, B, L->num_audio, sw->edges->audio_channels,
+                        L->audio_indices, L->timestep_indices, S, sw->sigma_now, sw->sigma_next, c->num_tvals, st));
   return MINIH3_OK;
 }
 

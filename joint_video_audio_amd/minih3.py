@@ -54,6 +54,11 @@ class _BlockWeightsW8A8(ctypes.Structure):
                                   "q_norm", "k_norm", "adaln_table")]
 
 
+class _StepWeights(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("blocks", _P), ("qblocks", _P), ("edges", _P), ("sigma_now", _P),
+                ("sigma_next", _P)]
+
+
 TAP_FLOAT = ("adaln1", "q_rot", "k_rot", "v_t", "attn_o", "attn_proj", "x_mid", "adaln2", "ffn_h", "ffn_out")
 TAP_INT = ("table_row", "doc_id", "tile_flags", "num_pad")
 
@@ -148,13 +153,18 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]
         L.minih3_euler_step.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                         ctypes.c_int32, _P, _P, ctypes.c_int32, _P]
+        L.minih3_denoise_step_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_StepWeights),
+                                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_denoise_step.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
+                                          ctypes.POINTER(_StepWeights), _P, _P, _P, _P, ctypes.c_size_t,
+                                          ctypes.c_uint32, _P]
         for fn in ("minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes", "minih3_linear_lora",
-                   "minih3_euler_step"):
+                   "minih3_euler_step", "minih3_denoise_step_workspace_bytes", "minih3_denoise_step"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
                    "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
-                   "minih3_block_forward_w8a8", "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
-            "minih3_linear_lora", "minih3_euler_step"):
+                   "minih3_block_forward_w8a8"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
                    "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
@@ -172,7 +182,8 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
             "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
             "minih3_block_forward_w8a8", "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
-            "minih3_linear_lora", "minih3_euler_step")
+            "minih3_linear_lora", "minih3_euler_step", "minih3_denoise_step_workspace_bytes",
+            "minih3_denoise_step")
 
 
 def status_string(s: int) -> str:
@@ -680,6 +691,41 @@ def euler_step(x: torch.Tensor, velocity: torch.Tensor, indices: torch.Tensor, t
                                    _ptr(timestep_indices), timestep_indices.numel(), _ptr(sigma_now),
                                    _ptr(sigma_next), sigma_now.numel(), _stream()), "euler_step")
     return out
+
+
+def denoise_step(cfg: Config, layout: DeviceLayout, blocks, edges: DeviceEdges, sigma_now: torch.Tensor,
+                 sigma_next: torch.Tensor, video: torch.Tensor, audio: torch.Tensor, text: torch.Tensor,
+                 flags: int = 0, workspace: Optional[torch.Tensor] = None):
+    """One denoising step: video [B, n_video, Cv] and audio [B, n_audio, Ca] fp32 latents are updated in place
+    (input projections, the block chain -- DeviceBlock or DeviceBlockW8A8 list --, heads, Euler update)."""
+    B, S = layout.batch, layout.seq_len
+    nv, na = layout.video_indices.numel(), layout.audio_indices.numel()
+    edges.check(cfg)
+    _req(video, torch.float32, "video", B * nv * edges.video_channels)
+    _req(audio, torch.float32, "audio", B * na * edges.audio_channels)
+    _req(text, act_torch_dtype(cfg), "text", B * layout.text_indices.numel() * cfg.hidden)
+    _req(sigma_now, torch.float32, "sigma_now", cfg.num_tvals)
+    _req(sigma_next, torch.float32, "sigma_next", cfg.num_tvals)
+    w8 = isinstance(blocks[0], DeviceBlockW8A8)
+    if w8:
+        arr = (_BlockWeightsW8A8 * len(blocks))(*[b.c() for b in blocks])
+    else:
+        for b in blocks:
+            b.check(cfg)
+        arr = (_BlockWeights * len(blocks))(*[b.c() for b in blocks])
+    ce = edges.c()
+    sw = _StepWeights(len(blocks), None if w8 else ctypes.cast(arr, _P), ctypes.cast(arr, _P) if w8 else None,
+                      ctypes.cast(ctypes.pointer(ce), _P), _ptr(sigma_now), _ptr(sigma_next))
+    if workspace is None:
+        nb = ctypes.c_size_t(0)
+        _check(lib().minih3_denoise_step_workspace_bytes(ctypes.byref(cfg), ctypes.byref(sw), B, S, nv, na,
+                                                         ctypes.byref(nb)), "denoise_step_workspace_bytes")
+        workspace = alloc_workspace(int(nb.value), video.device)
+    L = layout.c()
+    _check(lib().minih3_denoise_step(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(sw), _ptr(video), _ptr(audio),
+                                     _ptr(text), _ptr(workspace), workspace.numel(), flags, _stream()),
+           "denoise_step")
+    return video, audio
 
 
 def profile_collect() -> dict:

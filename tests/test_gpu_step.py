@@ -105,3 +105,57 @@ def test_euler_step_matches_and_keeps_pinned_rows():
     m.euler_step(xi, cu(vel), idx, tidx, cu(now), cu(nxt), out=xi)
     torch.cuda.synchronize()
     assert torch.equal(xi, got)
+
+
+# ---------------------------------------------------------------- a whole denoising step
+
+@pytest.mark.parametrize("mode", ["f32", "bf16", "w8a8"])
+def test_denoise_step(mode):
+    # input projections -> two blocks -> heads -> Euler update, against the
+    # oracle's composition of the same steps (bf16 storage of the packed
+    # sequence after the input projections and after the chain, as the
+    # library stores them)
+    print(f"denoise step {mode}", flush=True)
+    from oracle import block as ob
+    from oracle import edges as oe
+    from oracle import w8a8 as ow
+    from oracle import weights_f64
+    dtype = "f32" if mode == "f32" else "bf16"
+    dims = synth.ModelDims(hidden=512, num_heads=4, head_dim=128, ffn_dim=768, num_tvals=16, dtype=dtype)
+    segs = [("text", 23), ("cond", 12, (1, 3, 4)), ("audio", 17), ("video", 60, (2, 5, 6))]
+    wl = synth.make_custom(dims, segs, (2, 5, 6), 5, seed=8, batch=2, num_blocks=2)
+    L = wl.layout
+    e = synth.make_edges(dims, L, batch=2, seed=9)
+    k = 4
+    grid = (1.0 - np.arange(k) / k).astype(np.float32)
+    now, nxt = grid[np.arange(16) // k], grid[np.arange(16) % k]
+    cfg, lay, blocks, _ = dv.upload(wl)
+    if mode == "w8a8":
+        blocks = [m.DeviceBlockW8A8.from_block(b) for b in blocks]
+    video, audio = dv.f32(e.video), dv.f32(e.audio)
+    m.denoise_step(cfg, lay, blocks, dv.edges_for(e), dv.f32(now), dv.f32(nxt), video, audio, dv.to_device(e.text),
+                   flags=m.VALIDATE)
+    torch.cuda.synchronize()
+
+    store = (lambda a: a) if dtype == "f32" else ow.round_bf16
+    x = store(oe.embed_inputs(e.video, e.audio, e.text.values(), L, e.w_in, e.b_in, e.w_ain, e.b_ain, dims.hidden))
+    ws = [weights_f64(b) for b in wl.blocks]
+    for bi in range(2):
+        for i, w in enumerate(ws):
+            x[bi] = ow.block_forward_w8a8(x[bi], L, w, dims) if mode == "w8a8" else ob.block_forward(x[bi], L, w, dims)
+    x = store(x)
+    v, a = oe.output_heads(x, L, e.gamma, e.beta, e.final_norm_eps, e.w_out, e.b_out, e.w_aout, e.b_aout)
+    tv, ta = L.timestep_indices[L.video_indices], L.timestep_indices[L.audio_indices]
+    ref_v = ostep.euler_step(e.video, v, np.broadcast_to(now[tv], (2, len(tv))), np.broadcast_to(nxt[tv], (2, len(tv))))
+    ref_a = ostep.euler_step(e.audio, a, np.broadcast_to(now[ta], (2, len(ta))), np.broadcast_to(nxt[ta], (2, len(ta))))
+    # compare the updates (x' - x): they carry all of the step's arithmetic
+    for got, ref, x0, name in ((video, ref_v, e.video, "video"), (audio, ref_a, e.audio, "audio")):
+        d_got = to_np64(got) - x0.astype(np.float64)
+        d_ref = ref - x0.astype(np.float64)
+        if mode == "f32":
+            assert rel_l2(d_got, d_ref) <= REL_L2_F32, name
+        else:
+            assert_close(d_got, d_ref, f"step update {name}", mabs=0.1 if mode == "w8a8" else 5e-2)
+    # rows whose timestep value has r = t (the grid's diagonal) stay put
+    keep = now[tv] == nxt[tv]
+    assert keep.any() and np.array_equal(video.cpu().numpy()[:, keep], e.video[:, keep])
