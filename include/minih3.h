@@ -367,12 +367,13 @@ int minih3_linear_w8a8(const int8_t* qa, const float* sa, const int8_t* qw, cons
 int minih3_lora_pack_weight(int32_t dtype, const void* w, const void* lora_b, void* packed, int32_t N, int32_t K,
                             int32_t rank, void* stream);
 
-/* Bytes of workspace minih3_linear_lora needs. */
+/* Bytes of workspace minih3_linear_lora needs (M x rank values of dtype). */
 int minih3_linear_lora_workspace_bytes(int32_t dtype, int32_t M, int32_t K, int32_t rank, size_t* bytes);
 
 /* c[M, N] = a W^T + lora_scale * (a A^T) B^T with lora_scale = scale *
- * alpha / rank, the base weight left unmerged: t = a A^T (rounded to dtype),
- * then one projection over [a | lora_scale * t] and packed = [W | B].
+ * alpha / rank, the base weight left unmerged: t = lora_scale * a A^T
+ * (rounded to dtype, kept in the workspace), then one projection over
+ * [a | t] and packed = [W | B], its A operand read from a and t in place.
  * a [M, K], lora_a [rank, K], packed [N, K + rank], c [M, N], all dtype.
  * bf16: rank and N multiples of 256, K of 64; fp32: rank and N of 64, K of 16. */
 int minih3_linear_lora(int32_t dtype, const void* a, const void* lora_a, const void* packed, float lora_scale,

@@ -926,8 +926,7 @@ int minih3_lora_pack_weight(int32_t dtype, const void* w, const void* lora_b, vo
 
 int minih3_linear_lora_workspace_bytes(int32_t dtype, int32_t M, int32_t K, int32_t rank, size_t* bytes) {
   if (!bytes || M < 1 || K < 1 || rank < 1 || (dtype != MINIH3_BF16 && dtype != MINIH3_F32)) return MINIH3_E_ARG;
-  const size_t e = act_size(dtype);
-  *bytes = align_up((size_t)M * rank * e) + align_up((size_t)M * (K + rank) * e);
+  *bytes = align_up((size_t)M * rank * act_size(dtype));  // t
   return MINIH3_OK;
 }
 
@@ -936,26 +935,26 @@ int minih3_linear_lora(int32_t dtype, const void* a, const void* lora_a, const v
                        size_t workspace_bytes, void* stream) {
   if (!a || !lora_a || !packed || !c || M < 1 || N < 1 || K < 1 || rank < 1) return MINIH3_E_ARG;
   if (dtype != MINIH3_BF16 && dtype != MINIH3_F32) return MINIH3_E_ARG;
-  const size_t e = act_size(dtype);
-  const size_t tb = align_up((size_t)M * rank * e);
-  if (!workspace || workspace_bytes < tb + align_up((size_t)M * (K + rank) * e)) return MINIH3_E_WORKSPACE;
+  if (!workspace || workspace_bytes < align_up((size_t)M * rank * act_size(dtype))) return MINIH3_E_WORKSPACE;
   void* t = workspace;
-  void* xcat = (char*)workspace + tb;
   hipStream_t st = (hipStream_t)stream;
-  EpiArgs ea{};
+  // t = lora_scale * a A^T (stored in dtype), then one projection whose A
+  // operand is [a | t] read from the two arrays, against packed = [W | B]
+  EpiArgs et{};
+  et.scale = lora_scale;
+  EpiArgs ec{};
+  ec.a2 = t;
+  ec.k2 = rank;
   const int Kc = K + rank;
   if (dtype == MINIH3_BF16) {
     if (rank % 256 != 0 || N % 256 != 0 || K % 64 != 0 || !gemm_fits(M, rank, K) || !gemm_fits(M, N, Kc))
       return MINIH3_E_UNSUPPORTED;
-    HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)a, (const bf16_t*)lora_a, t, M, rank, K, ea, st));
-    HIPCHECK(launch_concat_rows<bf16_t>((const bf16_t*)a, (const bf16_t*)t, lora_scale, (bf16_t*)xcat, M, K, rank,
-                                        st));
-    HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)xcat, (const bf16_t*)packed, c, M, N, Kc, ea, st));
+    HIPCHECK(launch_gemm<bf16_t>(kEpiStoreScaled, (const bf16_t*)a, (const bf16_t*)lora_a, t, M, rank, K, et, st));
+    HIPCHECK(launch_gemm<bf16_t>(kEpiStore, (const bf16_t*)a, (const bf16_t*)packed, c, M, N, Kc, ec, st));
   } else {
     if (rank % 64 != 0 || N % 64 != 0 || K % 16 != 0) return MINIH3_E_UNSUPPORTED;
-    HIPCHECK(launch_gemm<float>(kEpiStore, (const float*)a, (const float*)lora_a, t, M, rank, K, ea, st));
-    HIPCHECK(launch_concat_rows<float>((const float*)a, (const float*)t, lora_scale, (float*)xcat, M, K, rank, st));
-    HIPCHECK(launch_gemm<float>(kEpiStore, (const float*)xcat, (const float*)packed, c, M, N, Kc, ea, st));
+    HIPCHECK(launch_gemm<float>(kEpiStoreScaled, (const float*)a, (const float*)lora_a, t, M, rank, K, et, st));
+    HIPCHECK(launch_gemm<float>(kEpiStore, (const float*)a, (const float*)packed, c, M, N, Kc, ec, st));
   }
   return MINIH3_OK;
 }

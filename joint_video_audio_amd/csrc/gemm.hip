@@ -10,6 +10,10 @@
 //   kEpiGatedResid : C = resid + gate[row] * acc   (gate from the AdaLN table;
 //                    a padding row keeps resid unchanged)
 //   kEpiSwiGLU     : W rows [0,F) gate, [F,2F) up; C[:, f] = silu(g_f) * u_f
+//   kEpiStoreScaled: C = scale * acc
+// The store epilogue also takes its A operand split in two arrays along K
+// (EpiArgs::a2), so that [x | t] . [W | B]^T of an unmerged low-rank adapter
+// needs no concatenated copy of its rows.
 //
 // bf16 kernel (gfx950): 256x256 output tile per workgroup of 4 waves, one per
 // SIMD, each 128x128 as 8x8 v_mfma_f32_16x16x32_bf16 accumulators in AGPRs
@@ -135,7 +139,10 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // fragment reads are unchanged; a step covers 128 int8 columns instead of
 // 64 bf16 ones. The int32 accumulators are turned into fp32
 // acc * row_scale[m] * col_scale[W row] before the epilogue.
-template <int EPI, int I8>
+//
+// SPLIT: the K steps below K - k2 read A (row stride K - k2), the others
+// read ea.a2 (row stride k2); the LDS ring is filled the same way.
+template <int EPI, int I8, int SPLIT = 0>
 __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
                                           void* __restrict__ Cv, int M, int N, int K, const EpiArgs& ea) {
   constexpr int WTM = 128, WTN = 128, MI = WTM / 16, NI = WTN / 16;
@@ -165,7 +172,9 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   // ---- DMA byte offsets. Wave w fills rows 64 w .. 64 w + 63 of every slot:
   // instruction j covers rows 64 w + 8 j .. + 7 (1 KiB); lane L takes row
   // 64 w + 8 j + L / 8, logical chunk (L % 8) ^ swz(row).
-  uint32_t voff_a[kIPW], voff_w[kIPW];
+  const int K1 = SPLIT ? K - ea.k2 : K;  // row stride of A
+  const uint8_t* A2 = static_cast<const uint8_t*>(ea.a2);
+  uint32_t voff_a[kIPW], voff_w[kIPW], voff_a2[SPLIT ? kIPW : 1];
 #pragma unroll
   for (int j = 0; j < kIPW; ++j) {
     const int row = 64 * wid + 8 * j + lane / kCPR;
@@ -180,17 +189,25 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
     } else {
       wr = tn * BN + row;
     }
-    voff_a[j] = (uint32_t)((long)am * K * kEs + c * 16);
+    voff_a[j] = (uint32_t)((long)am * K1 * kEs + c * 16);
     voff_w[j] = (uint32_t)((long)wr * K * kEs + c * 16);
+    if constexpr (SPLIT) voff_a2[j] = (uint32_t)((long)am * ea.k2 * kEs + c * 16);
   }
   const int KT = K / (kRowBytes / kEs);
+  const int KT1 = K1 / (kRowBytes / kEs);  // K steps served by A
   auto slot_ptr = [&](int s) { return lds + s * kSlotBytes; };
   // DMA instruction j of operand A (or W) of K step k into its ring slot;
   // past the end of K the last step is loaded again (the slot is free).
   auto dma_a1 = [&](int k, int j) {
     const int s = (2 * k) % kSlots;
-    const uint32_t soff = (uint32_t)((k < KT ? k : KT - 1) * kRowBytes);
-    dma16(A, voff_a[j], soff, (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+    const int kc = k < KT ? k : KT - 1;
+    if constexpr (SPLIT) {
+      const bool second = kc >= KT1;
+      dma16(second ? A2 : A, second ? voff_a2[j] : voff_a[j], (uint32_t)((second ? kc - KT1 : kc) * kRowBytes),
+            (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+    } else {
+      dma16(A, voff_a[j], (uint32_t)(kc * kRowBytes), (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+    }
   };
   auto dma_w1 = [&](int k, int j) {
     const int s = (2 * k + 1) % kSlots;
@@ -418,7 +435,11 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
       for (int ni = 0; ni < NI; ++ni) {
         const int r = wm * WTM + mi * 16 + fr_row, c = wn * WTN + ni * 16 + 4 * fr_q;
         u32x2 pk;
-        const floatx4 a = deq(mi, ni);
+        floatx4 a = deq(mi, ni);
+        if constexpr (EPI == kEpiStoreScaled) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] *= ea.scale;
+        }
         pk[0] = pack_bf16x2(a[0], a[1]);
         pk[1] = pack_bf16x2(a[2], a[3]);
         *reinterpret_cast<u32x2*>(lds + r * RB + c * 2) = pk;
@@ -439,6 +460,13 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
     k_gemm_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
                 int K, EpiArgs ea) {
   gemm_body<EPI, 0>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea);
+}
+
+__global__ void __launch_bounds__(64 * kWaves, 1)
+    k_gemm_bf16_split(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
+                      int K, EpiArgs ea) {
+  gemm_body<kEpiStore, 0, 1>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K,
+                             ea);
 }
 
 template <int EPI>
@@ -463,12 +491,15 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
   const int tx = tid & 15, ty = tid >> 4;
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const int ldc = EPI == kEpiSwiGLU ? ea.ffn_dim : N;
+  const float* A2 = static_cast<const float*>(ea.a2);
+  const int K1 = A2 ? K - ea.k2 : K;  // row stride of A
   float acc[NB][4][4] = {};
   for (int k0 = 0; k0 < K; k0 += TK) {
     for (int e = tid; e < TM * TK; e += 256) {
       const int r = e / TK, c = e % TK;
       const int m = m0 + r < M ? m0 + r : M - 1;
-      As[c][r] = A[(long)m * K + k0 + c];
+      const int kk = k0 + c;
+      As[c][r] = kk < K1 ? A[(long)m * K1 + kk] : A2[(long)m * ea.k2 + (kk - K1)];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int wr = (EPI == kEpiSwiGLU ? b * ea.ffn_dim : 0) + n0 + r;
@@ -502,6 +533,9 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = EPI == kEpiSwiGLU ? silu(acc[0][i][j]) * acc[NB - 1][i][j] : acc[0][i][j];
+    if (EPI == kEpiStoreScaled)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] *= ea.scale;
     if (EPI == kEpiGatedResid)
       epi_gated<float>(C, ldc, m, n, v, ea);
     else
@@ -520,8 +554,14 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* 
   if ((unsigned long)M * K * 2 > 0xFFFFFFFFul || (unsigned long)N * K * 2 > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
+  if (ea.a2) {  // split A operand: store epilogue only, both parts whole K steps
+    if (epi != kEpiStore || ea.k2 <= 0 || ea.k2 >= K || ea.k2 % BK != 0) return hipErrorInvalidValue;
+    k_gemm_bf16_split<<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea);
+    return hipGetLastError();
+  }
   switch (epi) {
     case kEpiStore: k_gemm_bf16<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiStoreScaled: k_gemm_bf16<kEpiStoreScaled><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiGatedResid: k_gemm_bf16<kEpiGatedResid><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;
@@ -531,7 +571,7 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* 
 
 hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* W, void* C, int M, int N, int K, const EpiArgs& ea,
                           hipStream_t st) {
-  if (M <= 0 || N % BN != 0 || K % 128 != 0 || !ea.row_scale || !ea.col_scale) return hipErrorInvalidValue;
+  if (M <= 0 || N % BN != 0 || K % 128 != 0 || !ea.row_scale || !ea.col_scale || ea.a2) return hipErrorInvalidValue;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
   if ((unsigned long)M * K > 0xFFFFFFFFul || (unsigned long)N * K > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
@@ -552,9 +592,11 @@ hipError_t launch_gemm<float>(int epi, const float* A, const float* W, void* Cv,
   float* C = static_cast<float*>(Cv);
   const int ncols = epi == kEpiSwiGLU ? ea.ffn_dim : N;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 64 != 0)) return hipErrorInvalidValue;
+  if (ea.a2 && (epi != kEpiStore || ea.k2 <= 0 || ea.k2 >= K)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(ncols / 64), (unsigned)((M + 63) / 64));
   switch (epi) {
     case kEpiStore: k_gemm_f32<kEpiStore><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiStoreScaled: k_gemm_f32<kEpiStoreScaled><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiGatedResid: k_gemm_f32<kEpiGatedResid><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiSwiGLU: k_gemm_f32<kEpiSwiGLU><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;

@@ -54,7 +54,7 @@ hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, c
 hipError_t launch_zero_f32(float* p, int n, hipStream_t st);
 
 // ---- GEMM: C[M,N] = A[M,K] . W[N,K]^T with fused epilogues ----
-enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2 };
+enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2, kEpiStoreScaled = 3 };
 struct EpiArgs {
   const void* resid;     // [M, ldc] gated residual: fp32 if resid_f32 else act
   int resid_f32, out_f32;  // bf16 kernel only: precision of resid and of C (gated residual)
@@ -67,6 +67,13 @@ struct EpiArgs {
   int ffn_dim;           // SwiGLU: F (W rows [0,F) gate, [F,2F) up)
   const float* row_scale;  // int8 kernel: per A row
   const float* col_scale;  // int8 kernel: per W row
+  float scale;           // kEpiStoreScaled: C = scale * acc
+  // Split A operand (store epilogue, bf16 and fp32): columns [0, K - k2) of
+  // A come from A itself (row stride K - k2), columns [K - k2, K) from a2
+  // (row stride k2); null a2: A is one [M, K] array. bf16: K - k2 and k2
+  // multiples of 64.
+  const void* a2;
+  int k2;
 };
 // int8 operands (K % 128 == 0), int32 accumulation, dequantized with
 // ea.row_scale[m] * ea.col_scale[W row] ahead of the epilogue (store,

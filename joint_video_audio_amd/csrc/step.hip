@@ -9,8 +9,9 @@
 // Unmerged LoRA, y = x W^T + s (x A^T) B^T with s = scale * alpha / rank, is
 // one contraction over the concatenated inner dimension:
 // y = [x | s t] [W | B]^T with t = x A^T. The projection kernel runs it as
-// is (K + rank columns); [W | B] is packed once per layer, [x | s t] per call
-// by k_concat_rows. The low-rank part adds rank / K of the layer's work.
+// is (K + rank columns): [W | B] is packed once per layer by k_concat_rows,
+// and the kernel reads its A operand from x and s t in place (no per-call
+// copy). The low-rank part adds about 2 rank / K of the layer's work.
 #include "common.h"
 #include "kernels.h"
 

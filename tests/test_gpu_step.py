@@ -18,7 +18,7 @@ def bf16_pair(a):
     return dv.to_device(t), t.values()
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 512, 512), (257, 768, 1024)])
+@pytest.mark.parametrize("M,N,K", [(300, 512, 512), (257, 768, 1024), (65, 256, 64)])
 @pytest.mark.parametrize("scale", [1.0, 0.5])
 def test_linear_lora_bf16(M, N, K, scale):
     print(f"linear_lora bf16 M={M} N={N} K={K} scale={scale}", flush=True)
@@ -105,6 +105,34 @@ def test_euler_step_matches_and_keeps_pinned_rows():
     m.euler_step(xi, cu(vel), idx, tidx, cu(now), cu(nxt), out=xi)
     torch.cuda.synchronize()
     assert torch.equal(xi, got)
+
+
+def test_euler_step_two_schedules():
+    # video and audio latents follow their own sigma schedules (shift 12 and
+    # shift 3) in one call: the audio rows carry their own timestep values, so
+    # one pair of per-value sigma tables serves both
+    dims = synth.ModelDims(hidden=256, num_heads=2, ffn_dim=256, num_tvals=16, dtype="bf16")
+    wl = synth.make_custom(dims, [("text", 5), ("audio", 21), ("video", 48, (2, 4, 6))], (2, 4, 6), 0, seed=11)
+    L = wl.layout
+    tidx = L.timestep_indices.copy()
+    step = 3  # grid position of this step (of 8)
+    tidx[L.video_indices] = step
+    tidx[L.audio_indices] = 8 + step
+    grid = 1.0 - np.arange(9) / 8.0
+    now = np.concatenate([ostep.shift_sigmas(grid[:8], 12.0), ostep.shift_sigmas(grid[:8], 3.0)]).astype(np.float32)
+    nxt = np.concatenate([ostep.shift_sigmas(grid[1:], 12.0), ostep.shift_sigmas(grid[1:], 3.0)]).astype(np.float32)
+    rng = np.random.default_rng(12)
+    cu = lambda t: torch.from_numpy(np.ascontiguousarray(t)).cuda()  # noqa: E731
+    tid = cu(tidx.astype(np.int32))
+    for idx, C, shift in ((L.video_indices, 96, 12.0), (L.audio_indices, 32, 3.0)):
+        x = rng.standard_normal((1, len(idx), C)).astype(np.float32)
+        v = rng.standard_normal((1, len(idx), C)).astype(np.float32)
+        got = m.euler_step(cu(x), cu(v), cu(idx.astype(np.int32)), tid, cu(now), cu(nxt))
+        torch.cuda.synchronize()
+        sn = ostep.shift_sigmas(grid[step], shift)
+        sx = ostep.shift_sigmas(grid[step + 1], shift)
+        ref = ostep.euler_step(x, v, np.full((1, len(idx)), sn), np.full((1, len(idx)), sx))
+        assert np.abs(got.cpu().numpy().astype(np.float64) - ref).max() <= 1e-6 * np.abs(ref).max(), shift
 
 
 # ---------------------------------------------------------------- a whole denoising step
