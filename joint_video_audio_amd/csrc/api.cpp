@@ -123,6 +123,7 @@ int check_layout(const minih3_layout* L, bool need_indices) {
 
 struct Workspace {
   void *a, *qkvh, *qn, *kn, *vt, *o, *xmid, *xping;
+  float* rope;    // bf16: [S, 3 rope_freq_dim] (cos, sin) of every rotation pair of every row
   int8_t* qx;     // rotated W8A8: int8 codes of a projection's input rows
   float* sx;      // and their scales
   uint64_t* masks;
@@ -182,6 +183,7 @@ Workspace carve(const minih3_config* c, int B, int S, char* base, bool w8a8 = fa
   w.counts = (int32_t*)take(4 * (size_t)S);
   w.npad = (int32_t*)take(4);
   w.err = (uint32_t*)take(4);
+  if (c->act_dtype == MINIH3_BF16) w.rope = (float*)take((size_t)S * 3 * c->rope_freq_dim * 8);
   if (w8a8) {
     const size_t kmax = D > Wd ? (D > F ? D : F) : (Wd > F ? Wd : F);
     w.qx = (int8_t*)take(M * kmax);
@@ -221,9 +223,17 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
   const int padless = (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0;
   const size_t e = sizeof(T);
 
+  const int fd = c->rope_freq_dim;
   {
     Timed tm(prof, kKTiles, st);
     HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, w.masks, w.list_real, w.list_pad, w.meta, st));
+    if (sizeof(T) == 2) {
+      // bf16: the QKV projection normalizes and rotates q and k itself; the
+      // rotary table is built once per call, and the rows past S of the
+      // per-head buffers (never written by it) are cleared once
+      if (fd > 0) HIPCHECK(launch_rope_table(L->position_ids, w.rope, S, fd, c->rope_theta, st));
+      HIPCHECK(launch_qk_tail_zero((bf16_t*)w.qn, (bf16_t*)w.kn, (bf16_t*)w.vt, B * H, S, Sp, st));
+    }
   }
 
   T* a = (T*)w.a;
@@ -281,20 +291,34 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
                                c->norm_eps, c->num_tags, c->num_tvals, st));
     }
     if (tap && taps->adaln1) HIPCHECK(hipMemcpyAsync(taps->adaln1, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
-    {
+    if (sizeof(T) == 2) {
+      // q/k RMSNorm + RoPE, the key norms and the v transpose in the
+      // projection's epilogue
       Timed tm(prof, kKQKV, st);
-      HIPCHECK(proj(kEpiStore, a, 0, qkv, 3 * Wd, D, ea));
-    }
-    {
-      // bf16: the same pass records the key norms the attention kernel needs
-      Timed tm(prof, kKQKNormRope, st);
-      float* kmax = nullptr;
-      if (sizeof(T) == 2) {
-        kmax = static_cast<float*>(w.attn_scratch);
-        HIPCHECK(launch_zero_f32(kmax, 2 * B * H, st));
+      float* kmax = static_cast<float*>(w.attn_scratch);
+      HIPCHECK(launch_zero_f32(kmax, 2 * B * H, st));
+      EpiArgs eq = ea;
+      eq.q_out = qn;
+      eq.k_out = kn;
+      eq.vt_out = vt;
+      eq.q_norm = bw.q_norm;
+      eq.k_norm = bw.k_norm;
+      eq.rope = w.rope;
+      eq.rope_pairs = 3 * fd;
+      eq.heads = H;
+      eq.stride = Sp;
+      eq.qk_eps = c->qk_norm_eps;
+      eq.kmax = kmax;
+      eq.masks = w.masks;
+      HIPCHECK(proj(kEpiQKRope, a, 0, nullptr, 3 * Wd, D, eq));
+    } else {
+      {
+        Timed tm(prof, kKQKV, st);
+        HIPCHECK(proj(kEpiStore, a, 0, qkv, 3 * Wd, D, ea));
       }
+      Timed tm(prof, kKQKNormRope, st);
       HIPCHECK(launch_qk_norm_rope<T>(qkv, bw.q_norm, bw.k_norm, L->position_ids, qn, kn, vt, B, S, H, Sp,
-                                      c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st, w.masks, kmax));
+                                      c->rope_freq_dim, c->rope_theta, c->qk_norm_eps, st, nullptr, nullptr));
     }
     if (tap) {
       const size_t hb = (size_t)B * H * Sp * hd * e;

@@ -61,6 +61,42 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over the N lanes of a row (N = 16 or 32, aligned groups), result in
+// every lane of the row: DPP within 16 lanes, then one lane exchange across
+// the two 16-lane halves.
+template <int N>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(N == 16 || N == 32, "row width");
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  if (N == 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
+// Per-head RMSNorm and rotary turn of one lane's CPL channels of a head row
+// of CPL * LPR = 128 channels spread over LPR aligned lanes: v is scaled by
+// 1 / sqrt(mean(v^2) + eps) and the weights g, then channel pair p (2p,
+// 2p + 1) is turned by the angle whose cosine and sine are cs[p], sn[p]
+// (1 and 0 for a pair that is not rotated). The fused multiply-adds are
+// explicit so that every kernel that calls this rounds alike.
+template <int CPL, int LPR>
+__device__ __forceinline__ void qk_norm_rotate(float* v, const float* g, const float* cs, const float* sn,
+                                               float eps) {
+  static_assert(CPL * LPR == 128, "head width");
+  float sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) sq = __builtin_fmaf(v[e], v[e], sq);
+  const float r = rsqrtf(row_sum<LPR>(sq) * (1.f / 128) + eps);
+#pragma unroll
+  for (int p = 0; p < CPL / 2; ++p) {
+    const float a = v[2 * p] * r * g[2 * p], b = v[2 * p + 1] * r * g[2 * p + 1];
+    v[2 * p] = __builtin_fmaf(a, cs[p], -(b * sn[p]));
+    v[2 * p + 1] = __builtin_fmaf(a, sn[p], b * cs[p]);
+  }
+}
+
 // AdaLN table row of a packed row: tag * num_tvals + tidx, or -1 for a
 // padding row. Out-of-range values are clamped so that the table is never
 // read out of bounds (the layout is validated separately on request).

@@ -11,6 +11,9 @@
 //                    a padding row keeps resid unchanged)
 //   kEpiSwiGLU     : W rows [0,F) gate, [F,2F) up; C[:, f] = silu(g_f) * u_f
 //   kEpiStoreScaled: C = scale * acc
+//   kEpiQKRope     : the QKV projection's tile leaves in the attention
+//                    kernel's layouts: q and k per-head RMSNorm + rotary turn
+//                    (with the key norms), v transposed
 // The store epilogue also takes its A operand split in two arrays along K
 // (EpiArgs::a2), so that [x | t] . [W | B]^T of an unmerged low-rank adapter
 // needs no concatenated copy of its rows.
@@ -83,6 +86,161 @@ __device__ __forceinline__ void epi_gated(T* C, int ldc, int m, int n, const flo
     for (int j = 0; j < 4; ++j) r[j] += g[j] * acc[j];
   }
   store4<T>(C + (long)m * ldc + n, r);
+}
+
+// q/k/v epilogue of the QKV projection. The staged bf16 tile (256 rows x 256
+// columns: two heads of q, k or v) is read from LDS (row pitch RB bytes).
+// Page "MiniMaxH3Transformer3DModel", Parameters (per-head query/key norms
+// with qk_norm_eps; rotary frequencies on three axes). q and k: 16 lanes per
+// row (both of its heads), 8 channels each, normalized and turned exactly as
+// the standalone q/k pass does (same function, same table values); keys also
+// give their norms from the stored bf16 values. v: a thread owns 8 rows x 8
+// channels, transposed in registers, so that each channel leaves as 16
+// contiguous bytes of its v^T row.
+__device__ __forceinline__ void qkv_tile_epilogue(const uint8_t* lds, int RB, int m0, int n0, int M,
+                                                  const EpiArgs& ea) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int H = ea.heads, Wd = H * 128, S = ea.S;
+  const long stride = ea.stride;
+  const int part = n0 / Wd;               // 0 q, 1 k, 2 v
+  const int h0 = (n0 - part * Wd) / 128;  // the tile's first head
+  if (part < 2) {
+    // 16-lane group gi (of 16) owns rows gi + 16 k, k < 16, both heads of a
+    // row (one set of table values); the table values and document words of
+    // the next four rows are loaded while the current four are computed.
+    const int cl = lane & 15, gi = wid * 4 + (lane >> 4);
+    const float* gp = part == 0 ? ea.q_norm : ea.k_norm;
+    bf16_t* out = static_cast<bf16_t*>(part == 0 ? ea.q_out : ea.k_out);
+    const float2* rope = reinterpret_cast<const float2*>(ea.rope);
+    float g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = gp[cl * 8 + e];
+    const int np = ea.rope_pairs;
+    const bool norms = part == 1 && ea.kmax;
+    const int b0 = m0 / S;  // batch item of the tile's first row
+    float mx[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    constexpr int U = 4;
+    struct Pre {
+      float2 t[4];
+      uint64_t mk;
+    };
+    auto fetch = [&](int k, Pre& p) {
+      int m = m0 + gi + 16 * k;
+      m = m < M ? m : M - 1;  // rows past M load row M - 1 (never used)
+      const int s = m % S;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = cl * 4 + q;
+        p.t[q] = j < np ? rope[(long)s * np + j] : make_float2(1.f, 0.f);
+      }
+      p.mk = norms ? ea.masks[2 * (s / 64) + 1] : 0ull;
+    };
+    auto row = [&](int k, const Pre& p) {
+      const int rr = gi + 16 * k, m = m0 + rr;
+      if (m >= M) return;  // uniform over the 16 lanes of a row
+      const int b = m / S, s = m - b * S;
+      const int d = (int)((p.mk >> (s % 64)) & 1ull);
+      float cs[4], sn[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cs[q] = p.t[q].x;
+        sn[q] = p.t[q].y;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(lds + rr * RB + (hh * 128 + cl * 8) * 2);
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(raw[i] << 16);
+          v[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+        }
+        qk_norm_rotate<8, 16>(v, g, cs, sn, ea.qk_eps);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+        *reinterpret_cast<u32x4*>(out + (((long)b * H + h0 + hh) * stride + s) * 128 + cl * 8) = o;
+        if (norms) {
+          float n2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x0 = __uint_as_float(o[i] << 16), x1 = __uint_as_float(o[i] & 0xffff0000u);
+            n2 = __builtin_fmaf(x0, x0, n2);
+            n2 = __builtin_fmaf(x1, x1, n2);
+          }
+          n2 = row_sum<16>(n2);
+          if (b == b0)
+            mx[hh][d] = fmaxf(mx[hh][d], n2);
+          else if (cl == 0)  // rows of a second batch item in the tile: straight to memory
+            atomicMax(reinterpret_cast<int*>(ea.kmax + 2 * ((long)b * H + h0 + hh) + d),
+                      __float_as_int(sqrtf(n2)));
+        }
+      }
+    };
+    Pre cur[U], nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) fetch(u, cur[u]);
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += U) {
+      if (k0 + U < 16)
+#pragma unroll
+        for (int u = 0; u < U; ++u) fetch(k0 + U + u, nxt[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) row(k0 + u, cur[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    if (norms) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          float x = mx[hh][d];
+          x = fmaxf(x, __shfl_xor(x, 16, 64));
+          x = fmaxf(x, __shfl_xor(x, 32, 64));
+          // non-negative floats order as ints
+          if (lane == 0 && x > 0.f)
+            atomicMax(reinterpret_cast<int*>(ea.kmax + 2 * ((long)b0 * H + h0 + hh) + d), __float_as_int(sqrtf(x)));
+        }
+    }
+  } else {
+    bf16_t* vt = static_cast<bf16_t*>(ea.vt_out);
+    for (int blk = tid; blk < 1024; blk += 256) {
+      const int r0 = (blk & 31) * 8, c0 = (blk >> 5) * 8;  // 8 rows x 8 channels of the tile
+      u32x4 in[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) in[i] = *reinterpret_cast<const u32x4*>(lds + (r0 + i) * RB + c0 * 2);
+      // out[e]: channel c0 + e of rows r0 .. r0 + 7
+      u32x4 outv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = in[2 * w][e / 2], hi = in[2 * w + 1][e / 2];
+          outv[e][w] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+      const int hh = c0 / 128, d0 = c0 % 128;
+      const int mf = m0 + r0;
+      const int b = mf / S, s = mf - b * S;
+      if (mf + 7 < M && s + 7 < S && (s & 7) == 0) {
+        bf16_t* dst = vt + (((long)b * H + h0 + hh) * 128 + d0) * stride + s;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(dst + (long)e * stride) = outv[e];
+      } else {
+        for (int i = 0; i < 8; ++i) {
+          const int m = mf + i;
+          if (m >= M) break;
+          const int bi = m / S, si = m - bi * S;
+          bf16_t* dst = vt + (((long)bi * H + h0 + hh) * 128 + d0) * stride + si;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w = outv[e][i / 2];
+            reinterpret_cast<uint16_t*>(dst)[(long)e * stride] = (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu));
+          }
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
@@ -445,12 +603,16 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
         *reinterpret_cast<u32x2*>(lds + r * RB + c * 2) = pk;
       }
     __syncthreads();
-    // one row (512 bytes) per wave instruction: lane owns columns 4*lane .. +3
-    for (int rr = wid; rr < BM; rr += kWaves) {
-      const int m = m0 + rr;
-      if (m < M)
-        *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(Cv) + (long)m * N + tn * BN + 4 * lane) =
-            *reinterpret_cast<const u32x2*>(lds + rr * RB + lane * 8);
+    if constexpr (EPI == kEpiQKRope) {
+      qkv_tile_epilogue(lds, RB, m0, tn * BN, M, ea);
+    } else {
+      // one row (512 bytes) per wave instruction: lane owns columns 4*lane .. +3
+      for (int rr = wid; rr < BM; rr += kWaves) {
+        const int m = m0 + rr;
+        if (m < M)
+          *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(Cv) + (long)m * N + tn * BN + 4 * lane) =
+              *reinterpret_cast<const u32x2*>(lds + rr * RB + lane * 8);
+      }
     }
   }
 }
@@ -545,11 +707,22 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
 
 // ---------------------------------------------------------------- launchers
 
+// Shapes the q/k/v epilogue assumes: N = 3 heads 128 with an even head count
+// (a 256-column tile holds two heads of one of q, k, v), M whole batch items,
+// stride a multiple of 64 not below S, at most 64 rotation pairs.
+static bool qk_epi_ok(int M, int N, const EpiArgs& ea) {
+  return ea.heads > 0 && ea.heads % 2 == 0 && N == 3 * ea.heads * 128 && ea.S > 0 && M % ea.S == 0 &&
+         ea.stride >= ea.S && ea.stride % 64 == 0 && (ea.rope || ea.rope_pairs == 0) && ea.rope_pairs >= 0 &&
+         ea.rope_pairs <= 64 && ea.q_out && ea.k_out && ea.vt_out && ea.q_norm && ea.k_norm &&
+         (!ea.kmax || ea.masks);
+}
+
 template <>
 hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* C, int M, int N, int K,
                                const EpiArgs& ea, hipStream_t st) {
   if (M <= 0 || N % BN != 0 || K % BK != 0) return hipErrorInvalidValue;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
+  if (epi == kEpiQKRope && !qk_epi_ok(M, N, ea)) return hipErrorInvalidValue;
   // DMA offsets are 32-bit byte offsets into A and W
   if ((unsigned long)M * K * 2 > 0xFFFFFFFFul || (unsigned long)N * K * 2 > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
@@ -562,6 +735,7 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* 
   switch (epi) {
     case kEpiStore: k_gemm_bf16<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiStoreScaled: k_gemm_bf16<kEpiStoreScaled><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiQKRope: k_gemm_bf16<kEpiQKRope><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiGatedResid: k_gemm_bf16<kEpiGatedResid><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiSwiGLU: k_gemm_bf16<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;
@@ -573,11 +747,13 @@ hipError_t launch_gemm_i8(int epi, const int8_t* A, const int8_t* W, void* C, in
                           hipStream_t st) {
   if (M <= 0 || N % BN != 0 || K % 128 != 0 || !ea.row_scale || !ea.col_scale || ea.a2) return hipErrorInvalidValue;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 128 != 0)) return hipErrorInvalidValue;
+  if (epi == kEpiQKRope && !qk_epi_ok(M, N, ea)) return hipErrorInvalidValue;
   if ((unsigned long)M * K > 0xFFFFFFFFul || (unsigned long)N * K > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
   switch (epi) {
     case kEpiStore: k_gemm_i8<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+    case kEpiQKRope: k_gemm_i8<kEpiQKRope><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiGatedResid: k_gemm_i8<kEpiGatedResid><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     case kEpiSwiGLU: k_gemm_i8<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
     default: return hipErrorInvalidValue;

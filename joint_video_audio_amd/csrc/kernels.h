@@ -54,7 +54,7 @@ hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, c
 hipError_t launch_zero_f32(float* p, int n, hipStream_t st);
 
 // ---- GEMM: C[M,N] = A[M,K] . W[N,K]^T with fused epilogues ----
-enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2, kEpiStoreScaled = 3 };
+enum Epi { kEpiStore = 0, kEpiGatedResid = 1, kEpiSwiGLU = 2, kEpiStoreScaled = 3, kEpiQKRope = 4 };
 struct EpiArgs {
   const void* resid;     // [M, ldc] gated residual: fp32 if resid_f32 else act
   int resid_f32, out_f32;  // bf16 kernel only: precision of resid and of C (gated residual)
@@ -74,6 +74,20 @@ struct EpiArgs {
   // multiples of 64.
   const void* a2;
   int k2;
+  // kEpiQKRope (bf16 kernel, N = 3 heads 128, heads even): the QKV tile (two
+  // heads of q, k or v) leaves in the attention layouts: q and k per-head
+  // RMS-normalized with q_norm / k_norm and turned by the rope table, as
+  // [B, heads, stride, 128]; v transposed, [B, heads, 128, stride]. With kmax
+  // (zero on entry) the largest |k| of the stored keys per (b, head) and
+  // document (masks: [2t] real rows, [2t + 1] padding rows of 64-row tile t)
+  // is recorded at kmax[2 (b heads + h) + doc].
+  void *q_out, *k_out, *vt_out;
+  const float *q_norm, *k_norm;
+  const float* rope;  // [S, rope_pairs] (cos, sin), from launch_rope_table
+  int rope_pairs, heads, stride;
+  float qk_eps;
+  float* kmax;
+  const uint64_t* masks;
 };
 // int8 operands (K % 128 == 0), int32 accumulation, dequantized with
 // ea.row_scale[m] * ea.col_scale[W row] ahead of the epilogue (store,
@@ -177,6 +191,10 @@ hipError_t launch_rot_quant(const T* x, int M, int K, int8_t* q, float* scale, h
 
 // ---- denoising step: unmerged LoRA, Euler update ----
 // out[m] = [x[m, 0:K] | s * t[m, 0:R]] (rows of K + R), 16-byte pieces.
+// table [S, 3 fd] of (cos, sin) pairs: the rotary turn of each pair of each row
+hipError_t launch_rope_table(const int32_t* pos, float* table, int S, int fd, float theta, hipStream_t st);
+// zero rows / columns [S, stride) of the per-head q, k, v^T buffers (BH = B * heads)
+hipError_t launch_qk_tail_zero(bf16_t* qo, bf16_t* ko, bf16_t* vto, int BH, int S, int stride, hipStream_t st);
 template <typename T>
 hipError_t launch_concat_rows(const T* x, const T* t, float s, T* out, long M, int K, int R, hipStream_t st);
 // x_next[b, i] = x[b, i] + (sig_next[v] - sig_now[v]) * vel[b, i], v =

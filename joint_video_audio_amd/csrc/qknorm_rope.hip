@@ -62,20 +62,6 @@ template <> struct Chunk<float> {
   static __device__ __forceinline__ float stored(float x) { return x; }
 };
 
-// Sum over the N lanes of a row (N = 16 or 32, aligned groups), result in
-// every lane of the row: DPP within 16 lanes (quad xor 1, quad xor 2, half
-// mirror, mirror), then one lane exchange across the two 16-lane halves.
-template <int N>
-__device__ __forceinline__ float row_sum(float v) {
-  static_assert(N == 16 || N == 32, "row width");
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  if (N == 32) v += __shfl_xor(v, 16, 64);
-  return v;
-}
-
 template <typename T, int HG>
 __global__ void __launch_bounds__(256) k_qk_norm_rope(const T* __restrict__ qkv, const float* __restrict__ gq,
                                                       const float* __restrict__ gk, const int32_t* __restrict__ pos,
@@ -145,23 +131,8 @@ __global__ void __launch_bounds__(256) k_qk_norm_rope(const T* __restrict__ qkv,
 #pragma unroll
         for (int e = 0; e < CPL; ++e) q[e] = k[e] = 0.f;
       }
-      float sq = 0.f, sk = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) {
-        sq += q[e] * q[e];
-        sk += k[e] * k[e];
-      }
-      const float rq = rsqrtf(row_sum<LPR>(sq) * (1.f / HD) + eps);
-      const float rk = rsqrtf(row_sum<LPR>(sk) * (1.f / HD) + eps);
-#pragma unroll
-      for (int p = 0; p < PPL; ++p) {
-        const float q0 = q[2 * p] * rq * gqv[2 * p], q1 = q[2 * p + 1] * rq * gqv[2 * p + 1];
-        const float k0 = k[2 * p] * rk * gkv[2 * p], k1 = k[2 * p + 1] * rk * gkv[2 * p + 1];
-        q[2 * p] = q0 * cs[p] - q1 * sn[p];
-        q[2 * p + 1] = q0 * sn[p] + q1 * cs[p];
-        k[2 * p] = k0 * cs[p] - k1 * sn[p];
-        k[2 * p + 1] = k0 * sn[p] + k1 * cs[p];
-      }
+      qk_norm_rotate<CPL, LPR>(q, gqv, cs, sn, eps);
+      qk_norm_rotate<CPL, LPR>(k, gkv, cs, sn, eps);
       if (!live) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) q[e] = k[e] = 0.f;
@@ -171,7 +142,7 @@ __global__ void __launch_bounds__(256) k_qk_norm_rope(const T* __restrict__ qkv,
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           const float a = Chunk<T>::stored(k[e]);
-          n2 += a * a;
+          n2 = __builtin_fmaf(a, a, n2);
         }
         n2 = row_sum<LPR>(n2);
         const int d = (int)((mpad >> r) & 1ull);
@@ -256,6 +227,51 @@ hipError_t launch_qk_norm_rope(const T* qkv, const float* gq, const float* gk, c
     launch_heads<T, 2>(grid, qkv, gq, gk, pos, qo, ko, vto, masks, kmax, S, H, stride, fd, eps, fr, st);
   else
     launch_heads<T, 1>(grid, qkv, gq, gk, pos, qo, ko, vto, masks, kmax, S, H, stride, fd, eps, fr, st);
+  return hipGetLastError();
+}
+
+// table[s * np + j] = (cos, sin) of pos[s][j / fd] * inv_freq[j mod fd], the
+// turn of rotation pair j (< np = 3 fd) of row s, computed as above: the
+// projection epilogue that normalizes and rotates q and k in place of
+// k_qk_norm_rope reads it.
+__global__ void __launch_bounds__(256) k_rope_table(const int32_t* __restrict__ pos, float2* __restrict__ table,
+                                                    int S, int fd, RopeFreqs fr) {
+  const int np = 3 * fd;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)S * np) return;
+  const int s = (int)(i / np), j = (int)(i - (long)s * np), ax = j / fd;
+  float sn, cs;
+  sincosf((float)pos[3L * s + ax] * fr.inv_freq[j - ax * fd], &sn, &cs);
+  table[i] = make_float2(cs, sn);
+}
+
+// Rows [S, stride) of q and k and columns [S, stride) of v^T set to zero,
+// one workgroup per (batch item, head).
+__global__ void __launch_bounds__(256) k_qk_tail_zero(bf16_t* __restrict__ qo, bf16_t* __restrict__ ko,
+                                                      bf16_t* __restrict__ vto, int S, int stride) {
+  const long bh = blockIdx.x;
+  const int n = (stride - S) * 128;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int s = S + i / 128, c = i % 128;
+    qo[(bh * stride + s) * 128 + c] = bf16_t(0);
+    ko[(bh * stride + s) * 128 + c] = bf16_t(0);
+    vto[(bh * 128 + c) * stride + s] = bf16_t(0);
+  }
+}
+
+hipError_t launch_rope_table(const int32_t* pos, float* table, int S, int fd, float theta, hipStream_t st) {
+  if (fd <= 0 || 6 * fd > 128 || S <= 0) return hipErrorInvalidValue;
+  RopeFreqs fr;
+  for (int j = 0; j < 64; ++j) fr.inv_freq[j] = j < fd ? (float)pow((double)theta, -(double)j / fd) : 0.f;
+  const long n = (long)S * 3 * fd;
+  k_rope_table<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(pos, reinterpret_cast<float2*>(table), S, fd, fr);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_tail_zero(bf16_t* qo, bf16_t* ko, bf16_t* vto, int BH, int S, int stride, hipStream_t st) {
+  if (stride < S) return hipErrorInvalidValue;
+  if (stride == S) return hipSuccess;
+  k_qk_tail_zero<<<dim3((unsigned)BH), 256, 0, st>>>(qo, ko, vto, S, stride);
   return hipGetLastError();
 }
 

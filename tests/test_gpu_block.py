@@ -97,6 +97,34 @@ def test_block_small_bf16_wide_heads():
     check_block(workload(dims_bf16(hidden=512, num_heads=6, ffn_dim=1024), pads=5, seed=3))
 
 
+@pytest.mark.parametrize("pads,batch,heads", [(13, 2, 4), (64, 1, 6), (0, 3, 4)])
+def test_fused_qk_epilogue_equals_the_separate_pass(pads, batch, heads):
+    # In a bf16 block the QKV projection normalizes, rotates and transposes
+    # q/k/v in its epilogue; its outputs equal the plain projection followed
+    # by the standalone q/k pass bit for bit (the same bf16 tile, the same
+    # arithmetic). Batch items of 204 / 255 / 191 rows put two items in one
+    # 256-row tile and ragged 8-row groups at their ends.
+    print(f"fused q/k epilogue pads={pads} batch={batch} heads={heads}", flush=True)
+    dims = dims_bf16(num_heads=heads, ffn_dim=1024)
+    wl = workload(dims, pads=pads, batch=batch, seed=9 + pads)
+    cfg, lay, blocks, x = dv.upload(wl)
+    taps = tap_buffers(cfg, lay, torch.bfloat16)
+    m.block_forward(cfg, lay, blocks, x, taps=taps)
+    B, S, D = lay.batch, lay.seq_len, cfg.hidden
+    qkv = m.linear(taps["adaln1"].view(B * S, D), blocks[0].w_qkv).view(B, S, -1)
+    q, k, vt = m.qk_norm_rope(cfg, lay, qkv, blocks[0].q_norm, blocks[0].k_norm)
+    torch.cuda.synchronize()
+    st = lay.seq_stride
+    assert torch.equal(taps["q_rot"][:, :, :S], q[:, :, :S])
+    assert torch.equal(taps["k_rot"][:, :, :S], k[:, :, :S])
+    assert torch.equal(taps["v_t"][:, :, :, :S], vt[:, :, :, :S])
+    # rows past S of the per-head buffers are zero
+    if st > S:
+        assert not taps["q_rot"][:, :, S:].float().abs().sum().item()
+        assert not taps["k_rot"][:, :, S:].float().abs().sum().item()
+        assert not taps["v_t"][:, :, :, S:].float().abs().sum().item()
+
+
 def test_block_invariants_bit_exact():
     print("block invariants", flush=True)
     dims = dims_bf16()
