@@ -97,15 +97,17 @@ def test_block_small_bf16_wide_heads():
     check_block(workload(dims_bf16(hidden=512, num_heads=6, ffn_dim=1024), pads=5, seed=3))
 
 
-@pytest.mark.parametrize("pads,batch,heads", [(13, 2, 4), (64, 1, 6), (0, 3, 4)])
-def test_fused_qk_epilogue_equals_the_separate_pass(pads, batch, heads):
+@pytest.mark.parametrize("pads,batch,heads,fd", [(13, 2, 4, 16), (64, 1, 6, 16), (0, 3, 4, 16), (13, 1, 4, 8),
+                                                 (5, 2, 4, 21), (13, 1, 4, 0)])
+def test_fused_qk_epilogue_equals_the_separate_pass(pads, batch, heads, fd):
     # In a bf16 block the QKV projection normalizes, rotates and transposes
     # q/k/v in its epilogue; its outputs equal the plain projection followed
     # by the standalone q/k pass bit for bit (the same bf16 tile, the same
     # arithmetic). Batch items of 204 / 255 / 191 rows put two items in one
-    # 256-row tile and ragged 8-row groups at their ends.
-    print(f"fused q/k epilogue pads={pads} batch={batch} heads={heads}", flush=True)
-    dims = dims_bf16(num_heads=heads, ffn_dim=1024)
+    # 256-row tile and ragged 8-row groups at their ends; 8, 16 or 21
+    # rotary frequencies per axis (24, 48 or 63 turned pairs of 64), or none.
+    print(f"fused q/k epilogue pads={pads} batch={batch} heads={heads} fd={fd}", flush=True)
+    dims = dims_bf16(num_heads=heads, ffn_dim=1024, rope_freq_dim=fd)
     wl = workload(dims, pads=pads, batch=batch, seed=9 + pads)
     cfg, lay, blocks, x = dv.upload(wl)
     taps = tap_buffers(cfg, lay, torch.bfloat16)
