@@ -12,6 +12,7 @@
 // residual adds and between blocks).
 #include "common.h"
 #include "kernels.h"
+#include "rotq.h"
 
 namespace minih3 {
 
@@ -136,6 +137,114 @@ __global__ void __launch_bounds__(NT) k_adaln(const TI* x, T* y,  // x and y may
       Vec<T>::store(yr + c * VN, o);
     }
   }
+}
+
+// AdaLN whose output row goes straight to rotated W8A8 codes: the modulated
+// row is rounded to bf16 (the value the bf16 kernel stores), then rotated and
+// quantized by rotate_quantize_row. Chunk c = t + 256 i of 8 values is block
+// 16 i + t / 16, lane t % 16 of that function's layout, so the registers
+// pass over as they are; codes and scale equal those of k_adaln (bf16)
+// followed by k_rot_quant bit for bit.
+template <typename TI, int MAXV>
+__global__ void __launch_bounds__(256) k_adaln_rq(const TI* x, int8_t* __restrict__ q, float* __restrict__ qscale,
+                                                  const float* __restrict__ table, const int32_t* __restrict__ tags,
+                                                  const int32_t* __restrict__ tidx, int S, int D, int which,
+                                                  float eps, int num_tags, int num_tvals) {
+  constexpr int NT = 256, VN = 8;
+  __shared__ float red[NT / 64];
+  __shared__ float red_q[4];
+  const long row = blockIdx.x;
+  const int s = (int)(row % S);
+  const int nv = D / VN;
+  const TI* xr = x + row * D;
+  float v[MAXV][VN];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = threadIdx.x + i * NT;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) v[i][e] = 0.f;
+    if (c < nv) {
+      load_in<TI, VN>(xr + c * VN, v[i]);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) sum += v[i][e];
+    }
+  }
+  const float mean = block_sum<NT>(sum, red) / (float)D;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = threadIdx.x + i * NT;
+    if (c < nv) {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        float d = v[i][e] - mean;
+        sq += d * d;
+      }
+    }
+  }
+  const float var = block_sum<NT>(sq, red) / (float)D;
+  const float rstd = rsqrtf(var + eps);
+  const int tr = table_row_of(tags[s], tidx[s], num_tags, num_tvals);
+  const float* shift = tr >= 0 ? table + ((long)tr * 6 + 3 * which + 0) * D : nullptr;
+  const float* scale = tr >= 0 ? table + ((long)tr * 6 + 3 * which + 1) * D : nullptr;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = threadIdx.x + i * NT;
+    if (c < nv) {
+      float o[VN];
+      if (tr >= 0) {
+#pragma unroll
+        for (int e = 0; e < VN; e += 4) {
+          floatx4 sh = *reinterpret_cast<const floatx4*>(shift + c * VN + e);
+          floatx4 sc = *reinterpret_cast<const floatx4*>(scale + c * VN + e);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[e + u] = (v[i][e + u] - mean) * rstd * (1.f + sc[u]) + sh[u];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) o[e] = (v[i][e] - mean) * rstd;
+      }
+#pragma unroll
+      for (int e = 0; e < VN; e += 2) {  // the stored bf16 values
+        const uint32_t pk = pack_bf16x2(o[e], o[e + 1]);
+        v[i][e] = __uint_as_float(pk << 16);
+        v[i][e + 1] = __uint_as_float(pk & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VN; ++e) v[i][e] = 0.f;
+    }
+  }
+  rotate_quantize_row<MAXV>(v, D / 128, q + row * D, qscale + row, red_q);
+}
+
+template <typename TI>
+hipError_t launch_adaln_rq_t(const TI* x, int8_t* q, float* qscale, const float* table, const int32_t* tags,
+                             const int32_t* tidx, int B, int S, int D, int which, float eps, int num_tags,
+                             int num_tvals, hipStream_t st) {
+  if (D % 128 != 0 || D > 8 * 1024) return hipErrorInvalidValue;
+  const int nv = D / 8;
+  dim3 grid((unsigned)((long)B * S));
+  if (nv <= 256)
+    k_adaln_rq<TI, 1><<<grid, 256, 0, st>>>(x, q, qscale, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else if (nv <= 512)
+    k_adaln_rq<TI, 2><<<grid, 256, 0, st>>>(x, q, qscale, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else if (nv <= 768)
+    k_adaln_rq<TI, 3><<<grid, 256, 0, st>>>(x, q, qscale, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  else
+    k_adaln_rq<TI, 4><<<grid, 256, 0, st>>>(x, q, qscale, table, tags, tidx, S, D, which, eps, num_tags, num_tvals);
+  return hipGetLastError();
+}
+
+hipError_t launch_adaln_rq(const void* x, bool x_f32, int8_t* q, float* qscale, const float* table,
+                           const int32_t* tags, const int32_t* tidx, int B, int S, int D, int which, float eps,
+                           int num_tags, int num_tvals, hipStream_t st) {
+  if (x_f32)
+    return launch_adaln_rq_t<float>(static_cast<const float*>(x), q, qscale, table, tags, tidx, B, S, D, which, eps,
+                                    num_tags, num_tvals, st);
+  return launch_adaln_rq_t<bf16_t>(static_cast<const bf16_t*>(x), q, qscale, table, tags, tidx, B, S, D, which, eps,
+                                   num_tags, num_tvals, st);
 }
 
 template <typename TI, typename T>

@@ -257,7 +257,10 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       bw = blocks[i];
     }
     // C = A . W^T with epilogue `epi`; `which` picks the weight (0 qkv, 1 out, 2 gate/up, 3 down)
-    auto proj = [&](int epi, const T* A, int which, void* C, int N, int K, EpiArgs& ea) -> hipError_t {
+    // With quantized set, A's rows are already rotated and quantized in
+    // w.qx / w.sx (by the AdaLN kernel).
+    auto proj = [&](int epi, const T* A, int which, void* C, int N, int K, EpiArgs& ea,
+                    bool quantized = false) -> hipError_t {
       if (!qblocks) {
         const void* W = which == 0 ? bw.w_qkv : which == 1 ? bw.w_out : which == 2 ? bw.w_gate_up : bw.w_down;
         return launch_gemm<T>(epi, A, (const T*)W, C, M, N, K, ea, st);
@@ -265,11 +268,13 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       const minih3_block_weights_w8a8& qb = qblocks[i];
       const int8_t* QW = which == 0 ? qb.q_qkv : which == 1 ? qb.q_out : which == 2 ? qb.q_gate_up : qb.q_down;
       const float* SW = which == 0 ? qb.s_qkv : which == 1 ? qb.s_out : which == 2 ? qb.s_gate_up : qb.s_down;
-      hipError_t r = launch_rot_quant<bf16_t>(reinterpret_cast<const bf16_t*>(A), M, K, w.qx, w.sx, st);
-      if (r != hipSuccess) return r;
+      if (!quantized) {
+        hipError_t r = launch_rot_quant<bf16_t>(reinterpret_cast<const bf16_t*>(A), M, K, w.qx, w.sx, st);
+        if (r != hipSuccess) return r;
+      }
       ea.row_scale = w.sx;
       ea.col_scale = SW;
-      r = launch_gemm_i8(epi, w.qx, QW, C, M, N, K, ea, st);
+      hipError_t r = launch_gemm_i8(epi, w.qx, QW, C, M, N, K, ea, st);
       ea.row_scale = ea.col_scale = nullptr;
       return r;
     };
@@ -285,10 +290,18 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
     ea.num_tvals = c->num_tvals;
     ea.ffn_dim = F;
 
+    // W8A8: the AdaLN kernels write the rotated int8 rows the next
+    // projection reads (unless the bf16 rows are asked for as a tap)
+    const bool fuse_q1 = qblocks && D % 128 == 0 && D <= 8192 && !(tap && taps->adaln1);
+    const bool fuse_q2 = qblocks && D % 128 == 0 && D <= 8192 && !(tap && taps->adaln2);
     {
       Timed tm(prof, kKAdaLN1, st);
-      HIPCHECK(launch_adaln<T>(src, src_f32, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 0,
-                               c->norm_eps, c->num_tags, c->num_tvals, st));
+      if (fuse_q1)
+        HIPCHECK(launch_adaln_rq(src, src_f32, w.qx, w.sx, bw.adaln_table, L->token_tags, L->timestep_indices, B, S,
+                                 D, 0, c->norm_eps, c->num_tags, c->num_tvals, st));
+      else
+        HIPCHECK(launch_adaln<T>(src, src_f32, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 0,
+                                 c->norm_eps, c->num_tags, c->num_tvals, st));
     }
     if (tap && taps->adaln1) HIPCHECK(hipMemcpyAsync(taps->adaln1, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
     if (sizeof(T) == 2) {
@@ -310,7 +323,7 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       eq.qk_eps = c->qk_norm_eps;
       eq.kmax = kmax;
       eq.masks = w.masks;
-      HIPCHECK(proj(kEpiQKRope, a, 0, nullptr, 3 * Wd, D, eq));
+      HIPCHECK(proj(kEpiQKRope, a, 0, nullptr, 3 * Wd, D, eq, fuse_q1));
     } else {
       {
         Timed tm(prof, kKQKV, st);
@@ -344,13 +357,17 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
     if (tap && taps->x_mid) HIPCHECK(launch_cast_f32<T>(xmid, (T*)taps->x_mid, (long)M * D, st));
     {
       Timed tm(prof, kKAdaLN2, st);
-      HIPCHECK(launch_adaln<T>(xmid, true, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 1,
-                               c->norm_eps, c->num_tags, c->num_tvals, st));
+      if (fuse_q2)
+        HIPCHECK(launch_adaln_rq(xmid, true, w.qx, w.sx, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D,
+                                 1, c->norm_eps, c->num_tags, c->num_tvals, st));
+      else
+        HIPCHECK(launch_adaln<T>(xmid, true, a, bw.adaln_table, L->token_tags, L->timestep_indices, B, S, D, 1,
+                                 c->norm_eps, c->num_tags, c->num_tvals, st));
     }
     if (tap && taps->adaln2) HIPCHECK(hipMemcpyAsync(taps->adaln2, a, (size_t)M * D * e, hipMemcpyDeviceToDevice, st));
     {
       Timed tm(prof, kKGateUp, st);
-      HIPCHECK(proj(kEpiSwiGLU, a, 2, hbuf, 2 * F, D, ea));
+      HIPCHECK(proj(kEpiSwiGLU, a, 2, hbuf, 2 * F, D, ea, fuse_q2));
     }
     if (tap && taps->ffn_h) HIPCHECK(hipMemcpyAsync(taps->ffn_h, hbuf, (size_t)M * F * e, hipMemcpyDeviceToDevice, st));
     if (tap && taps->ffn_out) HIPCHECK(proj(kEpiStore, hbuf, 3, taps->ffn_out, D, F, ea));

@@ -191,6 +191,11 @@ hipError_t launch_rot_quant(const T* x, int M, int K, int8_t* q, float* scale, h
 
 // ---- denoising step: unmerged LoRA, Euler update ----
 // out[m] = [x[m, 0:K] | s * t[m, 0:R]] (rows of K + R), 16-byte pieces.
+// AdaLN (bf16 semantics) straight to rotated W8A8 codes q [B*S, D] and row
+// scales qscale [B*S]; x bf16 or fp32; D % 128 == 0, D <= 8192.
+hipError_t launch_adaln_rq(const void* x, bool x_f32, int8_t* q, float* qscale, const float* table,
+                           const int32_t* tags, const int32_t* tidx, int B, int S, int D, int which, float eps,
+                           int num_tags, int num_tvals, hipStream_t st);
 // table [S, 3 fd] of (cos, sin) pairs: the rotary turn of each pair of each row
 hipError_t launch_rope_table(const int32_t* pos, float* table, int S, int fd, float theta, hipStream_t st);
 // zero rows / columns [S, stride) of the per-head q, k, v^T buffers (BH = B * heads)

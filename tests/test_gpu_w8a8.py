@@ -140,6 +140,28 @@ def test_block_w8a8_small(pads):
     assert np.array_equal(got[:, pad], wl.x.values()[:, pad])
 
 
+@pytest.mark.parametrize("hidden,heads,ffn", [(512, 4, 768), (5376, 56, 14336)])
+def test_block_w8a8_adaln_writes_the_same_codes(hidden, heads, ffn):
+    # In the W8A8 block the AdaLN kernels write the rotated int8 rows of the
+    # next projection themselves; asking for the bf16 AdaLN rows as taps
+    # takes the separate AdaLN -> rotate/quantize route instead. Both must give
+    # the same block output bit for bit (the same bf16 values, the same
+    # rotation and quantization arithmetic).
+    print(f"w8a8 fused AdaLN quantization hidden={hidden}", flush=True)
+    dims = synth.ModelDims(hidden=hidden, num_heads=heads, head_dim=128, ffn_dim=ffn, num_tvals=8, dtype="bf16")
+    segs = [("text", 21), ("audio", 30), ("video", 90, (2, 5, 9))]
+    wl = synth.make_custom(dims, segs, (2, 5, 9), 7, seed=4, batch=2)
+    cfg, lay, blocks, x = dv.upload(wl)
+    qb = [m.DeviceBlockW8A8.from_block(b) for b in blocks]
+    fused = m.block_forward_w8a8(cfg, lay, qb, x)
+    B, S = lay.batch, lay.seq_len
+    taps = dict(adaln1=torch.empty(B, S, hidden, dtype=torch.bfloat16, device="cuda"),
+                adaln2=torch.empty(B, S, hidden, dtype=torch.bfloat16, device="cuda"))
+    separate = m.block_forward_w8a8(cfg, lay, qb, x, taps=taps)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, separate)
+
+
 def test_block_w8a8_gate_zero_is_identity():
     dims = synth.ModelDims(hidden=512, num_heads=4, head_dim=128, ffn_dim=768, num_tvals=8, dtype="bf16")
     wl = synth.make_custom(dims, [("text", 40), ("video", 90, (2, 5, 9))], (2, 5, 9), 6, seed=3)
