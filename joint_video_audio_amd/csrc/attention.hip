@@ -602,6 +602,12 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   auto step = [&](int j, Half (&sc)[2], bf16x8 (&P)[2][2], bf16x8 (&G)[kAhead]) {
     Ahead a1;
     enter(j, a1);
+    // A wave's first half-step after the barrier issues at raised priority
+    // (arbitration between the two waves of a SIMD): the wave that reaches
+    // the second half first yields to the one still in its first. Measured
+    // ~2.4 % faster; raising the MFMA pairs only, or the second half, is
+    // slower.
+    __builtin_amdgcn_s_setprio(2);
     const uint8_t* Kn = kslot((j + 1) % kRing);
     const uint8_t* Vc = vslot(j % kRing);
     const uint8_t* Kn2 = kslot((j + 2) % kRing);
@@ -650,6 +656,7 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     };
     bf16x8 P1[2], Pn[2];
     half(0, sc[1], P1);  // scores of key half 1 of tile j become P[1]
+    __builtin_amdgcn_s_setprio(0);
     P[1][0] = P1[0];
     P[1][1] = P1[1];
     mask_half(sc[0], a1, 0);
