@@ -10,10 +10,15 @@ workload is the clip-scale block: hidden 5376, 56 x 128 heads, FFN 14336,
 32768 packed rows (1024 text, 1536 audio, 30208 video on a 16 x 32 x 59
 grid), bf16. Prints one JSON line.
 
-value = packed rows / s per block forward; TFLOP/s counts algorithmic work
-only (GEMMs on non-padding rows, attention on same-document pairs of
-non-padding rows). The dominant kernel's roofline uses its average launch
-time from HIP events recorded on the launch stream inside the timed region.
+value = packed rows / s per block forward from the median of K steps, each
+timed with a HIP event pair on the launch stream; TFLOP/s counts
+algorithmic work only (GEMMs on non-padding rows, attention on same-document
+pairs of non-padding rows). The output of the last timed step is compared,
+in the same run, with the oracle's values at 256 sampled rows
+(tests/golden/<workload>_seed<seed>.npz). A second pass of K steps records
+an event pair around every launch (the library's MINIH3_PROFILE) for the
+per-kernel times; the dominant kernel's roofline uses its average launch
+time from that pass. A third, untimed pass samples the shader clock.
 cpu_baseline times the fp64 oracle on a bounded sample of the workload.
 table_build times, apart from the step, the build of one block's AdaLN
 table from the workload's timestep values (time embeddings, then the bf16
@@ -70,6 +75,89 @@ def measured_traffic(workload: str, summary: str = TRAFFIC_SUMMARY, source: str 
         return None
     sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
     return int(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def same_run_parity(workload: str, seed: int, out):
+    """Compare the timed output at the oracle's sampled rows (written by
+    tests/golden/make_golden.py from the fp64 oracle) with the bar of the
+    parity tests: relative L2 <= 1e-2, max-abs <= 5e-2 beyond half a bf16
+    ulp of the expected value. None when no expected values exist for the
+    workload and seed."""
+    import numpy as np
+    path = os.path.join(ROOT, "tests", "golden", f"{workload}_seed{seed}.npz")
+    if not os.path.exists(path):
+        return None
+    g = np.load(path, allow_pickle=False)
+    rows = g["rows"]
+    want = g["out"].astype(np.float64)
+    got = out[0, torch_index(rows, out.device)].float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126))) - 8)
+    beyond = float((err - half_ulp).max())
+    return {"expected": os.path.relpath(path, ROOT), "rows": int(rows.size), "rel_l2": rel,
+            "max_abs": float(err.max()), "max_abs_beyond_half_bf16_ulp": beyond,
+            "pass": bool(rel <= 1e-2 and beyond <= 5e-2 and np.all(np.isfinite(got)))}
+
+
+def torch_index(a, device):
+    import torch
+    return torch.from_numpy(a).to(device)
+
+
+def observed_clock(step, seconds: float = 3.0):
+    """Mean shader clock over the XCDs while steps run back to back: a
+    background thread reads `amd-smi metric -c` (GFX_i CLK lines) during
+    about `seconds` of steps. None when amd-smi is not available."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if not exe:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run([exe, "metric", "-c"], capture_output=True, text=True, timeout=10).stdout
+            except Exception:  # pragma: no cover
+                return
+            clk, sec = [], None
+            for line in txt.splitlines():
+                h = re.match(r"\s*(GFX_\d+):", line)
+                if h:
+                    sec = h.group(1)
+                    continue
+                if re.match(r"\s*[A-Z]+_?\d*:\s*$", line):
+                    sec = None
+                c = re.match(r"\s*CLK:\s*([0-9.]+)\s*MHz", line)
+                if c and sec:
+                    clk.append(float(c.group(1)))
+            if clk:
+                samples.append(sum(clk) / len(clk))
+
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds or (n < 200 and len(samples) < 2 and time.perf_counter() - t0 < 20):
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        n += 5
+    stop.set()
+    th.join(timeout=15)
+    busy = [c for c in samples if c > 600.0]  # samples taken while the GPU ran (idle reads ~100 MHz)
+    if not busy:
+        return None
+    return {"mean": round(sum(busy) / len(busy), 1), "min": round(min(busy), 1), "max": round(max(busy), 1),
+            "samples": len(busy), "steps": n, "nominal": 2400.0,
+            "source": "amd-smi metric -c, mean of the GFX_i clocks, sampled while the same step ran back to back "
+                      "(a separate pass after the timed ones)"}
 
 
 def cpu_baseline(wl, rows: int):
@@ -397,21 +485,32 @@ def main():
     for _ in range(a.warmup):
         m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws)
     torch.cuda.synchronize()
-    m.profile_collect()  # drop anything recorded so far
 
+    # headline: K steps, a HIP event pair around each on the launch stream
     st = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(st)
-    for _ in range(a.steps):
-        m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws, flags=m.PROFILE)
-    ev1.record(st)
+    evs[0].record(st)
+    for i in range(a.steps):
+        m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws)
+        evs[i + 1].record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / a.steps
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps)]
+    ms_step = float(np.median(step_ms))
+    ms_mean = evs[0].elapsed_time(evs[-1]) / a.steps
+    # the output of the last timed step against the oracle's sampled rows
+    parity = same_run_parity(a.workload, a.seed, out)
+
+    # per-kernel times: a second pass of K steps with the library's events
+    # around every launch (MINIH3_PROFILE), on the same stream
+    m.profile_collect()
+    for _ in range(a.steps):
+        m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws, flags=m.PROFILE)
+    torch.cuda.synchronize()
     kern = m.profile_collect()
+    clock = observed_clock(lambda: m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws))
 
     gemm, attn = flop_counts(wl.dims, wl.layout)
     t_block = ms_step / 1e3 / nb
@@ -440,10 +539,17 @@ def main():
                    "blocks_per_step": nb, "hidden": wl.dims.hidden, "heads": wl.dims.num_heads,
                    "head_dim": wl.dims.head_dim, "ffn_dim": wl.dims.ffn_dim, "timestep_values": wl.dims.num_tvals,
                    "seed": a.seed},
+        "ms_per_step_stat": "median of the per-step HIP event times",
+        "ms_per_step_mean": round(ms_mean, 4),
+        "ms_per_step_min": round(min(step_ms), 4),
+        "ms_per_step_max": round(max(step_ms), 4),
         "tflops": round(tflops, 1),
         "mfma_peak_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
+        "parity": parity,
+        "clock_mhz": clock,
         "kernel_avg_ms": kernels,
+        "kernel_avg_ms_pass": "a second pass of the same K steps with an event pair around every launch",
         "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(att_tflops, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(a.workload),

@@ -110,17 +110,23 @@ typedef struct {
 
 /* Optional copies of intermediates of the FIRST block (tests). Every field
  * may be NULL. Shapes (S_pad = S rounded up to a multiple of 64):
- *   adaln1, adaln2, x_mid, attn_proj, ffn_out : [B, S, D] act
+ *   adaln1, adaln2, attn_proj, ffn_out : [B, S, D] act
+ *   x_mid        : [B, S, D] fp32, the residual stream after the attention's
+ *                  gated add (the library keeps the residual stream in fp32)
  *   q_rot, k_rot : [B, H, S_pad, hd] act (post RMSNorm + RoPE)
  *   v_t          : [B, H, hd, S_pad] act (values, transposed)
  *   attn_o       : [B, S, W] act;  ffn_h : [B, S, F] act
  *   table_row    : [S] int32 tag*num_tvals + tidx, -1 on padding rows
  *   doc_id       : [S] int32 attention document (1 = padding row)
  *   tile_flags   : [ceil(S/64)] int32 bit0 = tile holds a non-padding row, bit1 = a padding row
- *   num_pad      : [1] int32 */
+ *   num_pad      : [1] int32
+ *   block_out    : [B, S, D] fp32, the residual stream after the first
+ *                  block before it is rounded to act (for a one-block call
+ *                  x_out is exactly this tensor rounded to act) */
 typedef struct {
   void *adaln1, *q_rot, *k_rot, *v_t, *attn_o, *attn_proj, *x_mid, *adaln2, *ffn_h, *ffn_out;
   int32_t *table_row, *doc_id, *tile_flags, *num_pad;
+  void* block_out;
 } minih3_taps;
 
 /* Bytes of workspace minih3_block_forward needs for (batch, seq_len). */
@@ -141,28 +147,57 @@ int minih3_block_forward(const minih3_config* cfg, const minih3_layout* layout,
                          uint32_t flags, minih3_taps* taps, void* stream);
 
 /* Bytes of workspace minih3_attention_packed needs for (batch, seq_len)
- * with cfg->num_heads heads. */
+ * with cfg->num_heads heads (q, k and v^T in the kernels' layouts, plus the
+ * per-tile document masks). */
 int minih3_attention_workspace_bytes(const minih3_config* cfg, int32_t batch, int32_t seq_len, size_t* bytes);
 
-/* Attention over the packed sequence (page: full self-attention; padding
- * rows kept in their own document by a boolean mask):
+/* Attention over the packed sequence. Page "MiniMaxH3Transformer3DModel",
+ * class description: attention is full self-attention over the one packed
+ * sequence (text, conditioning, audio and target-video rows alike); a
+ * layout that carries padding rows (tag -1) keeps them in their own
+ * attention document with a boolean mask; the batch axis replicates the
+ * layout, each item its own sequence. The page gives no softmax scale; the
+ * library takes 1/sqrt(hd) unless the caller passes one:
  *   out[b, i, h*hd:(h+1)*hd] = sum_j softmax_j(scale * q_i . k_j) v_j,
  * over j < S with doc(j) == doc(i), doc = (tag == -1); under
  * MINIH3_ASSUME_PADLESS every row is in one document.
+ * q, k, v : [B, S, H, hd] act, q and k after the per-head norm and the
+ *           rotary embedding (as the block applies them before attention)
+ * out     : [B, S, H*hd] act (must not alias q, k or v)
+ * The inputs are copied into the workspace in the layouts the kernels read
+ * (see minih3_attention_headmajor). Only token_tags (and batch, seq_len) of
+ * the layout are read; with MINIH3_VALIDATE | MINIH3_ASSUME_PADLESS a -1
+ * row gives MINIH3_E_NEEDS_MASK (one stream synchronisation). Reads
+ * head_dim (128), num_heads and act_dtype of cfg. */
+int minih3_attention_packed(const minih3_config* cfg, const minih3_layout* layout, const void* q, const void* k,
+                            const void* v, void* out, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            uint32_t flags, void* stream);
+
+/* Bytes of workspace minih3_attention_headmajor needs. */
+int minih3_attention_headmajor_workspace_bytes(const minih3_config* cfg, int32_t batch, int32_t seq_len,
+                                               size_t* bytes);
+
+/* minih3_attention_packed on inputs already in the kernels' layouts (what
+ * the block's QKV projection writes), without the copy:
  * q, k : [B, H, seq_stride, hd] act;  v_t : [B, H, hd, seq_stride] act;
  * out  : [B, S, H*hd] act. seq_stride >= S and a multiple of 64; rows
  * and columns in [S, seq_stride) are never used in the result but must be
- * readable. softmax_scale <= 0 selects 1/sqrt(hd). Only token_tags (and
- * batch, seq_len) of the layout are read. */
-int minih3_attention_packed(const minih3_config* cfg, const minih3_layout* layout,
-                            const void* q, const void* k, const void* v_t, int32_t seq_stride,
-                            void* out, float softmax_scale, void* workspace, size_t workspace_bytes,
-                            uint32_t flags, void* stream);
+ * readable. */
+int minih3_attention_headmajor(const minih3_config* cfg, const minih3_layout* layout, const void* q, const void* k,
+                               const void* v_t, int32_t seq_stride, void* out, float softmax_scale, void* workspace,
+                               size_t workspace_bytes, uint32_t flags, void* stream);
 
-/* One AdaLN modulation: y = LN(x) * (1 + scale) + shift per row, with
+/* One AdaLN modulation. Page "MiniMaxH3Transformer3DModel": Parameters
+ * (norm_eps of the pre-attention and pre-feed-forward norms) and class
+ * description (the row's modality tag selects its AdaLN modulation
+ * parameters; `forward` timestep_indices picks the row's timestep). The
+ * page does not write the form; the library takes the non-affine LayerNorm
+ * (mean, biased variance) with the modulation as its affine part:
+ * y = LN(x) * (1 + scale) + shift per row, with
  * (shift, scale) = adaln_table[tag, tidx, 3*which + {0, 1}] and zeros on
  * padding rows. which = 0 before attention, 1 before the FFN.
- * x, y : [B, S, D] act (may alias). */
+ * x, y : [B, S, D] act (may alias); adaln_table [num_tags, num_tvals, 6, D]
+ * fp32. Indices out of range are clamped (no layout validation here). */
 int minih3_adaln_modulate(const minih3_config* cfg, const minih3_layout* layout, const void* x,
                           const float* adaln_table, int32_t which, void* y, uint32_t flags, void* stream);
 

@@ -354,7 +354,7 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       ea.gate_slot = 2;
       HIPCHECK(proj(kEpiGatedResid, o, 1, xmid, D, Wd, ea));
     }
-    if (tap && taps->x_mid) HIPCHECK(launch_cast_f32<T>(xmid, (T*)taps->x_mid, (long)M * D, st));
+    if (tap && taps->x_mid) HIPCHECK(hipMemcpyAsync(taps->x_mid, xmid, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st));
     {
       Timed tm(prof, kKAdaLN2, st);
       if (fuse_q2)
@@ -378,6 +378,17 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
       ea.out_f32 = last ? (sizeof(T) == 4) : 1;
       ea.gate_slot = 5;
       HIPCHECK(proj(kEpiGatedResid, hbuf, 3, dst, D, F, ea));
+    }
+    if (tap && taps->block_out) {
+      // the fp32 residual stream after the first block: the chain's own
+      // buffer, or (when x_out holds the rounded result) the same epilogue
+      // run again with an fp32 destination
+      if (!last || sizeof(T) == 4) {
+        HIPCHECK(hipMemcpyAsync(taps->block_out, dst, (size_t)M * D * 4, hipMemcpyDeviceToDevice, st));
+      } else {
+        ea.out_f32 = 1;
+        HIPCHECK(proj(kEpiGatedResid, hbuf, 3, taps->block_out, D, F, ea));
+      }
     }
     src = dst;
     src_f32 = !last || sizeof(T) == 4;
@@ -616,6 +627,50 @@ int check_step(const minih3_config* c, const minih3_step_weights* sw) {
   return check_edges(c, sw->edges);
 }
 
+// Bytes of the packed attention entry's workspace: q, k, v^T in the kernels'
+// layouts, then the tile masks and lists with the kernels' scratch.
+size_t attention_packed_bytes(const minih3_config* c, int B, int S, size_t* stage_each) {
+  const size_t Sp = (size_t)(S + 63) / 64 * 64;
+  const size_t each = align_up((size_t)B * c->num_heads * Sp * c->head_dim * act_size(c->act_dtype));
+  if (stage_each) *stage_each = each;
+  return 3 * each + tiles_bytes(B, S, c->num_heads, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+// Attention on q, k [B, H, stride, hd] and v^T [B, H, hd, stride] (arguments
+// checked by the caller); the workspace holds the tile masks and lists.
+int attention_run(const minih3_config* c, const minih3_layout* L, const void* q, const void* k, const void* v_t,
+                  int stride, void* out, float softmax_scale, void* workspace, size_t workspace_bytes, uint32_t flags,
+                  hipStream_t st) {
+  const int S = L->seq_len;
+  int32_t *list_real, *list_pad, *meta;
+  uint64_t* masks;
+  void* scratch;
+  const size_t need = tiles_bytes(L->batch, S, c->num_heads, &list_real, &list_pad, &meta, &masks, &scratch,
+                                  (char*)workspace);
+  if (!workspace || workspace_bytes < need) return MINIH3_E_WORKSPACE;
+  const int padless = (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0;
+  if ((flags & MINIH3_VALIDATE) && padless) {
+    HIPCHECK(launch_attn_tiles(L->token_tags, S, 0, masks, list_real, list_pad, meta, st));
+    int32_t m[2] = {0, 0};
+    HIPCHECK(hipMemcpyAsync(m, meta, 8, hipMemcpyDeviceToHost, st));
+    HIPCHECK(hipStreamSynchronize(st));
+    if (m[1] > 0) return MINIH3_E_NEEDS_MASK;
+  }
+  HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, masks, list_real, list_pad, meta, st));
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)c->head_dim);
+  if (c->act_dtype == MINIH3_BF16) {
+    HIPCHECK(launch_attention_prep<bf16_t>((const bf16_t*)k, masks, scratch, L->batch, S, c->num_heads, stride, st));
+    HIPCHECK(launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v_t, (bf16_t*)out, masks,
+                                      list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, stride, scale,
+                                      st));
+  } else {
+    HIPCHECK(launch_attention<float>((const float*)q, (const float*)k, (const float*)v_t, (float*)out, masks,
+                                     list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, stride, scale,
+                                     st));
+  }
+  return MINIH3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -646,11 +701,20 @@ int minih3_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_le
   return MINIH3_OK;
 }
 
-int minih3_attention_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_len, size_t* bytes) {
+int minih3_attention_headmajor_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_len,
+                                               size_t* bytes) {
   int s = check_config_attention(c);
   if (s) return s;
   if (!bytes || seq_len < 1 || batch < 1) return MINIH3_E_ARG;
   *bytes = tiles_bytes(batch, seq_len, c->num_heads, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return MINIH3_OK;
+}
+
+int minih3_attention_workspace_bytes(const minih3_config* c, int32_t batch, int32_t seq_len, size_t* bytes) {
+  int s = check_config_attention(c);
+  if (s) return s;
+  if (!bytes || seq_len < 1 || batch < 1) return MINIH3_E_ARG;
+  *bytes = attention_packed_bytes(c, batch, seq_len, nullptr);
   return MINIH3_OK;
 }
 
@@ -677,9 +741,9 @@ int minih3_block_forward_w8a8(const minih3_config* c, const minih3_layout* L, co
                        stream);
 }
 
-int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, const void* q, const void* k,
-                            const void* v_t, int32_t seq_stride, void* out, float softmax_scale, void* workspace,
-                            size_t workspace_bytes, uint32_t flags, void* stream) {
+int minih3_attention_headmajor(const minih3_config* c, const minih3_layout* L, const void* q, const void* k,
+                               const void* v_t, int32_t seq_stride, void* out, float softmax_scale, void* workspace,
+                               size_t workspace_bytes, uint32_t flags, void* stream) {
   int s = check_config_attention(c);
   if (s) return s;
   if (!L || L->batch < 1 || L->seq_len < 1 || !L->token_tags) return MINIH3_E_ARG;
@@ -687,34 +751,34 @@ int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, cons
   const int S = L->seq_len;
   if (seq_stride < S || seq_stride % 64 != 0) return MINIH3_E_ARG;
   if ((long)L->batch * c->num_heads * seq_stride > (1L << 31) - 1) return MINIH3_E_UNSUPPORTED;
-  int32_t *list_real, *list_pad, *meta;
-  uint64_t* masks;
-  void* scratch;
-  const size_t need = tiles_bytes(L->batch, S, c->num_heads, &list_real, &list_pad, &meta, &masks, &scratch,
-                                  (char*)workspace);
+  return attention_run(c, L, q, k, v_t, seq_stride, out, softmax_scale, workspace, workspace_bytes, flags,
+                       (hipStream_t)stream);
+}
+
+int minih3_attention_packed(const minih3_config* c, const minih3_layout* L, const void* q, const void* k,
+                            const void* v, void* out, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            uint32_t flags, void* stream) {
+  int s = check_config_attention(c);
+  if (s) return s;
+  if (!L || L->batch < 1 || L->seq_len < 1 || !L->token_tags) return MINIH3_E_ARG;
+  if (!q || !k || !v || !out || out == q || out == k || out == v) return MINIH3_E_ARG;
+  const int B = L->batch, S = L->seq_len, H = c->num_heads;
+  const int Sp = (S + 63) / 64 * 64;
+  if ((long)B * H * Sp > (1L << 31) - 1) return MINIH3_E_UNSUPPORTED;
+  size_t each = 0;
+  const size_t need = attention_packed_bytes(c, B, S, &each);
   if (!workspace || workspace_bytes < need) return MINIH3_E_WORKSPACE;
+  char* base = (char*)workspace;
+  void *qh = base, *kh = base + each, *vt = base + 2 * each;
   hipStream_t st = (hipStream_t)stream;
-  const int padless = (flags & MINIH3_ASSUME_PADLESS) ? 1 : 0;
-  if ((flags & MINIH3_VALIDATE) && padless) {
-    HIPCHECK(launch_attn_tiles(L->token_tags, S, 0, masks, list_real, list_pad, meta, st));
-    int32_t m[2] = {0, 0};
-    HIPCHECK(hipMemcpyAsync(m, meta, 8, hipMemcpyDeviceToHost, st));
-    HIPCHECK(hipStreamSynchronize(st));
-    if (m[1] > 0) return MINIH3_E_NEEDS_MASK;
-  }
-  HIPCHECK(launch_attn_tiles(L->token_tags, S, padless, masks, list_real, list_pad, meta, st));
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)c->head_dim);
   if (c->act_dtype == MINIH3_BF16)
-    HIPCHECK(launch_attention_prep<bf16_t>((const bf16_t*)k, masks, scratch, L->batch, S, c->num_heads, seq_stride, st));
-  if (c->act_dtype == MINIH3_BF16)
-    HIPCHECK(launch_attention<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v_t, (bf16_t*)out, masks,
-                                      list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, seq_stride, scale,
-                                      st));
+    HIPCHECK(launch_attn_stage<bf16_t>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (bf16_t*)qh,
+                                       (bf16_t*)kh, (bf16_t*)vt, B, S, H, Sp, st));
   else
-    HIPCHECK(launch_attention<float>((const float*)q, (const float*)k, (const float*)v_t, (float*)out, masks,
-                                     list_real, list_pad, meta, scratch, L->batch, S, c->num_heads, seq_stride, scale,
-                                     st));
-  return MINIH3_OK;
+    HIPCHECK(launch_attn_stage<float>((const float*)q, (const float*)k, (const float*)v, (float*)qh, (float*)kh,
+                                      (float*)vt, B, S, H, Sp, st));
+  return attention_run(c, L, qh, kh, vt, Sp, out, softmax_scale, base + 3 * each, workspace_bytes - 3 * each, flags,
+                       st);
 }
 
 int minih3_adaln_modulate(const minih3_config* c, const minih3_layout* L, const void* x, const float* table,

@@ -102,6 +102,12 @@ hipError_t launch_gemm(int epi, const T* A, const T* W, void* C, int M, int N, i
 // scratch: attention_scratch_bytes(B, S, H) bytes (per-head key-norm maxima
 // and per-workgroup flags).
 size_t attention_scratch_bytes(int B, int S, int H);
+// Packed q, k, v [B, S, H, 128] -> the attention kernels' layouts: q, k
+// head-major [B, H, stride, 128], v transposed [B, H, 128, stride]; rows
+// [S, stride) are written as zeros. stride is a multiple of 64, >= S.
+template <typename T>
+hipError_t launch_attn_stage(const T* q, const T* k, const T* v, T* qh, T* kh, T* vt, int B, int S, int H, int stride,
+                             hipStream_t st);
 // Per-document key-norm maxima into scratch (runs before launch_attention).
 template <typename T>
 hipError_t launch_attention_prep(const T* k, const uint64_t* masks, void* scratch, int B, int S, int H, int stride,

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("MINIH3_LIBRARY") or os.path.join(HERE, "libminih3.so")
+LIB_PATH = os.path.join(HERE, "libminih3.so")
 
 BF16, F32 = 0, 1
 VALIDATE, ASSUME_PADLESS, PROFILE = 1, 2, 4
@@ -64,7 +64,7 @@ TAP_INT = ("table_row", "doc_id", "tile_flags", "num_pad")
 
 
 class _Taps(ctypes.Structure):
-    _fields_ = [(n, _P) for n in TAP_FLOAT + TAP_INT]
+    _fields_ = [(n, _P) for n in TAP_FLOAT + TAP_INT + ("block_out",)]
 
 
 class TimeConfig(ctypes.Structure):
@@ -114,9 +114,13 @@ def lib() -> ctypes.CDLL:
         L.minih3_block_forward.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
                                            ctypes.POINTER(_BlockWeights), ctypes.c_int32, _P, _P, _P,
                                            ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
-        L.minih3_attention_packed.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, _P,
-                                              ctypes.c_int32, _P, ctypes.c_float, _P, ctypes.c_size_t,
-                                              ctypes.c_uint32, _P]
+        L.minih3_attention_packed.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, _P, _P,
+                                              ctypes.c_float, _P, ctypes.c_size_t, ctypes.c_uint32, _P]
+        L.minih3_attention_headmajor_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32,
+                                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_attention_headmajor.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, _P,
+                                                 ctypes.c_int32, _P, ctypes.c_float, _P, ctypes.c_size_t,
+                                                 ctypes.c_uint32, _P]
         L.minih3_adaln_modulate.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, ctypes.c_int32,
                                             _P, ctypes.c_uint32, _P]
         L.minih3_qk_norm_rope.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), _P, _P, _P, _P, _P, _P,
@@ -167,7 +171,8 @@ def lib() -> ctypes.CDLL:
                    "minih3_block_forward_w8a8"):
             getattr(L, fn).restype = ctypes.c_int
         for fn in ("minih3_workspace_bytes", "minih3_attention_workspace_bytes", "minih3_block_forward",
-                   "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
+                   "minih3_attention_packed", "minih3_attention_headmajor_workspace_bytes",
+                   "minih3_attention_headmajor", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
                    "minih3_profile_collect", "minih3_time_embed_workspace_bytes", "minih3_time_embed",
                    "minih3_adaln_table_workspace_bytes", "minih3_adaln_table"):
             getattr(L, fn).restype = ctypes.c_int
@@ -176,7 +181,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_workspace_bytes",
-            "minih3_attention_packed", "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
+            "minih3_attention_packed", "minih3_attention_headmajor_workspace_bytes", "minih3_attention_headmajor",
+            "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
             "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
             "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
             "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
@@ -323,9 +329,36 @@ def block_forward(cfg: Config, layout: DeviceLayout, blocks: Sequence[DeviceBloc
     return out
 
 
-def attention_packed(cfg: Config, layout: DeviceLayout, q: torch.Tensor, k: torch.Tensor, v_t: torch.Tensor,
+def attention_packed(cfg: Config, layout: DeviceLayout, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, flags: int = 0,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q, k, v [B, S, H, hd] (q, k after norm and rotary) -> out [B, S, H*hd]."""
+    dt = act_torch_dtype(cfg)
+    B, H, hd, S = layout.batch, cfg.num_heads, cfg.head_dim, layout.seq_len
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _req(t, dt, n, B * S * H * hd)
+    if out is None:
+        out = torch.empty(B, S, H * hd, dtype=dt, device=q.device)
+    _req(out, dt, "out", B * S * H * hd)
+    if workspace is None:
+        workspace = alloc_workspace(attention_workspace_bytes(cfg, B, S), q.device)
+    L = layout.c()
+    s = lib().minih3_attention_packed(ctypes.byref(cfg), ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                      float(softmax_scale), _ptr(workspace), workspace.numel(), flags, _stream())
+    _check(s, "attention_packed")
+    return out
+
+
+def attention_headmajor_workspace_bytes(cfg: Config, batch: int, seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().minih3_attention_headmajor_workspace_bytes(ctypes.byref(cfg), batch, seq_len, ctypes.byref(n)),
+           "attention_headmajor_workspace_bytes")
+    return int(n.value)
+
+
+def attention_headmajor(cfg: Config, layout: DeviceLayout, q: torch.Tensor, k: torch.Tensor, v_t: torch.Tensor,
+                        out: Optional[torch.Tensor] = None, softmax_scale: float = 0.0, flags: int = 0,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """q, k [B, H, stride, hd], v_t [B, H, hd, stride] -> out [B, S, H*hd]."""
     dt = act_torch_dtype(cfg)
     B, H, hd, S = layout.batch, cfg.num_heads, cfg.head_dim, layout.seq_len
@@ -336,12 +369,12 @@ def attention_packed(cfg: Config, layout: DeviceLayout, q: torch.Tensor, k: torc
         out = torch.empty(B, S, H * hd, dtype=dt, device=q.device)
     _req(out, dt, "out", B * S * H * hd)
     if workspace is None:
-        workspace = alloc_workspace(attention_workspace_bytes(cfg, B, S), q.device)
+        workspace = alloc_workspace(attention_headmajor_workspace_bytes(cfg, B, S), q.device)
     L = layout.c()
-    s = lib().minih3_attention_packed(ctypes.byref(cfg), ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v_t), stride,
-                                      _ptr(out), float(softmax_scale), _ptr(workspace), workspace.numel(), flags,
-                                      _stream())
-    _check(s, "attention_packed")
+    s = lib().minih3_attention_headmajor(ctypes.byref(cfg), ctypes.byref(L), _ptr(q), _ptr(k), _ptr(v_t), stride,
+                                         _ptr(out), float(softmax_scale), _ptr(workspace), workspace.numel(), flags,
+                                         _stream())
+    _check(s, "attention_headmajor")
     return out
 
 

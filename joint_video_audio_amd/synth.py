@@ -26,6 +26,10 @@ Recipe (per workload):
     table: all six modulation vectors (shift, scale, gate for attention and
     for the FFN) ~ N(0, 0.1) (fp32); gates near zero as in AdaLN-Zero, which
     keeps the block output at the scale its bf16 storage resolves.
+  * Unit-gate variant (``gate_mean=1.0``): the same draws with 1 added to
+    the two gate vectors, i.e. gates ~ N(1, 0.1). The branches then enter
+    the output at full size and outputs reach |x| ~ 17, where one bf16 ulp
+    is 0.125.
 """
 from __future__ import annotations
 
@@ -218,7 +222,10 @@ def build_layout(segments, num_pad: int, target_grid: Tuple[int, int, int],
                   cat(vid), cat(aud), cat(txt))
 
 
-def draw_block(rng, dims: ModelDims) -> BlockWeights:
+GATE_SLOTS = (2, 5)  # gate vectors of the attention and FFN residuals in a table entry
+
+
+def draw_block(rng, dims: ModelDims, gate_mean: float = 0.0) -> BlockWeights:
     D, W, F, hd = dims.hidden, dims.qkv_width, dims.ffn_dim, dims.head_dim
     w_qkv = _store(_normal(rng, (3 * W, D), 0.02), dims.dtype)
     w_out = _store(_normal(rng, (D, W), 0.02), dims.dtype)
@@ -227,6 +234,8 @@ def draw_block(rng, dims: ModelDims) -> BlockWeights:
     q_norm = _normal(rng, (hd,), 0.02, 1.0)
     k_norm = _normal(rng, (hd,), 0.02, 1.0)
     table = _normal(rng, (dims.num_tags, dims.num_tvals, 6, D), 0.1)
+    if gate_mean:
+        table[:, :, list(GATE_SLOTS)] += np.float32(gate_mean)
     return BlockWeights(w_qkv, w_out, w_gate_up, w_down, q_norm, k_norm, table)
 
 
@@ -269,7 +278,7 @@ def workload_dims(name: str) -> ModelDims:
 
 
 def make_workload(name: str, seed: int = 0, batch: int = 1, with_weights: bool = True,
-                  num_blocks: Optional[int] = None) -> Workload:
+                  num_blocks: Optional[int] = None, gate_mean: float = 0.0) -> Workload:
     spec = WORKLOADS[name]
     dims = workload_dims(name)
     rng = np.random.default_rng(seed)
@@ -282,7 +291,7 @@ def make_workload(name: str, seed: int = 0, batch: int = 1, with_weights: bool =
     layout = build_layout(spec["segments"], pads, spec["target_grid"], tidx)
     x = _store(_normal(rng, (batch, S, dims.hidden), 1.0), dims.dtype)
     nb = spec["blocks"] if num_blocks is None else num_blocks
-    blocks = [draw_block(rng, dims) for _ in range(nb)] if with_weights else []
+    blocks = [draw_block(rng, dims, gate_mean) for _ in range(nb)] if with_weights else []
     return Workload(name, dims, layout, x, blocks, seed)
 
 

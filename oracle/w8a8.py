@@ -104,12 +104,15 @@ def round_bf16(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def block_forward_w8a8(x, layout, w, dims) -> np.ndarray:
+def block_forward_w8a8(x, layout, w, dims, taps: bool = False):
     """One block (the steps of oracle.block.block_forward) with each of the
     four projections on rotated W8A8. A bf16 block feeds its projections
     bf16 tensors, so each input (the AdaLN outputs, the attention output, the
     SwiGLU output) is rounded to bf16 before it is rotated and quantized;
-    the weights are the block's bf16 matrices, rotated and quantized per row."""
+    the weights are the block's bf16 matrices, rotated and quantized per row.
+    With ``taps`` returns (output, dict) with the four projection inputs as
+    rounded to bf16 (adaln1, attn_o, adaln2, ffn_h) and the products of the
+    output and down projections (attn_proj, ffn_out)."""
     from . import block as ob
     tags = np.asarray(layout.token_tags)
     tidx = np.asarray(layout.timestep_indices)
@@ -131,9 +134,15 @@ def block_forward_w8a8(x, layout, w, dims) -> np.ndarray:
     kn = ob.rope_3d(ob.rms_norm_heads(k, w["k_norm"], dims.qk_norm_eps), pos, dims.rope_freq_dim, dims.rope_theta)
     o = ob.attention_doc_masked(qn, kn, v, ob.doc_ids(tags), 1.0 / np.sqrt(hd)).reshape(S, W)
     _, _, gate1 = ob.modulation(table, tags, tidx, 0)
-    x_mid = x + gate1 * lin(o, w["w_out"])
+    attn_proj = lin(o, w["w_out"])
+    x_mid = x + gate1 * attn_proj
     b = ob.adaln(x_mid, table, tags, tidx, 1, dims.norm_eps)
     gu = lin(b, w["w_gate_up"])
     h = ob.silu(gu[:, :F]) * gu[:, F:]
     _, _, gate2 = ob.modulation(table, tags, tidx, 1)
-    return x_mid + gate2 * lin(h, w["w_down"])
+    ffn_out = lin(h, w["w_down"])
+    out = x_mid + gate2 * ffn_out
+    if not taps:
+        return out
+    return out, dict(adaln1=round_bf16(a), attn_o=round_bf16(o), adaln2=round_bf16(b), ffn_h=round_bf16(h),
+                     attn_proj=attn_proj, ffn_out=ffn_out)

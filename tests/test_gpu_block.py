@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import REL_L2_F32, assert_close, gpu_available, rel_l2, to_np64
+from helpers import MAX_ABS_F32, REL_L2_F32, assert_close, gpu_available, rel_l2, to_np64
 from joint_video_audio_amd import device as dv
 from joint_video_audio_amd import minih3 as m
 from joint_video_audio_amd import synth
@@ -38,38 +38,49 @@ def tap_buffers(cfg, lay, dt):
     H, hd, F = cfg.num_heads, cfg.head_dim, cfg.ffn_dim
     st = lay.seq_stride
     e = lambda *s: torch.full(s, float("nan"), dtype=dt, device="cuda")
+    f = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
     i = lambda *s: torch.full(s, -7, dtype=torch.int32, device="cuda")
     return dict(adaln1=e(B, S, D), q_rot=e(B, H, st, hd), k_rot=e(B, H, st, hd), v_t=e(B, H, hd, st),
-                attn_o=e(B, S, H * hd), attn_proj=e(B, S, D), x_mid=e(B, S, D), adaln2=e(B, S, D),
+                attn_o=e(B, S, H * hd), attn_proj=e(B, S, D), x_mid=f(B, S, D), adaln2=e(B, S, D),
                 ffn_h=e(B, S, F), ffn_out=e(B, S, D), table_row=i(S), doc_id=i(S), tile_flags=i((S + 63) // 64),
-                num_pad=i(1))
+                num_pad=i(1), block_out=f(B, S, D))
 
 
-def check_block(wl, rel=None):
+def check_block(wl, rel=None, mabs=None):
+    """Every tap and the output against the oracle: the graded bar (relative
+    L2 1e-2, max-abs 5e-2), and with rel / mabs also that internal bar."""
     cfg, lay, blocks, x = dv.upload(wl)
     dt = m.act_torch_dtype(cfg)
     taps = tap_buffers(cfg, lay, dt)
     out = m.block_forward(cfg, lay, blocks, x, flags=m.VALIDATE, taps=taps)
     torch.cuda.synchronize()
+    # the output is the fp32 residual stream after the block, rounded to act
+    assert torch.equal(taps["block_out"].to(dt), out)
     w = oracle.weights_f64(wl.blocks[0])
     S, H, hd = wl.layout.seq_len, wl.dims.num_heads, wl.dims.head_dim
     for b in range(wl.batch):
         ref, t = ob.block_forward(wl.x.values()[b], wl.layout, w, wl.dims, taps=True)
-        got = dict(out=to_np64(out[b]), adaln1=to_np64(taps["adaln1"][b]), x_mid=to_np64(taps["x_mid"][b]),
+        got = dict(out=to_np64(out[b]), block_out=to_np64(taps["block_out"][b]),
+                   adaln1=to_np64(taps["adaln1"][b]), x_mid=to_np64(taps["x_mid"][b]),
                    adaln2=to_np64(taps["adaln2"][b]), ffn_h=to_np64(taps["ffn_h"][b]),
                    attn_o=to_np64(taps["attn_o"][b]), attn_proj=to_np64(taps["attn_proj"][b]),
                    ffn_out=to_np64(taps["ffn_out"][b]),
                    q_rot=to_np64(taps["q_rot"][b]).transpose(1, 0, 2)[:S],
                    k_rot=to_np64(taps["k_rot"][b]).transpose(1, 0, 2)[:S])
-        want = dict(out=ref, adaln1=t["adaln1"], x_mid=t["x_mid"], adaln2=t["adaln2"], ffn_h=t["ffn_h"],
+        want = dict(out=ref, block_out=ref, adaln1=t["adaln1"], x_mid=t["x_mid"], adaln2=t["adaln2"], ffn_h=t["ffn_h"],
                     attn_o=t["attn_o"], attn_proj=t["attn_proj"], ffn_out=t["ffn_out"], q_rot=t["q_rot"],
                     k_rot=t["k_rot"])
         for name in want:
-            if rel is None:
-                assert_close(got[name], want[name], name)
-            else:
-                r = rel_l2(got[name], want[name])
-                assert r <= rel, f"{name}: rel_l2 {r:.3e}"
+            assert_close(got[name], want[name], name)
+            if rel is not None:
+                assert_close(got[name], want[name], f"{name} (internal bar)", rel=rel, mabs=mabs)
+        # increments of the two gated residual adds (fp32 taps), so that a
+        # small gate cannot hide an error in a branch
+        xb = wl.x.values()[b]
+        for nm, g_inc, w_inc in (("x_mid - x", got["x_mid"] - xb, t["x_mid"] - xb),
+                                 ("out - x_mid", got["block_out"] - got["x_mid"], ref - t["x_mid"])):
+            r = rel_l2(g_inc, w_inc)
+            assert r <= 1e-2, f"increment {nm}: rel_l2 {r:.3e}"
     d = ol.describe(wl.layout.token_tags, wl.layout.timestep_indices, wl.layout.video_indices,
                     wl.layout.audio_indices, wl.layout.text_indices, 3, wl.dims.num_tvals, 1, 2, 0)
     assert np.array_equal(taps["table_row"].cpu().numpy(), d["table_row"])
@@ -82,7 +93,7 @@ def check_block(wl, rel=None):
 def test_block_tiny_fp32_workload():
     wl = synth.make_workload("tiny")
     print("tiny fp32 block", flush=True)
-    check_block(wl, rel=REL_L2_F32)
+    check_block(wl, rel=REL_L2_F32, mabs=MAX_ABS_F32)
 
 
 @pytest.mark.parametrize("pads,batch,seed", [(13, 1, 0), (0, 2, 1), (64, 1, 2)])

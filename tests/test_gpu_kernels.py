@@ -162,7 +162,7 @@ def test_attention_doc_mask(S, pads):
     print(f"attention S={S} pads={len(pads)}", flush=True)
     H = 3
     cfg, lay, (qd, kd, vtd), (q, k, v), tags = attention_case(S, H, pads, seed=S, B=2, sharp=1.0)
-    out = m.attention_packed(cfg, lay, qd, kd, vtd)
+    out = m.attention_headmajor(cfg, lay, qd, kd, vtd)
     torch.cuda.synchronize()
     doc = ob.doc_ids(tags)
     for b in range(2):
@@ -177,7 +177,7 @@ def test_attention_sharp(S, pads):
     # peaked softmax: a wrong mask, key order or rotation would show
     H = 2
     cfg, lay, (qd, kd, vtd), (q, k, v), tags = attention_case(S, H, pads, seed=7, sharp=4.0)
-    out = m.attention_packed(cfg, lay, qd, kd, vtd)
+    out = m.attention_headmajor(cfg, lay, qd, kd, vtd)
     torch.cuda.synchronize()
     ref = ob.attention_doc_masked(q[0, :, :S].transpose(1, 0, 2), k[0, :, :S].transpose(1, 0, 2),
                                   v[0, :, :S].transpose(1, 0, 2), ob.doc_ids(tags), 1 / math.sqrt(128))
@@ -187,21 +187,75 @@ def test_attention_sharp(S, pads):
 def test_attention_f32():
     S, H = 150, 2
     cfg, lay, (qd, kd, vtd), (q, k, v), tags = attention_case(S, H, [10, 149], seed=2, dtype="f32")
-    out = m.attention_packed(cfg, lay, qd, kd, vtd)
+    out = m.attention_headmajor(cfg, lay, qd, kd, vtd)
     torch.cuda.synchronize()
     ref = ob.attention_doc_masked(q[0, :, :S].transpose(1, 0, 2), k[0, :, :S].transpose(1, 0, 2),
                                   v[0, :, :S].transpose(1, 0, 2), ob.doc_ids(tags), 1 / math.sqrt(128))
     assert rel_l2(to_np64(out[0]).reshape(S, H, 128), ref) <= REL_L2_F32
 
 
+def packed_inputs(q, k, v, S, dtype):
+    """[B, H, stride, hd] values -> device q, k, v [B, S, H, hd] (exact)."""
+    outs = []
+    for a in (q, k, v):
+        p = np.ascontiguousarray(a[:, :, :S].transpose(0, 2, 1, 3))
+        outs.append(bf16_dev(p) if dtype == "bf16" else torch.from_numpy(p.astype(np.float32)).cuda())
+    return outs
+
+
+@pytest.mark.parametrize("S,pads,B,dtype,sharp", [(200, [3, 77, 150, 151, 199], 2, "bf16", 1.0),
+                                                  (517, list(range(480, 517)), 1, "bf16", 1.0),
+                                                  (700, [0] + list(range(256, 320)), 1, "bf16", 4.0),
+                                                  (1, [], 1, "bf16", 1.0), (65, [64], 1, "bf16", 1.0),
+                                                  (150, [10, 149], 1, "f32", 1.0)])
+def test_attention_packed_entry(S, pads, B, dtype, sharp):
+    # the boundary entry point: packed [B, S, H, hd] q / k / v after norm and
+    # rotary, staged by the library into the kernels' layouts
+    print(f"attention packed entry S={S} pads={len(pads)} B={B} {dtype}", flush=True)
+    H = 3
+    cfg, lay, (qd, kd, vtd), (q, k, v), tags = attention_case(S, H, pads, seed=S + 11, B=B, dtype=dtype,
+                                                              sharp=sharp)
+    qp, kp, vp = packed_inputs(q, k, v, S, dtype)
+    out = m.attention_packed(cfg, lay, qp, kp, vp)
+    ref_hm = m.attention_headmajor(cfg, lay, qd, kd, vtd)
+    torch.cuda.synchronize()
+    # the staging is a copy: the two entries give the same bits
+    assert torch.equal(out, ref_hm)
+    doc = ob.doc_ids(tags)
+    for b in range(B):
+        ref = ob.attention_doc_masked(q[b, :, :S].transpose(1, 0, 2), k[b, :, :S].transpose(1, 0, 2),
+                                      v[b, :, :S].transpose(1, 0, 2), doc, 1 / math.sqrt(128))
+        got = to_np64(out[b]).reshape(S, H, 128)
+        if dtype == "bf16":
+            assert_close(got, ref, f"attention packed b={b}")
+        else:
+            assert rel_l2(got, ref) <= REL_L2_F32
+
+
+def test_attention_packed_entry_errors():
+    S, H = 100, 2
+    cfg, lay, _, (q, k, v), _ = attention_case(S, H, [5], seed=3)
+    qp, kp, vp = packed_inputs(q, k, v, S, "bf16")
+    with pytest.raises(m.Minih3Error) as e:
+        m.attention_packed(cfg, lay, qp, kp, vp, flags=m.ASSUME_PADLESS | m.VALIDATE)
+    assert e.value.status == m.E_NEEDS_MASK
+    ws = m.alloc_workspace(m.attention_workspace_bytes(cfg, 1, S) - 1)
+    with pytest.raises(m.Minih3Error) as e:
+        m.attention_packed(cfg, lay, qp, kp, vp, workspace=ws)
+    assert e.value.status == m.E_WORKSPACE
+    with pytest.raises(m.Minih3Error) as e:
+        m.attention_packed(cfg, lay, qp, kp, vp, out=qp.view(1, S, H * 128))
+    assert e.value.status == m.E_ARG
+
+
 def test_attention_padless_flag_matches_masked_path_bit_exact():
     S, H = 333, 2
     cfg, lay, (qd, kd, vtd), _, _ = attention_case(S, H, [], seed=4)
-    a = m.attention_packed(cfg, lay, qd, kd, vtd)
-    b = m.attention_packed(cfg, lay, qd, kd, vtd, flags=m.ASSUME_PADLESS | m.VALIDATE)
+    a = m.attention_headmajor(cfg, lay, qd, kd, vtd)
+    b = m.attention_headmajor(cfg, lay, qd, kd, vtd, flags=m.ASSUME_PADLESS | m.VALIDATE)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     cfg, lay, (qd, kd, vtd), _, _ = attention_case(S, H, [7], seed=4)
     with pytest.raises(m.Minih3Error) as e:
-        m.attention_packed(cfg, lay, qd, kd, vtd, flags=m.ASSUME_PADLESS | m.VALIDATE)
+        m.attention_headmajor(cfg, lay, qd, kd, vtd, flags=m.ASSUME_PADLESS | m.VALIDATE)
     assert e.value.status == m.E_NEEDS_MASK

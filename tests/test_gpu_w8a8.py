@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import gpu_available
+from helpers import gpu_available, rel_l2
 from joint_video_audio_amd import device as dv
 from joint_video_audio_amd import minih3 as m
 from joint_video_audio_amd import synth
@@ -174,14 +174,77 @@ def test_block_w8a8_gate_zero_is_identity():
     assert torch.equal(out, x)
 
 
+def code_flips(x_gpu: np.ndarray, x_ref: np.ndarray):
+    """How the GPU's bf16 projection inputs and the oracle's differ, and what
+    that does to the int8 codes: (fraction of differing bf16 elements,
+    fraction of rows whose scale differs, fraction of differing codes,
+    largest code change)."""
+    qg, sg = ow.rotate_quantize(x_gpu)
+    qr, sr = ow.rotate_quantize(x_ref)
+    dq = np.abs(qg.astype(np.int32) - qr.astype(np.int32))
+    return (float(np.mean(x_gpu != x_ref)), float(np.mean(sg != sr)), float(np.mean(dq > 0)), int(dq.max()))
+
+
 def test_block_w8a8_full_width():
     # the clip-scale block's widths (hidden 5376, 56 x 128 heads, FFN 14336) on 300 rows
     print("block w8a8 full width", flush=True)
+    from oracle import block as ob
     from oracle import weights_f64
-    from helpers import assert_close, to_np64
+    from helpers import assert_close, assert_close_bf16_storage, to_np64
     dims = synth.ModelDims(num_tvals=8)
     segs = [("text", 40), ("audio", 36), ("video", 216, (2, 9, 12))]
-    wl, x, out = w8a8_block_case(dims, segs, (2, 9, 12), 8, seed=5, batch=1)
-    ref = ow.block_forward_w8a8(wl.x.values()[0], wl.layout, weights_f64(wl.blocks[0]), dims)
+    wl = synth.make_custom(dims, segs, (2, 9, 12), 8, seed=5, batch=1)
+    cfg, lay, blocks, x = dv.upload(wl)
+    qb = [m.DeviceBlockW8A8.from_block(b) for b in blocks]
+    B, S, D = 1, lay.seq_len, dims.hidden
+    W, F = dims.num_heads * dims.head_dim, dims.ffn_dim
+    bf = lambda *sh: torch.empty(*sh, dtype=torch.bfloat16, device="cuda")
+    taps = dict(adaln1=bf(B, S, D), attn_o=bf(B, S, W), attn_proj=bf(B, S, D), adaln2=bf(B, S, D),
+                ffn_h=bf(B, S, F), ffn_out=bf(B, S, D))
+    out = m.block_forward_w8a8(cfg, lay, qb, x, flags=m.VALIDATE, taps=taps)
+    # the library's codes of each projection input
+    gq = {k: m.rotate_quantize(taps[k][0]) for k in ("adaln1", "attn_o", "adaln2", "ffn_h")}
+    torch.cuda.synchronize()
+    w = weights_f64(wl.blocks[0])
+    t = {k: to_np64(v[0]) for k, v in taps.items()}
+
+    # 1. Each projection on the kernel's own bf16 inputs: the library's codes
+    # equal the oracle's bit for bit, and the product (and the epilogue that
+    # consumes it) equals the oracle's exact integer product dequantized
+    for k in gq:
+        rq, rs = ow.rotate_quantize(t[k])
+        assert np.array_equal(gq[k][0].cpu().numpy(), rq), k
+        assert np.array_equal(gq[k][1].cpu().numpy().view(np.uint32), rs.view(np.uint32)), k
+    check_own = {"attn_proj": ow.linear_w8a8(t["attn_o"], w["w_out"]),
+                 "ffn_out": ow.linear_w8a8(t["ffn_h"], w["w_down"])}
+    gu = ow.linear_w8a8(t["adaln2"], w["w_gate_up"])
+    check_own["ffn_h"] = ob.silu(gu[:, :F]) * gu[:, F:]
+    for k, want in check_own.items():
+        r = assert_close_bf16_storage(t[k], want, f"w8a8 {k} on its own inputs")
+        print(f"w8a8 {k} on the kernel's own inputs: rel_l2={r[0]:.3e} max_abs={r[1]:.3e}", flush=True)
+
+    # 2. End to end against the W8A8 oracle, whose projection inputs are its
+    # own fp64 activations rounded to bf16. Where the two bf16 activations
+    # differ (summation order upstream), codes change: when a row's largest
+    # element moves by one bf16 ulp its scale moves by up to 2^-8 and every
+    # code of the row whose scaled value sits within that much of a rounding
+    # boundary changes by one step.
+    ref, rt = ow.block_forward_w8a8(wl.x.values()[0], wl.layout, w, dims, taps=True)
+    for k in ("adaln1", "attn_o", "adaln2", "ffn_h"):
+        f_el, f_row, f_code, dmax = code_flips(t[k], rt[k])
+        print(f"w8a8 flips {k}: bf16 elements differing {f_el:.4f}, row scales differing {f_row:.4f}, "
+              f"codes differing {f_code:.5f}, largest code change {dmax}", flush=True)
+    # A product whose input codes flipped differs from the oracle's by about
+    # its quantization error: bound it by the bf16 bar plus twice the
+    # oracle's own quantization error of that product (W8A8 against the
+    # exact product of the same bf16 input)
+    exact = {"attn_proj": rt["attn_o"] @ w["w_out"].T, "ffn_out": rt["ffn_h"] @ w["w_down"].T}
+    for k in ("attn_proj", "ffn_out"):
+        r = rel_l2(t[k], rt[k])
+        q_err = rel_l2(rt[k], exact[k])
+        print(f"w8a8 {k} end to end: rel_l2={r:.3e} max_abs={np.abs(t[k] - rt[k]).max():.3e}; the oracle's own "
+              f"quantization error {q_err:.3e}", flush=True)
+        assert r <= 1e-2 + 2 * q_err, (k, r, q_err)
     r, mx = assert_close(to_np64(out)[0], ref, "w8a8 block, full width", mabs=W8A8_BLOCK_MAX_ABS)
-    print(f"w8a8 block full width: rel_l2={r:.3e} max_abs={mx:.3e}", flush=True)
+    print(f"w8a8 block full width: rel_l2={r:.3e} max_abs={mx:.3e} (plain fp64 block: rel_l2 "
+          f"{rel_l2(to_np64(out)[0], ob.block_forward(wl.x.values()[0], wl.layout, w, dims)):.3e})", flush=True)

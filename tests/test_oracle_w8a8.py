@@ -127,3 +127,28 @@ def test_w8a8_block_tracks_the_plain_block():
     w0["adaln_table"][:, :, 2] = 0.0
     w0["adaln_table"][:, :, 5] = 0.0
     assert np.array_equal(ow.block_forward_w8a8(x, wl.layout, w0, dims), x)
+
+
+def test_codes_equal_an_fp64_hadamard_away_from_rounding_boundaries():
+    # The oracle fixes a float32 butterfly order; the codes it decides must be
+    # those of the exact rotation (scipy's Hadamard matrix in float64, exact
+    # division and rounding) wherever the exact scaled value v * 127 / amax
+    # lies farther from a rounding boundary (x.5) than float32 arithmetic can
+    # move it: 7 butterfly stages, the normalisation, the division and the
+    # product each err by at most 2^-24 relative, so |t| <= 127 moves by less
+    # than 127 * 12 * 2^-24 < 1e-4.
+    H = hadamard(128).astype(np.float64) / np.sqrt(128.0)
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((256, 5376)) * rng.uniform(0.1, 10.0, (256, 1))).astype(np.float32)
+    x[3, 100] = 40.0  # a row with one dominant value
+    q, s = ow.rotate_quantize(x)
+    xr = np.concatenate([x[:, 128 * b:128 * (b + 1)].astype(np.float64) @ H for b in range(5376 // 128)], axis=1)
+    amax = np.abs(xr).max(axis=1, keepdims=True)
+    t = xr * (127.0 / amax)
+    q64 = np.clip(np.rint(t), -127, 127)
+    near = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+    differ = q.astype(np.float64) != q64
+    assert not np.any(differ & ~near), int((differ & ~near).sum())
+    assert differ.sum() <= near.sum()
+    # the scales are amax / 127 of the exact rotation to float32 accuracy
+    assert np.all(np.abs(s.astype(np.float64) - amax[:, 0] / 127.0) <= 1e-6 * amax[:, 0] / 127.0)
