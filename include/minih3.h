@@ -41,6 +41,7 @@ typedef enum {
   MINIH3_E_ARG = -1,           /* null pointer, bad size or unsupported dims   */
   MINIH3_E_WORKSPACE = -2,     /* workspace null or smaller than required      */
   MINIH3_E_UNSUPPORTED = -3,   /* a dims combination the kernels do not cover  */
+  MINIH3_E_SCRATCH = -4,       /* request larger than an allocation-free entry point's fixed scratch */
   MINIH3_E_LAYOUT_TAG = -10,   /* a tag outside {-1, 0 .. num_tags-1}          */
   MINIH3_E_LAYOUT_TVAL = -11,  /* timestep index outside [0, num_tvals) on a non-padding row */
   MINIH3_E_LAYOUT_INDEX = -12, /* index out of range, a row addressed twice, or a row of another modality */
@@ -277,6 +278,21 @@ int minih3_adaln_table_workspace_bytes(const minih3_config* cfg, int32_t embed_d
  * accumulation, fp32 output); embed_dim % 32 == 0. fp32: embed_dim % 16 == 0. */
 int minih3_adaln_table(const minih3_config* cfg, const float* emb, int32_t embed_dim, const void* w_proj,
                        const void* b_proj, float* table, void* workspace, size_t workspace_bytes, void* stream);
+
+/* minih3_adaln_table without a workspace, for callers that cannot
+ * allocate device memory: code recorded under HIP graph capture, serving
+ * loops that must not call hipMalloc, harnesses that forbid it. The caller
+ * passes the inputs and the output as for minih3_adaln_table; the bf16
+ * SiLU(emb) operand lives in a fixed 1 MiB device array of the library
+ * (one per device, held until the process ends). Limit:
+ * minih3_adaln_table_workspace_bytes(cfg, embed_dim) <= 1 MiB (e.g. up to
+ * 192 timestep values at embed_dim 2688), else MINIH3_E_SCRATCH before
+ * anything is enqueued. Every call on a device shares that array: calls
+ * that overlap on one device (other streams, other threads) race; calls
+ * in order on one stream do not. Nothing is allocated or freed; the first
+ * call on a device looks the array's address up once. */
+int minih3_adaln_table_noalloc(const minih3_config* cfg, const float* emb, int32_t embed_dim, const void* w_proj,
+                               const void* b_proj, float* table, void* stream);
 
 /* ---- Model edges: the packed sequence in, the velocities out ----
  * Page "MiniMaxH3Transformer3DModel": Parameters in_channels, patch_size,

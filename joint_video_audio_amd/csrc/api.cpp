@@ -20,6 +20,34 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// ---- the allocation-free AdaLN table build ----
+// Scratch of minih3_adaln_table_noalloc: the bf16 SiLU(emb) operand of the
+// table projection (padded rows, fragment order). A device variable: every
+// device the library runs on holds its own copy until the process ends, and
+// every call on that device shares it.
+constexpr size_t kNoallocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the array's name is a host-side stand-in, not a device address).
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MINIH3_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MINIH3_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MINIH3_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MINIH3_OK;
+}
+
 // Kernel ids reported by minih3_profile_collect.
 enum KernelId {
   kKLayout = 0, kKTiles, kKAdaLN1, kKQKV, kKQKNormRope, kKAttnPrep, kKAttention, kKOutProj, kKAdaLN2, kKGateUp,
@@ -681,6 +709,7 @@ const char* minih3_status_string(int s) {
     case MINIH3_E_ARG: return "invalid argument";
     case MINIH3_E_WORKSPACE: return "workspace missing or too small";
     case MINIH3_E_UNSUPPORTED: return "unsupported dimensions";
+    case MINIH3_E_SCRATCH: return "request exceeds the fixed scratch of an allocation-free entry point";
     case MINIH3_E_LAYOUT_TAG: return "layout: tag outside {-1, 0 .. num_tags-1}";
     case MINIH3_E_LAYOUT_TVAL: return "layout: timestep index outside [0, num_tvals) on a non-padding row";
     case MINIH3_E_LAYOUT_INDEX: return "layout: index out of range, duplicated, or addressing another modality";
@@ -887,6 +916,20 @@ int minih3_adaln_table(const minih3_config* c, const float* emb, int32_t embed_d
   return MINIH3_OK;
 }
 
+
+int minih3_adaln_table_noalloc(const minih3_config* c, const float* emb, int32_t embed_dim, const void* w_proj,
+                               const void* b_proj, float* table, void* stream) {
+  size_t need = 0;
+  int s = minih3_adaln_table_workspace_bytes(c, embed_dim, &need);
+  if (s) return s;
+  if (need > kNoallocScratchBytes) return MINIH3_E_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    s = noalloc_scratch(&ws);
+    if (s) return s;
+  }
+  return minih3_adaln_table(c, emb, embed_dim, w_proj, b_proj, table, ws, need, stream);
+}
 
 int minih3_edges_workspace_bytes(const minih3_config* c, const minih3_edges* e, int32_t seq_len, size_t* bytes) {
   int s = check_edges(c, e);

@@ -21,7 +21,7 @@ BF16, F32 = 0, 1
 VALIDATE, ASSUME_PADLESS, PROFILE = 1, 2, 4
 
 OK = 0
-E_ARG, E_WORKSPACE, E_UNSUPPORTED = -1, -2, -3
+E_ARG, E_WORKSPACE, E_UNSUPPORTED, E_SCRATCH = -1, -2, -3, -4
 E_LAYOUT_TAG, E_LAYOUT_TVAL, E_LAYOUT_INDEX, E_LAYOUT_PAD, E_NEEDS_MASK = -10, -11, -12, -13, -14
 E_HIP = -20
 
@@ -136,6 +136,8 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.POINTER(ctypes.c_size_t)]
         L.minih3_adaln_table.argtypes = [ctypes.POINTER(Config), _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t,
                                          _P]
+        L.minih3_adaln_table_noalloc.argtypes = [ctypes.POINTER(Config), _P, ctypes.c_int32, _P, _P, _P, _P]
+        L.minih3_adaln_table_noalloc.restype = ctypes.c_int
         L.minih3_edges_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Edges), ctypes.c_int32,
                                                    ctypes.POINTER(ctypes.c_size_t)]
         L.minih3_embed_inputs.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout), ctypes.POINTER(_Edges), _P,
@@ -185,7 +187,7 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
             "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
             "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
-            "minih3_adaln_table", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
+            "minih3_adaln_table", "minih3_adaln_table_noalloc", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
             "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
             "minih3_block_forward_w8a8", "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
             "minih3_linear_lora", "minih3_euler_step", "minih3_denoise_step_workspace_bytes",
@@ -501,6 +503,23 @@ def adaln_table(cfg: Config, emb: torch.Tensor, w_proj: torch.Tensor, b_proj: Op
         workspace = alloc_workspace(adaln_table_workspace_bytes(cfg, E), emb.device)
     _check(lib().minih3_adaln_table(ctypes.byref(cfg), _ptr(emb), E, _ptr(w_proj), _ptr(b_proj), _ptr(out),
                                     _ptr(workspace), workspace.numel(), _stream()), "adaln_table")
+    return out
+
+
+def adaln_table_noalloc(cfg: Config, emb: torch.Tensor, w_proj: torch.Tensor, out: torch.Tensor,
+                        b_proj: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """adaln_table into a caller-provided `out` with no workspace: the library
+    uses its fixed per-device scratch (see minih3_adaln_table_noalloc)."""
+    dt = act_torch_dtype(cfg)
+    T, V, D = cfg.num_tags, cfg.num_tvals, cfg.hidden
+    E = emb.shape[-1]
+    _req(emb, torch.float32, "emb", V * E)
+    _req(w_proj, dt, "w_proj", T * 6 * D * E)
+    if b_proj is not None:
+        _req(b_proj, dt, "b_proj", T * 6 * D)
+    _req(out, torch.float32, "table", T * V * 6 * D)
+    _check(lib().minih3_adaln_table_noalloc(ctypes.byref(cfg), _ptr(emb), E, _ptr(w_proj), _ptr(b_proj), _ptr(out),
+                                            _stream()), "adaln_table_noalloc")
     return out
 
 
