@@ -432,6 +432,66 @@ def lora(reps: int, warmup: int, M: int = 32768, rank: int = 256):
     return res
 
 
+def denoise_step(wl, reps: int, warmup: int, num_blocks: int = 4, rank: int = 256):
+    """Time one denoising step at the workload's scale: input projections,
+    `num_blocks` bf16 blocks each with an unmerged rank-256 adapter on its
+    four projections, the output heads and the Euler update of the latents
+    (minih3_denoise_step), beside the same step without adapters. Weights are
+    drawn on the device (torch, seeded) with the distributions of the
+    synthetic recipe; the layout, latents and edges are the workload's."""
+    import numpy as np
+    import torch
+    from joint_video_audio_amd import device as dv
+    from joint_video_audio_amd import minih3 as m
+    from joint_video_audio_amd import synth
+    dims = wl.dims
+    cfg = dv.config_for(dims)
+    lay = dv.layout_for(wl, batch=1)
+    e = synth.make_edges(dims, wl.layout, seed=1)
+    D, W, F = dims.hidden, dims.qkv_width, dims.ffn_dim
+    g = torch.Generator(device="cuda").manual_seed(7)
+    nrm = lambda *sh, std=0.02: (torch.randn(*sh, device="cuda", generator=g) * std).to(torch.bfloat16)  # noqa: E731
+    blocks, loras = [], []
+    for _ in range(num_blocks):
+        tab = torch.randn(dims.num_tags, dims.num_tvals, 6, D, device="cuda", generator=g) * 0.1
+        qn = 1 + 0.02 * torch.randn(128, device="cuda", generator=g)
+        kn = 1 + 0.02 * torch.randn(128, device="cuda", generator=g)
+        b = m.DeviceBlock(nrm(3 * W, D), nrm(D, W), nrm(2 * F, D), nrm(D, F), qn, kn, tab.contiguous())
+        shapes = synth.lora_shapes(dims)
+        a = {n: nrm(rank, K, std=K ** -0.5) for n, (N, K) in shapes.items()}
+        bm = {n: nrm(N, rank) for n, (N, K) in shapes.items()}
+        blocks.append(b)
+        loras.append(m.DeviceBlockLora.from_block(b, a, bm))
+    # the two-time workload's values are the (sigma_now, sigma_next) pairs of a k-point grid
+    k = int(round(dims.num_tvals ** 0.5))
+    assert k * k == dims.num_tvals, "a square number of timestep values (two-time pairs)"
+    grid = (1.0 - np.arange(k) / k).astype(np.float32)
+    v = np.arange(dims.num_tvals)
+    now, nxt = dv.f32(grid[v // k]), dv.f32(grid[v % k])
+    video0, audio0, text = dv.f32(e.video), dv.f32(e.audio), dv.to_device(e.text)
+    de = dv.edges_for(e)
+    res = {"blocks": num_blocks, "rank": rank, "rows": lay.seq_len, "reps": reps,
+           "note": "weights drawn on the device (seeded torch) with the synthetic recipe's distributions"}
+    for label, lo in (("with_adapters", loras), ("without_adapters", None)):
+        video, audio = video0.clone(), audio0.clone()
+        for _ in range(warmup):
+            m.denoise_step(cfg, lay, blocks, de, now, nxt, video, audio, text, loras=lo, lora_scale=1.0)
+        st = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(st)
+        for i in range(reps):
+            m.denoise_step(cfg, lay, blocks, de, now, nxt, video, audio, text, loras=lo, lora_scale=1.0)
+            evs[i + 1].record(st)
+        torch.cuda.synchronize()
+        ms = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]))
+        res[label] = {"ms_per_step": round(ms, 3), "ms_per_block": round(ms / num_blocks, 3),
+                      "rows_per_s_per_block": round(lay.seq_len / (ms / num_blocks / 1e3), 1)}
+    res["adapter_overhead"] = round(res["with_adapters"]["ms_per_step"] / res["without_adapters"]["ms_per_step"] - 1,
+                                    4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +506,8 @@ def main():
     ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--no-w8a8-block", action="store_true")
     ap.add_argument("--no-lora", action="store_true")
+    ap.add_argument("--no-denoise-step", action="store_true")
+    ap.add_argument("--no-clock", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -510,7 +572,8 @@ def main():
         m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws, flags=m.PROFILE)
     torch.cuda.synchronize()
     kern = m.profile_collect()
-    clock = observed_clock(lambda: m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws))
+    clock = None if a.no_clock else observed_clock(lambda: m.block_forward(cfg, lay, blocks, x, out=out,
+                                                                           workspace=ws))
 
     gemm, attn = flop_counts(wl.dims, wl.layout)
     t_block = ms_step / 1e3 / nb
@@ -565,6 +628,10 @@ def main():
         res["w8a8"] = w8a8(reps=10, warmup=2)
     if not a.no_lora and a.workload == "clip32k":
         res["lora"] = lora(reps=5, warmup=1)
+    if not a.no_denoise_step and a.workload == "clip32k":
+        del blocks, x, out, ws
+        torch.cuda.empty_cache()
+        res["denoise_step"] = denoise_step(wl, reps=3, warmup=1)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)

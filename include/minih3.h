@@ -263,6 +263,36 @@ int minih3_time_embed(const minih3_time_config* tc, const minih3_time_mlp* base,
                       const minih3_time_mlp* endpoint, const float* r, float gate, int32_t num_tvals, float* emb,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Unmerged adapter of one timestep MLP (header table of the HyperFlow page:
+ * LoRA on both time embedders), fp32: layer 1 computes
+ * W1 s + lora_scale * B1 (A1 s) + b1, layer 2 likewise with A2, B2; each as
+ * u = lora_scale * A x, then [x | u] . [W | B]^T with the packed matrices.
+ * a1 [rank, freq_dim], packed1 [hidden_dim, freq_dim + rank] = [W1 | B1],
+ * a2 [rank, hidden_dim], packed2 [embed_dim, hidden_dim + rank] = [W2 | B2]
+ * (minih3_lora_pack_weight with MINIH3_F32). */
+typedef struct {
+  const float* a1;
+  const float* packed1;
+  const float* a2;
+  const float* packed2;
+} minih3_time_mlp_lora;
+
+/* Bytes of workspace minih3_time_embed_lora needs (rank % 16 == 0). */
+int minih3_time_embed_lora_workspace_bytes(const minih3_time_config* tc, int32_t num_tvals, int32_t rank,
+                                           size_t* bytes);
+
+/* minih3_time_embed with an unmerged adapter on each timestep MLP: base_lora
+ * for the base MLP, endpoint_lora for the endpoint one (required when
+ * endpoint is set). The w1 and w2 of base / endpoint are not read (the
+ * packed matrices hold them); the biases are. lora_scale = scale * alpha /
+ * rank. Split-K partial sums are added in a fixed order, so repeated calls
+ * give identical bits. */
+int minih3_time_embed_lora(const minih3_time_config* tc, const minih3_time_mlp* base,
+                           const minih3_time_mlp_lora* base_lora, const float* t, const minih3_time_mlp* endpoint,
+                           const minih3_time_mlp_lora* endpoint_lora, const float* r, float gate, int32_t num_tvals,
+                           int32_t rank, float lora_scale, float* emb, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Bytes of workspace minih3_adaln_table needs (0 for fp32 activations). */
 int minih3_adaln_table_workspace_bytes(const minih3_config* cfg, int32_t embed_dim, size_t* bytes);
 
@@ -441,6 +471,35 @@ int minih3_euler_step(const float* x, const float* velocity, float* x_next, int3
                       int32_t channels, const int32_t* indices, const int32_t* timestep_indices, int32_t seq_len,
                       const float* sigma_now, const float* sigma_next, int32_t num_tvals, void* stream);
 
+/* Unmerged adapters of a block's four projections (header table of the
+ * HyperFlow page: LoRA on the attention and feed-forward layers; `forward`
+ * of the model page: a scale for the LoRA layers). Projection P with base
+ * weight W [N, K] computes x W^T + lora_scale * (x A^T) B^T, evaluated as in
+ * minih3_linear_lora: t = lora_scale * x A^T (act, in the workspace), then
+ * one projection of [x | t] against packed = [W | B] with P's fused
+ * epilogue (q/k norm + rotary, gated residual, SwiGLU). */
+typedef struct {
+  const void* a_qkv;     const void* packed_qkv;      /* [rank, D], [3W, D + rank] */
+  const void* a_out;     const void* packed_out;      /* [rank, W], [D, W + rank]  */
+  const void* a_gate_up; const void* packed_gate_up;  /* [rank, D], [2F, D + rank] */
+  const void* a_down;    const void* packed_down;     /* [rank, F], [D, F + rank]  */
+} minih3_block_lora;
+
+/* Bytes of workspace minih3_block_forward_lora needs. */
+int minih3_workspace_bytes_lora(const minih3_config* cfg, int32_t batch, int32_t seq_len, int32_t rank,
+                                size_t* bytes);
+
+/* minih3_block_forward with an unmerged adapter on every projection of
+ * every block: loras[i] belongs to blocks[i], whose w_qkv, w_out,
+ * w_gate_up and w_down are not read (packed holds them); q_norm, k_norm
+ * and adaln_table are. lora_scale = scale * alpha / rank. bf16: rank a
+ * multiple of 256; fp32: of 64. Taps as in minih3_block_forward (attn_proj
+ * and ffn_out include the adapter). */
+int minih3_block_forward_lora(const minih3_config* cfg, const minih3_layout* layout,
+                              const minih3_block_weights* blocks, const minih3_block_lora* loras, int32_t num_blocks,
+                              int32_t rank, float lora_scale, const void* x_in, void* x_out, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, minih3_taps* taps, void* stream);
+
 /* One denoising step of the model on the packed layout: the input
  * projections build x from the video / audio latents and the embedded text
  * rows (minih3_embed_inputs), the block chain runs on it
@@ -460,6 +519,9 @@ typedef struct {
   const minih3_edges* edges;
   const float* sigma_now;                    /* [num_tvals] */
   const float* sigma_next;                   /* [num_tvals] */
+  const minih3_block_lora* loras;            /* per block, or NULL (not with qblocks) */
+  int32_t lora_rank;                         /* rank of loras                */
+  float lora_scale;                          /* scale * alpha / rank         */
 } minih3_step_weights;
 
 /* Bytes of workspace minih3_denoise_step needs. */

@@ -154,6 +154,7 @@ struct Workspace {
   float* rope;    // bf16: [S, 3 rope_freq_dim] (cos, sin) of every rotation pair of every row
   int8_t* qx;     // rotated W8A8: int8 codes of a projection's input rows
   float* sx;      // and their scales
+  void* lora_t;   // unmerged adapters: lora_scale * x A^T of one projection [M, rank]
   uint64_t* masks;
   void* attn_scratch;
   int32_t *list_real, *list_pad, *meta, *counts, *npad;
@@ -185,7 +186,7 @@ size_t tiles_bytes(int B, int S, int H, int32_t** list_real, int32_t** list_pad,
   return off;
 }
 
-Workspace carve(const minih3_config* c, int B, int S, char* base, bool w8a8 = false) {
+Workspace carve(const minih3_config* c, int B, int S, char* base, bool w8a8 = false, int lora_rank = 0) {
   Workspace w{};
   const size_t e = act_size(c->act_dtype);
   const size_t D = c->hidden, H = c->num_heads, hd = c->head_dim, F = c->ffn_dim;
@@ -217,6 +218,7 @@ Workspace carve(const minih3_config* c, int B, int S, char* base, bool w8a8 = fa
     w.qx = (int8_t*)take(M * kmax);
     w.sx = (float*)take(4 * M);
   }
+  if (lora_rank > 0) w.lora_t = take(M * (size_t)lora_rank * e);
   w.total = off;
   return w;
 }
@@ -241,7 +243,8 @@ int status_from_err(uint32_t err) {
 template <typename T>
 int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks, int nb,
                const T* x_in, T* x_out, Workspace& w, uint32_t flags, minih3_taps* taps, hipStream_t st,
-               const minih3_block_weights_w8a8* qblocks = nullptr) {
+               const minih3_block_weights_w8a8* qblocks = nullptr, const minih3_block_lora* loras = nullptr,
+               int lora_rank = 0, float lora_scale = 0.f) {
   const int B = L->batch, S = L->seq_len;
   const int D = c->hidden, H = c->num_heads, hd = c->head_dim, F = c->ffn_dim;
   const int Wd = H * hd;
@@ -289,6 +292,21 @@ int run_blocks(const minih3_config* c, const minih3_layout* L, const minih3_bloc
     // w.qx / w.sx (by the AdaLN kernel).
     auto proj = [&](int epi, const T* A, int which, void* C, int N, int K, EpiArgs& ea,
                     bool quantized = false) -> hipError_t {
+      if (loras) {
+        // unmerged adapter: t = lora_scale * A . La^T, then [A | t] . [W | B]^T
+        const minih3_block_lora& lb = loras[i];
+        const void* La = which == 0 ? lb.a_qkv : which == 1 ? lb.a_out : which == 2 ? lb.a_gate_up : lb.a_down;
+        const void* Pw =
+            which == 0 ? lb.packed_qkv : which == 1 ? lb.packed_out : which == 2 ? lb.packed_gate_up : lb.packed_down;
+        EpiArgs et{};
+        et.scale = lora_scale;
+        hipError_t r = launch_gemm<T>(kEpiStoreScaled, A, (const T*)La, w.lora_t, M, lora_rank, K, et, st);
+        if (r != hipSuccess) return r;
+        EpiArgs e2 = ea;
+        e2.a2 = w.lora_t;
+        e2.k2 = lora_rank;
+        return launch_gemm<T>(epi, A, (const T*)Pw, C, M, N, K + lora_rank, e2, st);
+      }
       if (!qblocks) {
         const void* W = which == 0 ? bw.w_qkv : which == 1 ? bw.w_out : which == 2 ? bw.w_gate_up : bw.w_down;
         return launch_gemm<T>(epi, A, (const T*)W, C, M, N, K, ea, st);
@@ -458,25 +476,34 @@ int check_time_config(const minih3_time_config* tc) {
 }
 
 struct TimeWorkspace {
-  float *s[2], *h[2], *part[2];
+  float *s[2], *h[2], *part[2], *u1[2], *u2[2];
   size_t total;
 };
 
 // Per chain (base, endpoint): the sinusoid and the hidden activations in
-// fragment order, and the split-K partial sums of the second layer.
-TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base) {
+// fragment order, and the split-K partial sums of the second layer; with
+// adapters of rank R also each layer's scaled low-rank input (fragment order).
+TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base, int rank = 0) {
   TimeWorkspace w{};
+  const int Kl2 = tc->hidden_dim + rank;  // contraction of the second layer
   const size_t sb = align_up((size_t)padded_rows(M) * tc->freq_dim * 4);
   const size_t hb = align_up((size_t)padded_rows(M) * tc->hidden_dim * 4);
-  const size_t pb = align_up((size_t)skinny_splits(tc->hidden_dim, kTimeSplits) * M * tc->embed_dim * 4);
+  const size_t pb = align_up((size_t)skinny_splits(Kl2, kTimeSplits) * M * tc->embed_dim * 4);
+  const size_t ub = rank > 0 ? align_up((size_t)padded_rows(M) * rank * 4) : 0;
   size_t off = 0;
+  auto take = [&](size_t n) {
+    float* p = base ? (float*)(base + off) : nullptr;
+    off += n;
+    return p;
+  };
   for (int c = 0; c < 2; ++c) {
-    w.s[c] = base ? (float*)(base + off) : nullptr;
-    off += sb;
-    w.h[c] = base ? (float*)(base + off) : nullptr;
-    off += hb;
-    w.part[c] = base ? (float*)(base + off) : nullptr;
-    off += pb;
+    w.s[c] = take(sb);
+    w.h[c] = take(hb);
+    w.part[c] = take(pb);
+    if (rank > 0) {
+      w.u1[c] = take(ub);
+      w.u2[c] = take(ub);
+    }
   }
   w.total = off;
   return w;
@@ -484,17 +511,42 @@ TimeWorkspace carve_time(const minih3_time_config* tc, int M, char* base) {
 
 // The timestep MLP over M timesteps, with the endpoint MLP on r alongside it
 // when `ep` is set (one launch per layer for both); emb = E(t), or the blend
-// (1 - gate) E(t) + gate E'(r).
+// (1 - gate) E(t) + gate E'(r). With adapters (la, and lep for the endpoint
+// MLP) each layer runs unmerged: u = ls * A x, then [x | u] . [W | B]^T
+// (the packed matrices replace w1 and w2; the biases stay).
 int time_mlps(const minih3_time_config* tc, const minih3_time_mlp* m, const float* t, const minih3_time_mlp* ep,
-              const float* r, float gate, int M, float* emb, TimeWorkspace& w, hipStream_t st) {
+              const float* r, float gate, int M, float* emb, TimeWorkspace& w, hipStream_t st,
+              const minih3_time_mlp_lora* la = nullptr, const minih3_time_mlp_lora* lep = nullptr, int rank = 0,
+              float ls = 0.f) {
   const int F = tc->freq_dim, Hd = tc->hidden_dim, E = tc->embed_dim;
   const int chains = ep ? 2 : 1;
+  const int R = la ? rank : 0;
   HIPCHECK(launch_sinusoid(t, ep ? r : nullptr, w.s[0], w.s[1], M, F, tc->max_period, st));
   SkinnyArgs l1{{w.s[0], w.s[1]}, {m->w1, ep ? ep->w1 : nullptr}, {m->b1, ep ? ep->b1 : nullptr}, {w.h[0], w.h[1]}};
-  HIPCHECK(launch_skinny_f32(kFragToFrag, l1, chains, M, Hd, F, 1, Hd, 1, st));
-  const int splits = skinny_splits(Hd, kTimeSplits);  // what the launch below uses
+  if (R) {
+    SkinnyArgs u{{w.s[0], w.s[1]}, {la->a1, ep ? lep->a1 : nullptr}, {nullptr, nullptr}, {w.u1[0], w.u1[1]}};
+    u.scale = ls;
+    HIPCHECK(launch_skinny_f32(kFragToFrag, u, chains, M, R, F, 1, R, 0, st));
+    l1.w[0] = la->packed1;
+    l1.w[1] = ep ? lep->packed1 : nullptr;
+    l1.x2[0] = w.u1[0];
+    l1.x2[1] = w.u1[1];
+    l1.k2 = R;
+  }
+  HIPCHECK(launch_skinny_f32(kFragToFrag, l1, chains, M, Hd, F + R, 1, Hd, 1, st));
+  const int splits = skinny_splits(Hd + R, kTimeSplits);  // what the launch below uses
   SkinnyArgs l2{{w.h[0], w.h[1]}, {m->w2, ep ? ep->w2 : nullptr}, {nullptr, nullptr}, {w.part[0], w.part[1]}};
-  HIPCHECK(launch_skinny_f32(kFragToRows, l2, chains, M, E, Hd, kTimeSplits, E, 0, st));
+  if (R) {
+    SkinnyArgs u{{w.h[0], w.h[1]}, {la->a2, ep ? lep->a2 : nullptr}, {nullptr, nullptr}, {w.u2[0], w.u2[1]}};
+    u.scale = ls;
+    HIPCHECK(launch_skinny_f32(kFragToFrag, u, chains, M, R, Hd, 1, R, 0, st));
+    l2.w[0] = la->packed2;
+    l2.w[1] = ep ? lep->packed2 : nullptr;
+    l2.x2[0] = w.u2[0];
+    l2.x2[1] = w.u2[1];
+    l2.k2 = R;
+  }
+  HIPCHECK(launch_skinny_f32(kFragToRows, l2, chains, M, E, Hd + R, kTimeSplits, E, 0, st));
   HIPCHECK(launch_rows_finish(w.part[0], ep ? w.part[1] : nullptr, splits, m->b2, ep ? ep->b2 : nullptr, emb, M, E,
                               0, gate, st));
   return MINIH3_OK;
@@ -553,9 +605,24 @@ int validate_layout(const minih3_config* c, const minih3_layout* L, uint32_t fla
   return status_from_err(err);
 }
 
+// Shapes an unmerged adapter of rank `rank` needs on top of the plain block.
+int check_lora(const minih3_config* c, const minih3_block_lora* loras, int num_blocks, int rank) {
+  if (!loras) return MINIH3_OK;
+  if (rank < 1) return MINIH3_E_ARG;
+  if (c->act_dtype == MINIH3_BF16 ? rank % 256 != 0 : rank % 64 != 0) return MINIH3_E_UNSUPPORTED;
+  for (int i = 0; i < num_blocks; ++i) {
+    const minih3_block_lora& b = loras[i];
+    if (!b.a_qkv || !b.packed_qkv || !b.a_out || !b.packed_out || !b.a_gate_up || !b.packed_gate_up || !b.a_down ||
+        !b.packed_down)
+      return MINIH3_E_ARG;
+  }
+  return MINIH3_OK;
+}
+
 int block_forward(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks,
                   const minih3_block_weights_w8a8* qblocks, int32_t num_blocks, const void* x_in, void* x_out,
-                  void* workspace, size_t workspace_bytes, uint32_t flags, minih3_taps* taps, void* stream) {
+                  void* workspace, size_t workspace_bytes, uint32_t flags, minih3_taps* taps, void* stream,
+                  const minih3_block_lora* loras = nullptr, int lora_rank = 0, float lora_scale = 0.f) {
   int s = check_config(c);
   if (s) return s;
   const bool validate = flags & MINIH3_VALIDATE;
@@ -570,10 +637,13 @@ int block_forward(const minih3_config* c, const minih3_layout* L, const minih3_b
         return MINIH3_E_ARG;
     } else {
       const minih3_block_weights& b = blocks[i];
-      if (!b.w_qkv || !b.w_out || !b.w_gate_up || !b.w_down || !b.q_norm || !b.k_norm || !b.adaln_table)
-        return MINIH3_E_ARG;
+      if (!b.q_norm || !b.k_norm || !b.adaln_table) return MINIH3_E_ARG;
+      if (!loras && (!b.w_qkv || !b.w_out || !b.w_gate_up || !b.w_down)) return MINIH3_E_ARG;
     }
   }
+  if (loras && qblocks) return MINIH3_E_UNSUPPORTED;
+  s = check_lora(c, loras, num_blocks, lora_rank);
+  if (s) return s;
   if (qblocks) {
     if (c->act_dtype != MINIH3_BF16) return MINIH3_E_UNSUPPORTED;
     const long Wq = (long)c->num_heads * c->head_dim;
@@ -584,10 +654,12 @@ int block_forward(const minih3_config* c, const minih3_layout* L, const minih3_b
   if (c->act_dtype == MINIH3_BF16) {
     const long rows = (long)L->batch * L->seq_len, D = c->hidden, W = (long)c->num_heads * c->head_dim;
     const long F = c->ffn_dim;
-    if (!gemm_fits(rows, 3 * W, D) || !gemm_fits(rows, D, W) || !gemm_fits(rows, 2 * F, D) || !gemm_fits(rows, D, F))
+    const long R = loras ? lora_rank : 0;
+    if (!gemm_fits(rows, 3 * W, D + R) || !gemm_fits(rows, D, W + R) || !gemm_fits(rows, 2 * F, D + R) ||
+        !gemm_fits(rows, D, F + R))
       return MINIH3_E_UNSUPPORTED;
   }
-  Workspace w = carve(c, L->batch, L->seq_len, (char*)workspace, qblocks != nullptr);
+  Workspace w = carve(c, L->batch, L->seq_len, (char*)workspace, qblocks != nullptr, loras ? lora_rank : 0);
   if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const bool prof = flags & MINIH3_PROFILE;
@@ -615,8 +687,9 @@ int block_forward(const minih3_config* c, const minih3_layout* L, const minih3_b
   }
   if (c->act_dtype == MINIH3_BF16)
     return run_blocks<bf16_t>(c, L, blocks, num_blocks, (const bf16_t*)x_in, (bf16_t*)x_out, w, flags, taps, st,
-                              qblocks);
-  return run_blocks<float>(c, L, blocks, num_blocks, (const float*)x_in, (float*)x_out, w, flags, taps, st);
+                              qblocks, loras, lora_rank, lora_scale);
+  return run_blocks<float>(c, L, blocks, num_blocks, (const float*)x_in, (float*)x_out, w, flags, taps, st, nullptr,
+                           loras, lora_rank, lora_scale);
 }
 
 // Workspace of a denoising step: the packed sequence twice (input and
@@ -641,7 +714,7 @@ int carve_step(const minih3_config* c, const minih3_step_weights* sw, int B, int
   w.vel_a = take((size_t)B * na * sw->edges->audio_channels * 4);
   w.edges_bytes = carve_edges(c, sw->edges, S, nullptr).total;
   w.edges = take(w.edges_bytes);
-  w.blocks_bytes = carve(c, B, S, nullptr, sw->qblocks != nullptr).total;
+  w.blocks_bytes = carve(c, B, S, nullptr, sw->qblocks != nullptr, sw->loras ? sw->lora_rank : 0).total;
   w.blocks = take(w.blocks_bytes);
   w.total = off;
   return MINIH3_OK;
@@ -650,6 +723,7 @@ int carve_step(const minih3_config* c, const minih3_step_weights* sw, int B, int
 int check_step(const minih3_config* c, const minih3_step_weights* sw) {
   if (!c || !sw || !sw->edges || !sw->sigma_now || !sw->sigma_next || sw->num_blocks < 1) return MINIH3_E_ARG;
   if ((sw->blocks == nullptr) == (sw->qblocks == nullptr)) return MINIH3_E_ARG;
+  if (sw->loras && sw->qblocks) return MINIH3_E_UNSUPPORTED;
   int s = check_config(c);
   if (s) return s;
   return check_edges(c, sw->edges);
@@ -752,6 +826,23 @@ int minih3_block_forward(const minih3_config* c, const minih3_layout* L, const m
                          uint32_t flags, minih3_taps* taps, void* stream) {
   return block_forward(c, L, blocks, nullptr, num_blocks, x_in, x_out, workspace, workspace_bytes, flags, taps,
                        stream);
+}
+
+int minih3_workspace_bytes_lora(const minih3_config* c, int32_t batch, int32_t seq_len, int32_t rank, size_t* bytes) {
+  int s = check_config(c);
+  if (s) return s;
+  if (!bytes || batch < 1 || seq_len < 1 || rank < 1) return MINIH3_E_ARG;
+  *bytes = carve(c, batch, seq_len, nullptr, false, rank).total;
+  return MINIH3_OK;
+}
+
+int minih3_block_forward_lora(const minih3_config* c, const minih3_layout* L, const minih3_block_weights* blocks,
+                              const minih3_block_lora* loras, int32_t num_blocks, int32_t rank, float lora_scale,
+                              const void* x_in, void* x_out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                              minih3_taps* taps, void* stream) {
+  if (!loras) return MINIH3_E_ARG;
+  return block_forward(c, L, blocks, nullptr, num_blocks, x_in, x_out, workspace, workspace_bytes, flags, taps, stream,
+                       loras, rank, lora_scale);
 }
 
 int minih3_workspace_bytes_w8a8(const minih3_config* c, int32_t batch, int32_t seq_len, size_t* bytes) {
@@ -885,6 +976,35 @@ int minih3_time_embed(const minih3_time_config* tc, const minih3_time_mlp* base,
   if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   return time_mlps(tc, base, t, endpoint, r ? r : t, gate, num_tvals, emb, w, st);
+}
+
+int minih3_time_embed_lora_workspace_bytes(const minih3_time_config* tc, int32_t num_tvals, int32_t rank,
+                                           size_t* bytes) {
+  int s = check_time_config(tc);
+  if (s) return s;
+  if (num_tvals < 1 || rank < 16 || rank % 16 != 0 || !bytes) return MINIH3_E_ARG;
+  *bytes = carve_time(tc, num_tvals, nullptr, rank).total;
+  return MINIH3_OK;
+}
+
+int minih3_time_embed_lora(const minih3_time_config* tc, const minih3_time_mlp* base,
+                           const minih3_time_mlp_lora* base_lora, const float* t, const minih3_time_mlp* endpoint,
+                           const minih3_time_mlp_lora* endpoint_lora, const float* r, float gate, int32_t num_tvals,
+                           int32_t rank, float lora_scale, float* emb, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int s = check_time_config(tc);
+  if (s) return s;
+  if (num_tvals < 1 || !base || !base_lora || !t || !emb) return MINIH3_E_ARG;
+  if (rank < 16 || rank % 16 != 0) return MINIH3_E_UNSUPPORTED;
+  if (endpoint && !endpoint_lora) return MINIH3_E_ARG;
+  for (const minih3_time_mlp_lora* l : {base_lora, endpoint ? endpoint_lora : base_lora})
+    if (!l->a1 || !l->packed1 || !l->a2 || !l->packed2) return MINIH3_E_ARG;
+  if ((long)num_tvals * tc->hidden_dim > (1L << 28) || (long)num_tvals * tc->embed_dim > (1L << 28))
+    return MINIH3_E_UNSUPPORTED;
+  TimeWorkspace w = carve_time(tc, num_tvals, (char*)workspace, rank);
+  if (!workspace || workspace_bytes < w.total) return MINIH3_E_WORKSPACE;
+  return time_mlps(tc, base, t, endpoint, r ? r : t, gate, num_tvals, emb, w, (hipStream_t)stream, base_lora,
+                   endpoint ? endpoint_lora : nullptr, rank, lora_scale);
 }
 
 int minih3_adaln_table_workspace_bytes(const minih3_config* c, int32_t embed_dim, size_t* bytes) {
@@ -1145,7 +1265,7 @@ int minih3_denoise_step(const minih3_config* c, const minih3_layout* L, const mi
   if (s) return s;
   const uint32_t bflags = flags & ~(uint32_t)MINIH3_VALIDATE;  // validated once above
   s = block_forward(c, L, sw->blocks, sw->qblocks, sw->num_blocks, w.x0, w.x1, w.blocks, w.blocks_bytes, bflags,
-                    nullptr, stream);
+                    nullptr, stream, sw->loras, sw->lora_rank, sw->lora_scale);
   if (s) return s;
   s = minih3_output_heads(c, L, sw->edges, w.x1, (float*)w.vel_v, (float*)w.vel_a, w.edges, w.edges_bytes, 0, stream);
   if (s) return s;

@@ -92,15 +92,21 @@ __global__ void __launch_bounds__(256) k_sinusoid(Pair<const float*> tp, Pair<fl
 // One split: act(y + bias) goes, with OF, to out in fragment order (Mpad
 // rows, zero past M), else to out row (n / ng) * M + m at column n % ng;
 // several splits: the raw partial sum goes to part[split][m][n].
+// With k2 > 0 (XF only) the last k2 columns of the input come from x2 in
+// its own fragment order ([Mpad, k2]) and x holds the first K - k2 columns.
+// scale multiplies the product before the bias and the activation.
 template <int IN, int XF, int OF, int MB>
 __global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<const float*> wp,
                                                     Pair<const float*> bp, Pair<float*> op, int mchunks, int M,
-                                                    int N, int K, int kchunk, int ng, int act) {
+                                                    int N, int K, int kchunk, int ng, int act, Pair<const float*> x2p,
+                                                    int k2, float scale) {
   const int lane = threadIdx.x & 63;
   const int nb = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (nb * 16 >= N) return;  // whole wave; no barrier follows
   const int chain = blockIdx.z / mchunks;
   const float* __restrict__ x = xp.p[chain];
+  const float* __restrict__ x2 = x2p.p[chain];
+  const int K1 = K - k2;  // columns held by x
   const float* __restrict__ w = wp.p[chain];
   const float* __restrict__ bias = bp.p[chain];
   float* __restrict__ out = op.p[chain];
@@ -127,8 +133,14 @@ __global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if constexpr (XF) {
-        const long unit = ((long)(m0 / 16 + mb) * (K / 16) + (k - 4 * q) / 16) * 64 + lane;
-        xv[slot][mb] = *reinterpret_cast<const floatx4*>(x + unit * 4);
+        const int ks = k - 4 * q;  // first column of the step
+        if (ks >= K1) {
+          const long unit = ((long)(m0 / 16 + mb) * (k2 / 16) + (ks - K1) / 16) * 64 + lane;
+          xv[slot][mb] = *reinterpret_cast<const floatx4*>(x2 + unit * 4);
+        } else {
+          const long unit = ((long)(m0 / 16 + mb) * (K1 / 16) + ks / 16) * 64 + lane;
+          xv[slot][mb] = *reinterpret_cast<const floatx4*>(x + unit * 4);
+        }
       } else {
         const int m = m0 + 16 * mb + r16;
         xv[slot][mb] = m < M ? skinny_in<IN>(x, m, K, k) : floatx4{0.f, 0.f, 0.f, 0.f};
@@ -164,7 +176,10 @@ __global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<
       floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
       if (m < M) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = act ? silu_f(acc[mb][j] + b[j]) : acc[mb][j] + b[j];
+        for (int j = 0; j < 4; ++j) {
+          const float y = scale * acc[mb][j] + b[j];
+          v[j] = act ? silu_f(y) : y;
+        }
       }
       *reinterpret_cast<floatx4*>(out + (((long)(m0 / 16 + mb) * (N / 16) + nb) * 64 + lane) * 4) = v;
       continue;
@@ -176,7 +191,7 @@ __global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[j] += b[j];
+        v[j] = scale * v[j] + b[j];
         if (act) v[j] = silu_f(v[j]);
       }
       *reinterpret_cast<floatx4*>(out + ((long)g * M + m) * ng + c) = v;
@@ -374,13 +389,17 @@ template <int IN, int XF, int OF>
 static void skinny_launch(dim3 grid, int mb, const SkinnyArgs& g, int mchunks, int M, int N, int K, int kchunk,
                           int ng, int act, hipStream_t st) {
   const Pair<const float*> xp{{g.x[0], g.x[1]}}, wp{{g.w[0], g.w[1]}}, bp{{g.bias[0], g.bias[1]}};
+  const Pair<const float*> x2p{{g.x2[0], g.x2[1]}};
   const Pair<float*> op{{g.out[0], g.out[1]}};
   if (mb == 4)
-    k_skinny_f32<IN, XF, OF, 4><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act);
+    k_skinny_f32<IN, XF, OF, 4><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p, g.k2,
+                                                      g.scale);
   else if (mb == 2)
-    k_skinny_f32<IN, XF, OF, 2><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act);
+    k_skinny_f32<IN, XF, OF, 2><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p, g.k2,
+                                                      g.scale);
   else
-    k_skinny_f32<IN, XF, OF, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act);
+    k_skinny_f32<IN, XF, OF, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p, g.k2,
+                                                      g.scale);
 }
 
 hipError_t launch_skinny_f32(int mode, const SkinnyArgs& g, int chains, int M, int N, int K, int splits, int ng,
@@ -391,6 +410,9 @@ hipError_t launch_skinny_f32(int mode, const SkinnyArgs& g, int chains, int M, i
   const int kchunk = skinny_kchunk(K, splits);
   splits = (K + kchunk - 1) / kchunk;
   if (mode == kFragToFrag && splits != 1) return hipErrorInvalidValue;
+  if (g.k2 < 0 || g.k2 % 16 != 0 || g.k2 >= K || (g.k2 > 0 && (mode == kRowsSilu || !g.x2[0])) ||
+      (g.k2 > 0 && chains == 2 && !g.x2[1]) || (g.scale != 1.f && splits != 1))
+    return hipErrorInvalidValue;
   const int mchunks = (M + 16 * mb - 1) / (16 * mb);
   dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)splits, (unsigned)(chains * mchunks));
   if (mode == kFragToFrag)

@@ -624,11 +624,11 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   gemm_body<EPI, 0>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea);
 }
 
+template <int EPI>
 __global__ void __launch_bounds__(64 * kWaves, 1)
     k_gemm_bf16_split(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M, int N,
                       int K, EpiArgs ea) {
-  gemm_body<kEpiStore, 0, 1>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K,
-                             ea);
+  gemm_body<EPI, 0, 1>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea);
 }
 
 template <int EPI>
@@ -727,9 +727,18 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* 
   if ((unsigned long)M * K * 2 > 0xFFFFFFFFul || (unsigned long)N * K * 2 > 0xFFFFFFFFul) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * (N / BN);
   dim3 grid((unsigned)tiles);
-  if (ea.a2) {  // split A operand: store epilogue only, both parts whole K steps
-    if (epi != kEpiStore || ea.k2 <= 0 || ea.k2 >= K || ea.k2 % BK != 0) return hipErrorInvalidValue;
-    k_gemm_bf16_split<<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea);
+  if (ea.a2) {  // split A operand [A | a2]: both parts whole K steps, any epilogue
+    if (ea.k2 <= 0 || ea.k2 >= K || ea.k2 % BK != 0) return hipErrorInvalidValue;
+    if ((unsigned long)M * ea.k2 * 2 > 0xFFFFFFFFul) return hipErrorInvalidValue;
+    switch (epi) {
+      case kEpiStore: k_gemm_bf16_split<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+      case kEpiQKRope: k_gemm_bf16_split<kEpiQKRope><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+      case kEpiGatedResid:
+        k_gemm_bf16_split<kEpiGatedResid><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea);
+        break;
+      case kEpiSwiGLU: k_gemm_bf16_split<kEpiSwiGLU><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   switch (epi) {
@@ -768,7 +777,7 @@ hipError_t launch_gemm<float>(int epi, const float* A, const float* W, void* Cv,
   float* C = static_cast<float*>(Cv);
   const int ncols = epi == kEpiSwiGLU ? ea.ffn_dim : N;
   if (epi == kEpiSwiGLU && (N != 2 * ea.ffn_dim || ea.ffn_dim % 64 != 0)) return hipErrorInvalidValue;
-  if (ea.a2 && (epi != kEpiStore || ea.k2 <= 0 || ea.k2 >= K)) return hipErrorInvalidValue;
+  if (ea.a2 && (ea.k2 <= 0 || ea.k2 >= K || ea.k2 % 16 != 0)) return hipErrorInvalidValue;
   dim3 grid((unsigned)(ncols / 64), (unsigned)((M + 63) / 64));
   switch (epi) {
     case kEpiStore: k_gemm_f32<kEpiStore><<<grid, 256, 0, st>>>(A, W, C, M, N, K, ea); break;

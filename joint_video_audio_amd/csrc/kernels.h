@@ -139,12 +139,19 @@ hipError_t launch_sinusoid(const float* t0, const float* t1, float* s0, float* s
 // SiLU(x)). Row-major results go to out row (n / ng) * M + m, column n % ng
 // (ng % 16 == 0); bias may be null. The split count actually used is
 // skinny_splits(K, splits).
+// With x2 set (fragment-order modes), the input is [x | x2] along K: the
+// last k2 columns (k2 % 16 == 0) come from x2 [Mpad, k2] in fragment order
+// and x holds the first K - k2. scale multiplies the product before the bias
+// (one split only when scale != 1).
 enum SkinnyMode { kFragToFrag = 0, kFragToRows = 1, kRowsSilu = 2 };
 struct SkinnyArgs {
   const float* x[2];
   const float* w[2];
   const float* bias[2];
   float* out[2];
+  const float* x2[2] = {nullptr, nullptr};
+  int k2 = 0;
+  float scale = 1.f;
 };
 hipError_t launch_skinny_f32(int mode, const SkinnyArgs& args, int chains, int M, int N, int K, int splits, int ng,
                              int act, hipStream_t st);

@@ -56,7 +56,12 @@ class _BlockWeightsW8A8(ctypes.Structure):
 
 class _StepWeights(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("blocks", _P), ("qblocks", _P), ("edges", _P), ("sigma_now", _P),
-                ("sigma_next", _P)]
+                ("sigma_next", _P), ("loras", _P), ("lora_rank", ctypes.c_int32), ("lora_scale", ctypes.c_float)]
+
+
+class _BlockLora(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("a_qkv", "packed_qkv", "a_out", "packed_out", "a_gate_up", "packed_gate_up",
+                                  "a_down", "packed_down")]
 
 
 TAP_FLOAT = ("adaln1", "q_rot", "k_rot", "v_t", "attn_o", "attn_proj", "x_mid", "adaln2", "ffn_h", "ffn_out")
@@ -74,6 +79,10 @@ class TimeConfig(ctypes.Structure):
 
 class _TimeMLP(ctypes.Structure):
     _fields_ = [("w1", _P), ("b1", _P), ("w2", _P), ("b2", _P)]
+
+
+class _TimeMLPLora(ctypes.Structure):
+    _fields_ = [("a1", _P), ("packed1", _P), ("a2", _P), ("packed2", _P)]
 
 
 class _Edges(ctypes.Structure):
@@ -132,6 +141,14 @@ def lib() -> ctypes.CDLL:
         L.minih3_time_embed.argtypes = [ctypes.POINTER(TimeConfig), ctypes.POINTER(_TimeMLP), _P,
                                         ctypes.POINTER(_TimeMLP), _P, ctypes.c_float, ctypes.c_int32, _P, _P,
                                         ctypes.c_size_t, _P]
+        L.minih3_time_embed_lora_workspace_bytes.argtypes = [ctypes.POINTER(TimeConfig), ctypes.c_int32,
+                                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_time_embed_lora.argtypes = [ctypes.POINTER(TimeConfig), ctypes.POINTER(_TimeMLP),
+                                             ctypes.POINTER(_TimeMLPLora), _P, ctypes.POINTER(_TimeMLP),
+                                             ctypes.POINTER(_TimeMLPLora), _P, ctypes.c_float, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+        L.minih3_time_embed_lora_workspace_bytes.restype = ctypes.c_int
+        L.minih3_time_embed_lora.restype = ctypes.c_int
         L.minih3_adaln_table_workspace_bytes.argtypes = [ctypes.POINTER(Config), ctypes.c_int32,
                                                          ctypes.POINTER(ctypes.c_size_t)]
         L.minih3_adaln_table.argtypes = [ctypes.POINTER(Config), _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t,
@@ -150,6 +167,14 @@ def lib() -> ctypes.CDLL:
         L.minih3_block_forward_w8a8.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
                                                 ctypes.POINTER(_BlockWeightsW8A8), ctypes.c_int32, _P, _P, _P,
                                                 ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
+        L.minih3_workspace_bytes_lora.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.minih3_block_forward_lora.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_Layout),
+                                                ctypes.POINTER(_BlockWeights), ctypes.POINTER(_BlockLora),
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P,
+                                                ctypes.c_size_t, ctypes.c_uint32, ctypes.POINTER(_Taps), _P]
+        L.minih3_workspace_bytes_lora.restype = ctypes.c_int
+        L.minih3_block_forward_lora.restype = ctypes.c_int
         L.minih3_linear_w8a8.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
         L.minih3_lora_pack_weight.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, _P]
@@ -186,10 +211,12 @@ EXPORTED = ("minih3_workspace_bytes", "minih3_block_forward", "minih3_attention_
             "minih3_attention_packed", "minih3_attention_headmajor_workspace_bytes", "minih3_attention_headmajor",
             "minih3_adaln_modulate", "minih3_qk_norm_rope", "minih3_linear",
             "minih3_profile_collect", "minih3_kernel_name", "minih3_status_string",
-            "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_adaln_table_workspace_bytes",
+            "minih3_time_embed_workspace_bytes", "minih3_time_embed", "minih3_time_embed_lora_workspace_bytes",
+            "minih3_time_embed_lora", "minih3_adaln_table_workspace_bytes",
             "minih3_adaln_table", "minih3_adaln_table_noalloc", "minih3_edges_workspace_bytes", "minih3_embed_inputs", "minih3_output_heads",
             "minih3_rotate_quantize", "minih3_linear_w8a8", "minih3_workspace_bytes_w8a8",
-            "minih3_block_forward_w8a8", "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
+            "minih3_block_forward_w8a8", "minih3_workspace_bytes_lora", "minih3_block_forward_lora",
+            "minih3_lora_pack_weight", "minih3_linear_lora_workspace_bytes",
             "minih3_linear_lora", "minih3_euler_step", "minih3_denoise_step_workspace_bytes",
             "minih3_denoise_step")
 
@@ -479,6 +506,66 @@ def time_embed(tc: TimeConfig, base: DeviceTimeMLP, t: torch.Tensor, endpoint: O
     return out
 
 
+class DeviceTimeMLPLora:
+    """Unmerged adapter of one timestep MLP (fp32): a1 [rank, freq], packed1 = [W1 | B1], a2 [rank, hidden],
+    packed2 = [W2 | B2]."""
+
+    def __init__(self, a1, packed1, a2, packed2):
+        self.a1, self.packed1, self.a2, self.packed2 = a1, packed1, a2, packed2
+        self.rank = int(a1.shape[0])
+
+    @classmethod
+    def from_mlp(cls, mlp: DeviceTimeMLP, a1, b1, a2, b2) -> "DeviceTimeMLPLora":
+        return cls(a1, lora_pack_weight(mlp.w1, b1), a2, lora_pack_weight(mlp.w2, b2))
+
+    def check(self, tc: TimeConfig):
+        r = self.rank
+        _req(self.a1, torch.float32, "a1", r * tc.freq_dim)
+        _req(self.packed1, torch.float32, "packed1", tc.hidden_dim * (tc.freq_dim + r))
+        _req(self.a2, torch.float32, "a2", r * tc.hidden_dim)
+        _req(self.packed2, torch.float32, "packed2", tc.embed_dim * (tc.hidden_dim + r))
+
+    def c(self) -> _TimeMLPLora:
+        return _TimeMLPLora(*(_ptr(t) for t in (self.a1, self.packed1, self.a2, self.packed2)))
+
+
+def time_embed_lora(tc: TimeConfig, base: DeviceTimeMLP, base_lora: DeviceTimeMLPLora, t: torch.Tensor,
+                    lora_scale: float, endpoint: Optional[DeviceTimeMLP] = None,
+                    endpoint_lora: Optional[DeviceTimeMLPLora] = None, r: Optional[torch.Tensor] = None,
+                    gate: float = 0.0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """time_embed with unmerged adapters on the timestep MLPs (lora_scale = scale * alpha / rank)."""
+    n = t.numel()
+    _req(t, torch.float32, "t", n)
+    base_lora.check(tc)
+    if endpoint is not None:
+        if endpoint_lora is None:
+            raise ValueError("an endpoint MLP needs its adapter")
+        endpoint_lora.check(tc)
+        if endpoint_lora.rank != base_lora.rank:
+            raise ValueError("the two adapters share a rank")
+    if r is not None:
+        _req(r, torch.float32, "r", n)
+    if out is None:
+        out = torch.empty(n, tc.embed_dim, dtype=torch.float32, device=t.device)
+    _req(out, torch.float32, "out", n * tc.embed_dim)
+    rank = base_lora.rank
+    if workspace is None:
+        nb = ctypes.c_size_t(0)
+        _check(lib().minih3_time_embed_lora_workspace_bytes(ctypes.byref(tc), n, rank, ctypes.byref(nb)),
+               "time_embed_lora_workspace_bytes")
+        workspace = alloc_workspace(int(nb.value), t.device)
+    cb, cl = base.c(), base_lora.c()
+    ce = endpoint.c() if endpoint is not None else None
+    cel = endpoint_lora.c() if endpoint is not None else None
+    _check(lib().minih3_time_embed_lora(ctypes.byref(tc), ctypes.byref(cb), ctypes.byref(cl), _ptr(t),
+                                        ctypes.byref(ce) if ce is not None else None,
+                                        ctypes.byref(cel) if cel is not None else None, _ptr(r), float(gate), n,
+                                        rank, float(lora_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                        _stream()), "time_embed_lora")
+    return out
+
+
 def adaln_table_workspace_bytes(cfg: Config, embed_dim: int) -> int:
     nb = ctypes.c_size_t(0)
     _check(lib().minih3_adaln_table_workspace_bytes(ctypes.byref(cfg), embed_dim, ctypes.byref(nb)),
@@ -654,6 +741,79 @@ class DeviceBlockW8A8:
         return _BlockWeightsW8A8(*ptrs, _ptr(self.q_norm), _ptr(self.k_norm), _ptr(self.adaln_table))
 
 
+class DeviceBlockLora:
+    """Unmerged adapter of one block: per projection the A matrix [rank, K]
+    and the packed [W | B] [N, K + rank] (act dtype)."""
+
+    NAMES = ("qkv", "out", "gate_up", "down")
+
+    def __init__(self, a: dict, packed: dict, rank: int):
+        self.a, self.packed, self.rank = a, packed, int(rank)
+
+    @classmethod
+    def from_block(cls, b: DeviceBlock, a: dict, bmat: dict) -> "DeviceBlockLora":
+        """a[name] [rank, K] and bmat[name] [N, rank] for the four projections of b."""
+        packed = {}
+        for n, w in zip(cls.NAMES, (b.w_qkv, b.w_out, b.w_gate_up, b.w_down)):
+            packed[n] = lora_pack_weight(w, bmat[n])
+        return cls({n: a[n] for n in cls.NAMES}, packed, a["qkv"].shape[0])
+
+    def check(self, cfg: Config):
+        dt = act_torch_dtype(cfg)
+        D, W, F = cfg.hidden, cfg.num_heads * cfg.head_dim, cfg.ffn_dim
+        shapes = {"qkv": (3 * W, D), "out": (D, W), "gate_up": (2 * F, D), "down": (D, F)}
+        for n, (N, K) in shapes.items():
+            _req(self.a[n], dt, f"lora a_{n}", self.rank * K)
+            _req(self.packed[n], dt, f"lora packed_{n}", N * (K + self.rank))
+
+    def c(self) -> _BlockLora:
+        ptrs = []
+        for n in self.NAMES:
+            ptrs += [_ptr(self.a[n]), _ptr(self.packed[n])]
+        return _BlockLora(*ptrs)
+
+
+def workspace_bytes_lora(cfg: Config, batch: int, seq_len: int, rank: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().minih3_workspace_bytes_lora(ctypes.byref(cfg), batch, seq_len, rank, ctypes.byref(n)),
+           "workspace_bytes_lora")
+    return int(n.value)
+
+
+def block_forward_lora(cfg: Config, layout: DeviceLayout, blocks: Sequence[DeviceBlock],
+                       loras: Sequence[DeviceBlockLora], x: torch.Tensor, lora_scale: float,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                       taps: Optional[dict] = None) -> torch.Tensor:
+    """block_forward with the unmerged adapter loras[i] on every projection of blocks[i];
+    lora_scale = scale * alpha / rank."""
+    dt = act_torch_dtype(cfg)
+    B, S, D = layout.batch, layout.seq_len, cfg.hidden
+    _req(x, dt, "x", B * S * D)
+    if len(loras) != len(blocks):
+        raise ValueError("one adapter per block")
+    rank = loras[0].rank
+    for lb in loras:
+        lb.check(cfg)
+        if lb.rank != rank:
+            raise ValueError("adapters of one call share a rank")
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, dt, "out", B * S * D)
+    if workspace is None:
+        workspace = alloc_workspace(workspace_bytes_lora(cfg, B, S, rank), x.device)
+    arr = (_BlockWeights * len(blocks))(*[b.c() for b in blocks])
+    larr = (_BlockLora * len(loras))(*[lb.c() for lb in loras])
+    ct = None
+    if taps:
+        ct = _Taps(**{k: (ctypes.c_void_p(v.data_ptr()) if v is not None else None) for k, v in taps.items()})
+    L = layout.c()
+    s = lib().minih3_block_forward_lora(ctypes.byref(cfg), ctypes.byref(L), arr, larr, len(blocks), rank,
+                                        float(lora_scale), _ptr(x), _ptr(out), _ptr(workspace), workspace.numel(),
+                                        flags, ctypes.byref(ct) if ct is not None else None, _stream())
+    _check(s, "block_forward_lora")
+    return out
+
+
 def workspace_bytes_w8a8(cfg: Config, batch: int, seq_len: int) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().minih3_workspace_bytes_w8a8(ctypes.byref(cfg), batch, seq_len, ctypes.byref(n)),
@@ -747,9 +907,11 @@ def euler_step(x: torch.Tensor, velocity: torch.Tensor, indices: torch.Tensor, t
 
 def denoise_step(cfg: Config, layout: DeviceLayout, blocks, edges: DeviceEdges, sigma_now: torch.Tensor,
                  sigma_next: torch.Tensor, video: torch.Tensor, audio: torch.Tensor, text: torch.Tensor,
-                 flags: int = 0, workspace: Optional[torch.Tensor] = None):
+                 flags: int = 0, workspace: Optional[torch.Tensor] = None,
+                 loras: Optional[Sequence["DeviceBlockLora"]] = None, lora_scale: float = 1.0):
     """One denoising step: video [B, n_video, Cv] and audio [B, n_audio, Ca] fp32 latents are updated in place
-    (input projections, the block chain -- DeviceBlock or DeviceBlockW8A8 list --, heads, Euler update)."""
+    (input projections, the block chain -- DeviceBlock or DeviceBlockW8A8 list, with unmerged adapters on the
+    DeviceBlock chain when loras is given (lora_scale = scale * alpha / rank) --, heads, Euler update)."""
     B, S = layout.batch, layout.seq_len
     nv, na = layout.video_indices.numel(), layout.audio_indices.numel()
     edges.check(cfg)
@@ -766,8 +928,17 @@ def denoise_step(cfg: Config, layout: DeviceLayout, blocks, edges: DeviceEdges, 
             b.check(cfg)
         arr = (_BlockWeights * len(blocks))(*[b.c() for b in blocks])
     ce = edges.c()
+    larr, rank = None, 0
+    if loras is not None:
+        if w8 or len(loras) != len(blocks):
+            raise ValueError("adapters go with the bf16 / fp32 block chain, one per block")
+        for lb in loras:
+            lb.check(cfg)
+        rank = loras[0].rank
+        larr = (_BlockLora * len(loras))(*[lb.c() for lb in loras])
     sw = _StepWeights(len(blocks), None if w8 else ctypes.cast(arr, _P), ctypes.cast(arr, _P) if w8 else None,
-                      ctypes.cast(ctypes.pointer(ce), _P), _ptr(sigma_now), _ptr(sigma_next))
+                      ctypes.cast(ctypes.pointer(ce), _P), _ptr(sigma_now), _ptr(sigma_next),
+                      ctypes.cast(larr, _P) if larr is not None else None, rank, float(lora_scale))
     if workspace is None:
         nb = ctypes.c_size_t(0)
         _check(lib().minih3_denoise_step_workspace_bytes(ctypes.byref(cfg), ctypes.byref(sw), B, S, nv, na,

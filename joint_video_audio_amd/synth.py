@@ -441,3 +441,50 @@ def make_edges(dims: ModelDims, layout: Layout, batch: int = 1, seed: int = 0, v
     w_aout = _normal(rng, (audio_channels, D), D ** -0.5)
     b_aout = _normal(rng, (audio_channels,), 0.02)
     return Edges(video, audio, text, w_in, b_in, w_ain, b_ain, gamma, beta, w_out, b_out, w_aout, b_aout)
+
+
+# --------------------------------------------------------------------------
+# Unmerged adapters of the block projections
+# --------------------------------------------------------------------------
+#
+# Recipe: ``numpy.random.default_rng(seed)``; per block, for the projections
+# qkv, out, gate_up, down in that order: A [rank, K] ~ N(0, 1 / K), then
+# B [N, rank] ~ N(0, 0.02^2), both in the activation dtype. (A trained
+# adapter starts from B = 0; a random B makes the low-rank path visible.)
+
+LORA_SHAPES = ("qkv", "out", "gate_up", "down")
+
+
+def lora_shapes(dims: ModelDims) -> dict:
+    """(N, K) of each projection's base weight."""
+    D, W, F = dims.hidden, dims.qkv_width, dims.ffn_dim
+    return {"qkv": (3 * W, D), "out": (D, W), "gate_up": (2 * F, D), "down": (D, F)}
+
+
+def make_lora(dims: ModelDims, rank: int, num_blocks: int = 1, seed: int = 0) -> List[dict]:
+    """Per block {name: (A, B)} as stored Tensors."""
+    rng = np.random.default_rng(seed)
+    shapes = lora_shapes(dims)
+    out = []
+    for _ in range(num_blocks):
+        blk = {}
+        for n in LORA_SHAPES:
+            N, K = shapes[n]
+            a = _store(_normal(rng, (rank, K), K ** -0.5), dims.dtype)
+            b = _store(_normal(rng, (N, rank), 0.02), dims.dtype)
+            blk[n] = (a, b)
+        out.append(blk)
+    return out
+
+
+def make_time_lora(cond: "Conditioning", rank: int, seed: int = 0) -> List[dict]:
+    """Adapters of the timestep MLPs (base, then endpoint when present), fp32:
+    A1 [rank, freq] ~ N(0, 1 / freq), B1 [hidden, rank] ~ N(0, 0.02^2),
+    A2 [rank, hidden] ~ N(0, 1 / hidden), B2 [embed, rank] ~ N(0, 0.02^2)."""
+    rng = np.random.default_rng(seed)
+    F, Hd, E = cond.freq_dim, cond.hidden_dim, cond.embed_dim
+    out = []
+    for _ in range(2 if cond.endpoint is not None else 1):
+        out.append(dict(a1=_normal(rng, (rank, F), F ** -0.5), b1=_normal(rng, (Hd, rank), 0.02),
+                        a2=_normal(rng, (rank, Hd), Hd ** -0.5), b2=_normal(rng, (E, rank), 0.02)))
+    return out
