@@ -566,10 +566,11 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, c, 0, 0, 0);
   };
   // Entering step j of the walk: every wave waits for its own DMA of K(j+2)
-  // and V(j+1) and for its reads of step j - 1 (the first kAhead reads of
-  // step j, issued at the end of step j - 1, may still be in flight); one
-  // barrier publishes K(j+2), V(j+1) and frees the slots of K(j) and V(j-1).
-  auto enter = [&](int j, Ahead& a1) {
+  // and V(j+1) (issued during step j - 2) and for its reads of step j - 1
+  // (the first kAhead reads of step j, issued at the end of step j - 1, may
+  // still be in flight); one barrier publishes K(j+2), V(j+1) and frees the
+  // slots of K(j) and V(j-1), which step j refills (dma1).
+  auto enter = [&](int j, Ahead& a1, int& t3, int& t4) {
     const int cb = (j + 1) >> 6;
     if (((j + 1) & 63) == 0) {  // the walk enters block cb
       bcur = bnext;
@@ -579,7 +580,8 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       wait_vmcnt<0>();
     }
     a1 = at(j + 1, cb);
-    const int t3 = at(j + 3, cb).t, t4 = at(j + 4, cb).t;  // past the end: the last tile again, never read
+    t3 = at(j + 3, cb).t;  // past the end: the last tile again, never read
+    t4 = at(j + 4, cb).t;
     wait_vmcnt<4>();
     wait_lgkm<kAhead>();
     __builtin_amdgcn_s_barrier();
@@ -588,8 +590,19 @@ __global__ void __launch_bounds__(kNW * 64, 1)
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
     }
-    dma_k(t4, j % kRing);        // K(j+4) into the slot of K(j)
-    dma_v(t3, (j + 3) % kRing);  // V(j+3) into the slot of V(j-1)
+  };
+  // One DMA instruction of K(j+4) (into the slot of K(j), free since the
+  // barrier of step j) or V(j+3) (into the slot of V(j-1)). The four of a
+  // step go out one at the end of each quarter step, K in the first half and
+  // V in the second: issued together right after the barrier, the 32
+  // instructions of the eight waves queued at the address unit and the step
+  // ran 4.5 % slower (same bits either way).
+  auto dma1 = [&](int which, int t, int j) {
+    if (which < 2)
+      dma16(kh, koff[which], (uint32_t)t * kTileBytes, (lds_ptr_t)(kslot(j % kRing) + (8 * wid + 4 * which) * 256));
+    else
+      dma16(vh, voff[which - 2], (uint32_t)t * (kKV * 2),
+            (lds_ptr_t)(vslot((j + 3) % kRing) + (16 * wid + 8 * (which - 2)) * 128));
   };
   // A step of the walk. On entry sc holds the scores of tile j (the first
   // half already turned into P[0], the second half masked) and G the first
@@ -601,7 +614,8 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   // fragments of step j + 1, whose tiles the barrier of step j published.
   auto step = [&](int j, Half (&sc)[2], bf16x8 (&P)[2][2], bf16x8 (&G)[kAhead]) {
     Ahead a1;
-    enter(j, a1);
+    int t3, t4;
+    enter(j, a1, t3, t4);
     // A wave's first half-step after the barrier issues at raised priority
     // (arbitration between the two waves of a SIMD): the wave that reaches
     // the second half first yields to the one still in its first. Measured
@@ -637,6 +651,10 @@ __global__ void __launch_bounds__(kNW * 64, 1)
           const int db = fi >> 1;
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma16(F[f], P[kc][qb], o[db][qb]);
+        }
+        if ((fi & 7) == 7) {
+          const int w = 2 * kc + (fi >> 3);  // K, K, V, V
+          dma1(w, w < 2 ? t4 : t3, j);
         }
         const int qb = fi >> 3, e = fi & 7;
         float x = src[e >> 2][qb][e & 3];
@@ -709,7 +727,8 @@ __global__ void __launch_bounds__(kNW * 64, 1)
     // last tile: O^T only (its values were made visible, and their tail
     // zeroed, when step n - 2 was entered)
     Ahead a1;
-    enter(n - 1, a1);
+    int u3, u4;
+    enter(n - 1, a1, u3, u4);
     const uint8_t* Vc = vslot((n - 1) % kRing);
     P[1][0] = probs(sc[1], 0);
     P[1][1] = probs(sc[1], 1);
