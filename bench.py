@@ -25,7 +25,11 @@ table from the workload's timestep values (time embeddings, then the bf16
 AdaLN projection), with the projection's HBM roofline; edges times the
 input projections into the packed sequence and the output heads (fp32);
 w8a8 times the rotated W8A8 INT8 variant of the four projections beside the
-bf16 ones (a separate variant: the headline step is bf16).
+bf16 ones (a separate variant: the headline step is bf16). other_workloads
+times the other full-width workloads (8192 rows padless, 16384 rows with 640
+padding rows, the four-block chain on 24576 + P rows) the same way, each with
+its own same-run parity check; denoise_step times a clip-scale denoising step
+(4 blocks) with and without unmerged adapters.
 """
 from __future__ import annotations
 
@@ -492,6 +496,48 @@ def denoise_step(wl, reps: int, warmup: int, num_blocks: int = 4, rank: int = 25
     return res
 
 
+def other_workloads(names, steps: int, warmup: int, seed: int = 0):
+    """The other full-width workloads, each timed like the headline (median of
+    `steps` per-step HIP event times, no per-kernel events) with its timed
+    output compared with the oracle's sampled rows in the same run."""
+    import numpy as np
+    import torch
+    from joint_video_audio_amd import device as dv
+    from joint_video_audio_amd import minih3 as m
+    from joint_video_audio_amd import synth
+    res = {}
+    for name in names:
+        t0 = time.time()
+        wl = synth.make_workload(name, seed=seed)
+        cfg, lay, blocks, x = dv.upload(wl)
+        out = torch.empty_like(x)
+        ws = m.alloc_workspace(m.workspace_bytes(cfg, lay.batch, lay.seq_len))
+        print(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        for _ in range(warmup):
+            m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws)
+        st = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(st)
+        for i in range(steps):
+            m.block_forward(cfg, lay, blocks, x, out=out, workspace=ws)
+            evs[i + 1].record(st)
+        torch.cuda.synchronize()
+        ms = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]))
+        nb = len(blocks)
+        gemm, attn = flop_counts(wl.dims, wl.layout)
+        t_block = ms / 1e3 / nb
+        tfl = (gemm + attn) / t_block / 1e12
+        res[name] = {"seq_len": lay.seq_len, "pad_rows": wl.layout.num_pad, "blocks_per_step": nb,
+                     "ms_per_step": round(ms, 4), "ms_per_block": round(ms / nb, 4),
+                     "rows_per_s": round(lay.seq_len / t_block, 1), "tflops": round(tfl, 1),
+                     "mfma_peak_frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "parity": same_run_parity(name, seed, out)}
+        del blocks, x, out, ws, wl
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,6 +554,7 @@ def main():
     ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--no-denoise-step", action="store_true")
     ap.add_argument("--no-clock", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the timed steps, copy a buffer of BYTES twice with torch (a plain copy kernel "
                          "of known size for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -632,6 +679,9 @@ def main():
         del blocks, x, out, ws
         torch.cuda.empty_cache()
         res["denoise_step"] = denoise_step(wl, reps=3, warmup=1)
+    if not a.no_other_workloads and a.workload == "clip32k":
+        others = [n for n in ("padless8k", "padded16k", "chain4x24k")]
+        res["other_workloads"] = other_workloads(others, steps=5, warmup=2, seed=a.seed)
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_rows)
