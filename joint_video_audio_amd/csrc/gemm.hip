@@ -31,6 +31,8 @@
 // One barrier per K step. Tiles are ordered so that the workgroups an XCD
 // runs together share A and W panels in its L2. Plain (store) tiles are
 // staged in LDS and written as whole contiguous rows.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -300,10 +302,19 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 //
 // SPLIT: the K steps below K - k2 read A (row stride K - k2), the others
 // read ea.a2 (row stride k2); the LDS ring is filled the same way.
-template <int EPI, int I8, int SPLIT = 0>
+//
+// HALF: the workgroup computes one 128-row half (bid & 1) of the 256 x 256
+// tile pid_base + bid / 2 in the usual tile order: waves of 64 x 128
+// outputs, the same K loop with 32 MFMAs per half step, A slots half
+// filled. Every output is the same sequence of MFMAs over K as in a whole
+// tile, so the values are bit for bit those of the whole-tile kernel.
+template <int EPI, int I8, int SPLIT = 0, int HALF = 0>
 __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const uint8_t* __restrict__ W,
-                                          void* __restrict__ Cv, int M, int N, int K, const EpiArgs& ea) {
-  constexpr int WTM = 128, WTN = 128, MI = WTM / 16, NI = WTN / 16;
+                                          void* __restrict__ Cv, int M, int N, int K, const EpiArgs& ea,
+                                          int pid_base = 0) {
+  static_assert(!HALF || (EPI == kEpiGatedResid && !SPLIT), "half tiles serve the gated-residual epilogue");
+  constexpr int WTM = HALF ? 64 : 128, WTN = 128, MI = WTM / 16, NI = WTN / 16;
+  constexpr int kIPWA = HALF ? kIPW / 2 : kIPW;  // DMA instructions of A per wave and K step
   constexpr int kEs = I8 ? 1 : 2;  // bytes per element
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kSlotBytes];
 
@@ -313,11 +324,18 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
 
   // ---- tile order: XCD-contiguous ranges, then groups of 8 M-tiles
   const int MT = (M + BM - 1) / BM, NTL = N / BN;
-  const int T = MT * NTL;
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, loc = bid >> 3;
-  const int q8 = T >> 3, r8 = T & 7;
-  const int pid = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+  int pid, mh = 0;
+  if constexpr (HALF) {
+    pid = pid_base + (bid >> 1);
+    mh = bid & 1;
+  } else {
+    // the launch covers tiles 0 .. gridDim.x - 1 of the order
+    const int G = gridDim.x;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int q8 = G >> 3, r8 = G & 7;
+    pid = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+  }
   constexpr int GROUP_M = 8;
   const int npg = GROUP_M * NTL;
   const int g = pid / npg;
@@ -325,20 +343,28 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   const int gsz = MT - first_m < GROUP_M ? MT - first_m : GROUP_M;
   const int tm = first_m + (pid % npg) % gsz;
   const int tn = (pid % npg) / gsz;
-  const int m0 = tm * BM;
+  const int m0 = tm * BM + mh * (BM / 2);
 
-  // ---- DMA byte offsets. Wave w fills rows 64 w .. 64 w + 63 of every slot:
-  // instruction j covers rows 64 w + 8 j .. + 7 (1 KiB); lane L takes row
-  // 64 w + 8 j + L / 8, logical chunk (L % 8) ^ swz(row).
+  // ---- DMA byte offsets. Wave w fills rows 64 w .. 64 w + 63 of every slot
+  // (of an A slot of a half tile rows 32 w .. 32 w + 31): instruction j covers
+  // rows 64 w + 8 j .. + 7 (1 KiB); lane L takes row 64 w + 8 j + L / 8,
+  // logical chunk (L % 8) ^ swz(row).
   const int K1 = SPLIT ? K - ea.k2 : K;  // row stride of A
   const uint8_t* A2 = static_cast<const uint8_t*>(ea.a2);
-  uint32_t voff_a[kIPW], voff_w[kIPW], voff_a2[SPLIT ? kIPW : 1];
+  uint32_t voff_a[kIPWA], voff_w[kIPW], voff_a2[SPLIT ? kIPW : 1];
+#pragma unroll
+  for (int j = 0; j < kIPWA; ++j) {
+    const int row = (HALF ? 32 : 64) * wid + 8 * j + lane / kCPR;
+    const int c = (lane % kCPR) ^ gemm_swz(row);
+    int am = m0 + row;
+    am = am < M ? am : M - 1;
+    voff_a[j] = (uint32_t)((long)am * K1 * kEs + c * 16);
+    if constexpr (SPLIT) voff_a2[j] = (uint32_t)((long)am * ea.k2 * kEs + c * 16);
+  }
 #pragma unroll
   for (int j = 0; j < kIPW; ++j) {
     const int row = 64 * wid + 8 * j + lane / kCPR;
     const int c = (lane % kCPR) ^ gemm_swz(row);
-    int am = m0 + row;
-    am = am < M ? am : M - 1;
     int wr;
     if (EPI == kEpiSwiGLU) {
       // wave block of WTN rows: first half gate rows, second half the matching up rows
@@ -347,9 +373,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
     } else {
       wr = tn * BN + row;
     }
-    voff_a[j] = (uint32_t)((long)am * K1 * kEs + c * 16);
     voff_w[j] = (uint32_t)((long)wr * K * kEs + c * 16);
-    if constexpr (SPLIT) voff_a2[j] = (uint32_t)((long)am * ea.k2 * kEs + c * 16);
   }
   const int KT = K / (kRowBytes / kEs);
   const int KT1 = K1 / (kRowBytes / kEs);  // K steps served by A
@@ -364,7 +388,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
       dma16(second ? A2 : A, second ? voff_a2[j] : voff_a[j], (uint32_t)((second ? kc - KT1 : kc) * kRowBytes),
             (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
     } else {
-      dma16(A, voff_a[j], (uint32_t)(kc * kRowBytes), (lds_ptr_t)(slot_ptr(s) + (64 * wid + 8 * j) * kRowBytes));
+      dma16(A, voff_a[j], (uint32_t)(kc * kRowBytes),
+            (lds_ptr_t)(slot_ptr(s) + ((HALF ? 32 : 64) * wid + 8 * j) * kRowBytes));
     }
   };
   auto dma_w1 = [&](int k, int j) {
@@ -413,25 +438,54 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
     else
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mi][ni]) : "v"(fw[set][ni]), "v"(fa[set][mi]));
   };
-  // One half K step (64 MFMAs) in a fixed issue order: MFMA i, then after
-  // every fourth MFMA one fragment of the next half, after every eighth one
-  // DMA instruction of (dk, W or A); each group is fenced so the DMA of the
-  // four waves reaches the address unit evenly.
+  // Fragment read issued after MFMA i of a half step (-1: none). Whole tile:
+  // after every fourth MFMA, in read_frag's order. Half tile (12 fragments
+  // over 32 MFMAs): placed so that a register is rewritten no sooner than 12
+  // MFMAs after its last use in the previous half step (W fragment ni after
+  // MFMA 4 + ni or later) and arrives well before its first use.
+  auto read_at = [](int i) {
+    if constexpr (HALF) {
+      switch (i) {
+        case 0: return 0;    // a0
+        case 2: return 9;    // a1
+        case 5: return 1;    // w0
+        case 7: return 2;    // w1
+        case 9: return 3;    // w2
+        case 11: return 4;   // w3
+        case 14: return 10;  // a2
+        case 16: return 5;   // w4
+        case 18: return 6;   // w5
+        case 20: return 7;   // w6
+        case 22: return 8;   // w7
+        case 25: return 11;  // a3
+        default: return -1;
+      }
+    } else {
+      return (i & 3) == 0 ? i >> 2 : -1;
+    }
+  };
+  // One half K step (MI * NI MFMAs) in a fixed issue order: MFMA i, then
+  // the fragment read_at(i) of the next half, and DMA instructions of (dk, W
+  // or A) spread evenly (eight per half step; the four of a half tile's A
+  // after every eighth MFMA); each group is fenced so the DMA of the four
+  // waves reaches the address unit evenly.
   auto half = [&](int set, int nk, int nh, bool reads, int dk, bool dw) {
+    constexpr int NM = MI * NI;
 #pragma unroll
-    for (int i = 0; i < MI * NI; ++i) {
+    for (int i = 0; i < NM; ++i) {
       mfma1(set, i);
-      if (reads && (i & 3) == 0) read_frag(nk, nh, set ^ 1, i >> 2);
-      if (dk >= 0 && (i & 7) == 7) {
-        if (dw)
-          dma_w1(dk, i >> 3);
-        else
-          dma_a1(dk, i >> 3);
+      if (reads && read_at(i) >= 0) read_frag(nk, nh, set ^ 1, read_at(i));
+      if (dk >= 0) {
+        if (dw) {
+          if (i % (NM / kIPW) == NM / kIPW - 1) dma_w1(dk, i / (NM / kIPW));
+        } else {
+          if (i % (NM / kIPWA) == NM / kIPWA - 1) dma_a1(dk, i / (NM / kIPWA));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  static_assert(kIPW == 8 && MI * NI == 64, "eight DMA instructions per half K step");
+  static_assert(kIPW == 8 && MI * NI == (HALF ? 32 : 64), "eight W DMA instructions per half K step");
 
   // The accumulators pass through these statements (which the compiler cannot
   // move them across): the first gives the zeroing its wait states before any
@@ -454,14 +508,14 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   // ---- prologue: A0 W0 A1 W1 in flight, wait for step 0
   fence_acc(false);
 #pragma unroll
-  for (int j = 0; j < kIPW; ++j) dma_a1(0, j);
+  for (int j = 0; j < kIPWA; ++j) dma_a1(0, j);
 #pragma unroll
   for (int j = 0; j < kIPW; ++j) dma_w1(0, j);
 #pragma unroll
-  for (int j = 0; j < kIPW; ++j) dma_a1(1, j);
+  for (int j = 0; j < kIPWA; ++j) dma_a1(1, j);
 #pragma unroll
   for (int j = 0; j < kIPW; ++j) dma_w1(1, j);
-  wait_vmcnt<2 * kIPW>();
+  wait_vmcnt<kIPWA + kIPW>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int r = 0; r < MI + NI; ++r) read_frag(0, 0, 0, r);
@@ -477,7 +531,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
     half(0, kt, 1, true, kt + 2, false);
-    wait_vmcnt<kIPW>();  // A_{kt+1}, W_{kt+1} landed; A_{kt+2} may be in flight
+    wait_vmcnt<kIPWA>();  // A_{kt+1}, W_{kt+1} landed; A_{kt+2} may be in flight
     wait_lgkm0();        // this wave's reads of step kt are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -631,6 +685,15 @@ __global__ void __launch_bounds__(64 * kWaves, 1)
   gemm_body<EPI, 0, 1>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea);
 }
 
+// The last, partial wave of tiles as half tiles (see gemm_body).
+template <int EPI>
+__global__ void __launch_bounds__(64 * kWaves, 1)
+    k_gemm_bf16_half(const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, void* __restrict__ Cv, int M,
+                     int N, int K, EpiArgs ea, int pid_base) {
+  gemm_body<EPI, 0, 0, 1>(reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(W), Cv, M, N, K, ea,
+                          pid_base);
+}
+
 template <int EPI>
 __global__ void __launch_bounds__(64 * kWaves, 1)
     k_gemm_i8(const int8_t* __restrict__ A, const int8_t* __restrict__ W, void* __restrict__ Cv, int M, int N, int K,
@@ -707,6 +770,21 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, c
 
 // ---------------------------------------------------------------- launchers
 
+// Compute units of the current device (cached per device; 0 on error).
+static int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Shapes the q/k/v epilogue assumes: N = 3 heads 128 with an even head count
 // (a 256-column tile holds two heads of one of q, k, v), M whole batch items,
 // stride a multiple of 64 not below S, at most 64 rotation pairs.
@@ -740,6 +818,20 @@ hipError_t launch_gemm<bf16_t>(int epi, const bf16_t* A, const bf16_t* W, void* 
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+  }
+  if (epi == kEpiGatedResid) {
+    // One workgroup per CU: when the tiles end in a wave that fills at most
+    // half the CUs, the whole waves run as usual and the rest as half tiles
+    // (one wave of at most all CUs, each with half the work).
+    const int cus = device_cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int whole = tiles / cus * cus, rest = tiles - whole;
+    if (whole > 0 && rest > 0 && 2 * rest <= cus) {
+      k_gemm_bf16<kEpiGatedResid><<<dim3((unsigned)whole), 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea);
+      k_gemm_bf16_half<kEpiGatedResid><<<dim3((unsigned)(2 * rest)), 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea,
+                                                                                          whole);
+      return hipGetLastError();
+    }
   }
   switch (epi) {
     case kEpiStore: k_gemm_bf16<kEpiStore><<<grid, 64 * kWaves, 0, st>>>(A, W, C, M, N, K, ea); break;

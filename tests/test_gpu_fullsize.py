@@ -226,3 +226,30 @@ def test_row_permutation_full_size():
     assert torch.equal(b[:, pad], xp[:, pad])
     print(f"permutation: vs original rel {r[0]:.2e} max {r[1]:.2e}; vs oracle rel {r2[0]:.2e} max {r2[1]:.2e}",
           flush=True)
+
+
+def test_half_tile_tail_bit_exact_full_size():
+    # The output and down projections (N = 5376, 21 column tiles) run their
+    # last, partial wave of 256 x 256 tiles as 128-row half tiles when it
+    # fills at most half the CUs. The padded four-block layout at seed 1
+    # (25060 rows: 2058 tiles, 10 past the last whole wave of 256) takes that
+    # path, the same rows cut before their padding (24576 rows: 224 past) do
+    # not; every output is the same MFMA sequence over K either way, so the
+    # real rows must agree bit for bit (first block of the chain).
+    print("full-size half-tile tail vs whole tiles", flush=True)
+    wl = workload("chain4x24k", 1)
+    L = wl.layout
+    n = int((L.token_tags != -1).sum())
+    assert np.all(L.token_tags[:n] != -1) and np.all(L.token_tags[n:] == -1)
+    tiles = lambda rows: -(-rows // 256) * (5376 // 256)
+    assert 0 < tiles(L.seq_len) % 256 <= 128 and tiles(n) % 256 > 128
+    cfg, lay, blocks, x = dv.upload(wl)
+    a = m.block_forward(cfg, lay, blocks[:1], x)
+    lt = m.DeviceLayout(1, L.token_tags[:n], L.timestep_indices[:n], L.position_ids[:n], L.video_indices,
+                        L.audio_indices, L.text_indices)
+    b = m.block_forward(cfg, lt, blocks[:1], x[:, :n].contiguous(), flags=m.VALIDATE)
+    torch.cuda.synchronize()
+    same = torch.equal(a[:, :n], b)
+    r = rel_l2(to_np64(b[0]), to_np64(a[0, :n]))
+    print(f"half-tile tail: bit-exact {same} rel {r:.2e}", flush=True)
+    assert same
