@@ -516,8 +516,12 @@ __global__ void __launch_bounds__(kNW * 64, 1)
   // MFMA in that order), so the eight probabilities of a lane are exactly the
   // B operand (keys 32 kc + 8 g4 .. +7) of the O^T MFMA.
   typedef floatx4 Half[2][2];
+  // the wave's document flags as wave-uniform integers, so that the test of
+  // a tile is scalar work
+  const int only_real = __builtin_amdgcn_readfirstlane((int)(wq_real && !wq_pad));
+  const int only_pad = __builtin_amdgcn_readfirstlane((int)(wq_pad && !wq_real));
   auto is_clean = [&](const Ahead& a) {
-    return (wq_real && !wq_pad && a.mr == ~0ull) || (wq_pad && !wq_real && a.mp == ~0ull);
+    return (only_real && a.mr == ~0ull) || (only_pad && a.mp == ~0ull);
   };
   auto mask_half = [&](Half& sh, const Ahead& a, int kc) {
     if (is_clean(a)) return;
