@@ -410,18 +410,35 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   // 16-byte chunk 4 h + (lane >> 4) of half h of the K step
   const int fr_row = lane & 15, fr_q = lane >> 4, fr_sw = gemm_swz(fr_row);
   bf16x8 fa[2][MI], fw[2][NI];
-  // fragment r (0..15) of half h of K step k into register set `set`, in the
-  // order the MFMAs first use them: a0 w0..w7 a1..a7
-  auto read_frag = [&](int k, int h, int set, int r) {
+  // A half step's reads come from two lane addresses, the A and the W slot of
+  // its K step plus the lane's row and chunk, formed once before the half's
+  // MFMA stream (and pinned there), so that the reads inside the stream only
+  // add immediates: VALU work between the MFMAs slows them (address
+  // arithmetic per read cost ~3 % on every projection).
+  typedef __attribute__((address_space(3))) const bf16x8* lds_frag_t;
+  typedef __attribute__((address_space(3))) const uint8_t* lds_u8_t;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8_t)lds;
+  uint32_t la[2], lw[2];  // the lane's byte offset in an A / W slot, half h
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
     const int chunk = ((4 * h + fr_q) ^ fr_sw) << 4;
+    la[h] = (uint32_t)((wm * WTM + fr_row) * kRowBytes + chunk);
+    lw[h] = (uint32_t)((wn * WTN + fr_row) * kRowBytes + chunk);
+  }
+  auto frag_base = [&](int k, int h, uint32_t& aA, uint32_t& aW) {
+    aA = lds0 + (uint32_t)(((2 * k) % kSlots) * kSlotBytes) + la[h];
+    aW = lds0 + (uint32_t)(((2 * k + 1) % kSlots) * kSlotBytes) + lw[h];
+    asm volatile("" : "+v"(aA), "+v"(aW));
+  };
+  // fragment r (0..MI + NI - 1) of the half step whose addresses are aA, aW
+  // into register set `set`, in the order the MFMAs first use them:
+  // a0 w0..w7 a1..a(MI-1)
+  auto read_frag = [&](uint32_t aA, uint32_t aW, int set, int r) {
     if (r >= 1 && r <= NI) {
-      const uint8_t* Ws = slot_ptr((2 * k + 1) % kSlots);
-      const int ni = r - 1;
-      fw[set][ni] = *reinterpret_cast<const bf16x8*>(Ws + (wn * WTN + ni * 16 + fr_row) * kRowBytes + chunk);
+      fw[set][r - 1] = *(lds_frag_t)(uintptr_t)(aW + (uint32_t)((r - 1) * 16 * kRowBytes));
     } else {
-      const uint8_t* As = slot_ptr((2 * k) % kSlots);
       const int mi = r == 0 ? 0 : r - NI;
-      fa[set][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * WTM + mi * 16 + fr_row) * kRowBytes + chunk);
+      fa[set][mi] = *(lds_frag_t)(uintptr_t)(aA + (uint32_t)(mi * 16 * kRowBytes));
     }
   };
   // C[m][n] for m = row (lane & 15) of block mi, n = 4 (lane >> 4) + e of
@@ -471,10 +488,12 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   // waves reaches the address unit evenly.
   auto half = [&](int set, int nk, int nh, bool reads, int dk, bool dw) {
     constexpr int NM = MI * NI;
+    uint32_t aA = 0, aW = 0;
+    if (reads) frag_base(nk, nh, aA, aW);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma1(set, i);
-      if (reads && read_at(i) >= 0) read_frag(nk, nh, set ^ 1, read_at(i));
+      if (reads && read_at(i) >= 0) read_frag(aA, aW, set ^ 1, read_at(i));
       if (dk >= 0) {
         if (dw) {
           if (i % (NM / kIPW) == NM / kIPW - 1) dma_w1(dk, i / (NM / kIPW));
@@ -517,8 +536,12 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   for (int j = 0; j < kIPW; ++j) dma_w1(1, j);
   wait_vmcnt<kIPWA + kIPW>();
   __builtin_amdgcn_s_barrier();
+  {
+    uint32_t aA, aW;
+    frag_base(0, 0, aA, aW);
 #pragma unroll
-  for (int r = 0; r < MI + NI; ++r) read_frag(0, 0, 0, r);
+    for (int r = 0; r < MI + NI; ++r) read_frag(aA, aW, 0, r);
+  }
 
   // K step kt: its first half loads A_{kt+2} (the slot of W_{kt-1}) and reads
   // the second half's fragments; every wave then waits for its own DMA of
