@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(256) k_sinusoid(Pair<const float*> tp, Pair<fl
 // With k2 > 0 (XF only) the last k2 columns of the input come from x2 in
 // its own fragment order ([Mpad, k2]) and x holds the first K - k2 columns.
 // scale multiplies the product before the bias and the activation.
-template <int IN, int XF, int OF, int MB>
+template <int IN, int XF, int OF, int MB, int S2>
 __global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<const float*> wp,
                                                     Pair<const float*> bp, Pair<float*> op, int mchunks, int M,
                                                     int N, int K, int kchunk, int ng, int act, Pair<const float*> x2p,
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(256) k_skinny_f32(Pair<const float*> xp, Pair<
     for (int mb = 0; mb < MB; ++mb) {
       if constexpr (XF) {
         const int ks = k - 4 * q;  // first column of the step
-        if (ks >= K1) {
+        if (S2 && ks >= K1) {  // S2: the input has a second part (the steps from K1 on)
           const long unit = ((long)(m0 / 16 + mb) * (k2 / 16) + (ks - K1) / 16) * 64 + lane;
           xv[slot][mb] = *reinterpret_cast<const floatx4*>(x2 + unit * 4);
         } else {
@@ -391,15 +391,29 @@ static void skinny_launch(dim3 grid, int mb, const SkinnyArgs& g, int mchunks, i
   const Pair<const float*> xp{{g.x[0], g.x[1]}}, wp{{g.w[0], g.w[1]}}, bp{{g.bias[0], g.bias[1]}};
   const Pair<const float*> x2p{{g.x2[0], g.x2[1]}};
   const Pair<float*> op{{g.out[0], g.out[1]}};
-  if (mb == 4)
-    k_skinny_f32<IN, XF, OF, 4><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p, g.k2,
-                                                      g.scale);
-  else if (mb == 2)
-    k_skinny_f32<IN, XF, OF, 2><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p, g.k2,
-                                                      g.scale);
-  else
-    k_skinny_f32<IN, XF, OF, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p, g.k2,
-                                                      g.scale);
+  // the two-part input gets its own instantiation: the test of the part
+  // inside the load loop would otherwise sit among the MFMAs of every launch
+  if (g.k2 > 0) {
+    if (mb == 4)
+      k_skinny_f32<IN, XF, OF, 4, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p,
+                                                           g.k2, g.scale);
+    else if (mb == 2)
+      k_skinny_f32<IN, XF, OF, 2, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p,
+                                                           g.k2, g.scale);
+    else
+      k_skinny_f32<IN, XF, OF, 1, 1><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p,
+                                                           g.k2, g.scale);
+  } else {
+    if (mb == 4)
+      k_skinny_f32<IN, XF, OF, 4, 0><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p,
+                                                           g.k2, g.scale);
+    else if (mb == 2)
+      k_skinny_f32<IN, XF, OF, 2, 0><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p,
+                                                           g.k2, g.scale);
+    else
+      k_skinny_f32<IN, XF, OF, 1, 0><<<grid, 256, 0, st>>>(xp, wp, bp, op, mchunks, M, N, K, kchunk, ng, act, x2p,
+                                                           g.k2, g.scale);
+  }
 }
 
 hipError_t launch_skinny_f32(int mode, const SkinnyArgs& g, int chains, int M, int N, int K, int splits, int ng,
