@@ -22,8 +22,10 @@ oracle and the input generator:
 plus properties that hold at any size on every row: padding rows leave the
 block bit-unchanged, the mask-free flag equals the masked path when no
 padding row is present, padding contents never reach real rows, the real
-rows of a padded sequence equal the sequence cut before its padding, and a
-permutation of the rows permutes the outputs (page
+rows of a padded sequence equal the sequence cut before its padding (also
+when only one of the two runs its projections' last wave as half tiles), a
+second batch item changes nothing in the first, and a permutation of the
+rows permutes the outputs (page
 "MiniMaxH3Transformer3DModel", class description: full self-attention over
 the packed sequence, padding rows in their own document).
 
@@ -253,3 +255,25 @@ def test_half_tile_tail_bit_exact_full_size():
     r = rel_l2(to_np64(b[0]), to_np64(a[0, :n]))
     print(f"half-tile tail: bit-exact {same} rel {r:.2e}", flush=True)
     assert same
+
+
+def test_batch_replication_full_size():
+    # the batch axis replicates the layout and each item is its own sequence
+    # (page "MiniMaxH3Transformer3DModel", class description): two items with
+    # the padded layout, one of them the single-item input and the other
+    # re-randomised, give the single-item output bit for bit on the first
+    print("full-size batch replication", flush=True)
+    wl = workload("padded16k")
+    cfg, lay, blocks, x = dv.upload(wl)
+    a = m.block_forward(cfg, lay, blocks, x)
+    lay2 = dv.layout_for(wl, batch=2)
+    x2 = torch.cat([x, (torch.randn_like(x, dtype=torch.float32) * 2).to(x.dtype)], dim=0).contiguous()
+    b = m.block_forward(cfg, lay2, blocks, x2, flags=m.VALIDATE)
+    torch.cuda.synchronize()
+    same = torch.equal(b[:1], a)
+    print(f"batch item 0 vs single: bit-exact {same}", flush=True)
+    assert same
+    # and the second item equals its own single-item run
+    c = m.block_forward(cfg, lay, blocks, x2[1:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(b[1:], c)
