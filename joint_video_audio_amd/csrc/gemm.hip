@@ -322,7 +322,9 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid & 1, wn = wid >> 1;
 
-  // ---- tile order: XCD-contiguous ranges, then groups of 8 M-tiles
+  // ---- tile order: XCD-contiguous ranges, then groups of 4 M-tiles (an
+  // XCD's 32 concurrent tiles are 4 M-tiles x 8 N-tiles; groups of 8 M-tiles
+  // ran the QKV projection 3 % slower, of 2 and 16 slower still)
   const int MT = (M + BM - 1) / BM, NTL = N / BN;
   const int bid = blockIdx.x;
   int pid, mh = 0;
@@ -336,7 +338,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
     const int q8 = G >> 3, r8 = G & 7;
     pid = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
   }
-  constexpr int GROUP_M = 8;
+  constexpr int GROUP_M = 4;
   const int npg = GROUP_M * NTL;
   const int g = pid / npg;
   const int first_m = g * GROUP_M;
