@@ -324,7 +324,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A, const u
 
   // ---- tile order: XCD-contiguous ranges, then groups of 4 M-tiles (an
   // XCD's 32 concurrent tiles are 4 M-tiles x 8 N-tiles; groups of 8 M-tiles
-  // ran the QKV projection 3 % slower, of 2 and 16 slower still)
+  // ran the QKV projection 3 % slower; groups of 2, 3, 6 and 16 were slower
+  // too)
   const int MT = (M + BM - 1) / BM, NTL = N / BN;
   const int bid = blockIdx.x;
   int pid, mh = 0;
