@@ -21,6 +21,10 @@
  *    float32); bfloat16 values are stored as IEEE bf16 bit patterns.
  *  - Every call returns an int status (minih3_status) and never aborts.
  *    Argument errors are found on the host before anything is enqueued.
+ *  - Sizes (batch, seq_len, M, N, K) are at least 1: an empty sequence or
+ *    matrix is the argument error MINIH3_E_ARG. Row counts of one modality
+ *    (num_video, num_audio, num_text, the Euler step's num_rows) may be 0:
+ *    that modality's part of the call is then skipped.
  *    Layout errors are found only under MINIH3_VALIDATE, which costs one
  *    stream synchronisation. Without it an invalid layout gives unspecified
  *    numbers, but every index the kernels use is clamped into range, so no

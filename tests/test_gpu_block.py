@@ -2,7 +2,8 @@
 
 minih3_block_forward is compared with the fp64 oracle on the tiny fp32
 workload and on small bf16 layouts that span several GEMM, attention and
-RoPE tiles with ragged tails, including the intermediate taps. Invariants
+RoPE tiles with ragged tails, including the intermediate taps, and on
+degenerate layouts (one modality, a one-row document, padding only). Invariants
 the model page states are checked bit-exactly where they do not change any
 reduction order.
 """
@@ -136,6 +137,22 @@ def test_fused_qk_epilogue_equals_the_separate_pass(pads, batch, heads, fd):
         assert not taps["q_rot"][:, :, S:].float().abs().sum().item()
         assert not taps["k_rot"][:, :, S:].float().abs().sum().item()
         assert not taps["v_t"][:, :, :, S:].float().abs().sum().item()
+
+
+@pytest.mark.parametrize("segs,grid,pads", [
+    ([("video", 150, (2, 5, 15))], (2, 5, 15), 0),  # one modality, no padding document
+    ([("text", 70)], (1, 1, 1), 30),                 # text rows and padding only
+    ([("audio", 1)], (1, 1, 1), 100),                # a single real row: a one-row document
+    ([], (1, 1, 1), 80),                             # padding rows only
+])
+def test_block_degenerate_layouts(segs, grid, pads):
+    print(f"degenerate layout {[sg[:2] for sg in segs]} pads={pads}", flush=True)
+    wl = synth.make_custom(dims_bf16(), segs, grid, pads, seed=5)
+    out = check_block(wl)
+    if not segs:
+        # every row is padding: the block leaves the sequence unchanged
+        x = dv.to_device(wl.x)
+        assert torch.equal(out, x)
 
 
 def test_block_invariants_bit_exact():

@@ -102,6 +102,28 @@ def test_embed_inputs_reports_invalid_layouts():
     assert ei.value.status == m.E_LAYOUT_INDEX
 
 
+@pytest.mark.parametrize("segs,grid", [
+    ([("text", 21), ("video", 70, (2, 5, 7))], (2, 5, 7)),  # no audio rows
+    ([("text", 9), ("audio", 45)], (4, 1, 1)),              # no video rows: the narrower head alone
+    ([("text", 30)], (1, 1, 1)),                            # neither head has rows
+])
+def test_edges_with_a_modality_absent(segs, grid):
+    print(f"edges without a modality {[sg[:2] for sg in segs]}", flush=True)
+    dims = synth.ModelDims(hidden=512, num_heads=4, ffn_dim=768, num_tvals=8, dtype="bf16")
+    L = synth.make_custom(dims, segs, grid, 5, seed=9).layout
+    e = synth.make_edges(dims, L, seed=10)
+    cfg, lay, x = run_embed(dims, L, e, 1, flags=m.VALIDATE)
+    check_embed(dims, L, e, x)
+    v, a = m.output_heads(cfg, lay, dv.edges_for(e), x, flags=m.VALIDATE)
+    torch.cuda.synchronize()
+    rv, ra = oe.output_heads(to_np64(x), L, e.gamma, e.beta, e.final_norm_eps, e.w_out, e.b_out, e.w_aout, e.b_aout)
+    assert tuple(v.shape) == rv.shape and tuple(a.shape) == ra.shape
+    if rv.size:
+        assert_f32(to_np64(v), rv, "video head")
+    if ra.size:
+        assert_f32(to_np64(a), ra, "audio head")
+
+
 def test_edges_full_clip_scale():
     print("edges full clip scale", flush=True)
     wl = synth.make_workload("clip32k", with_weights=False)

@@ -112,3 +112,33 @@ def test_edges_host_side_checks():
     no_w = m._Edges(96, 32, 1e-5, None, *([p] * 9))
     assert lib.minih3_output_heads(ctypes.byref(cfg), ctypes.byref(L), ctypes.byref(no_w), p, p, p, p, 1 << 30, 0,
                                    None) == m.E_ARG
+
+
+def test_empty_inputs_are_argument_errors():
+    # zero-size sequences and matrices are refused on the host, before any
+    # GPU work; a modality with no rows is not an error (the Euler step over
+    # zero rows returns at once)
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libminih3.so not built")
+    lib = m.lib()
+    cfg = dv.config_for(synth.workload_dims("clip32k"))
+    p = ctypes.c_void_p(16)
+    n = ctypes.c_size_t(0)
+    for b, s in ((1, 0), (0, 8), (1, -3)):
+        assert lib.minih3_workspace_bytes(ctypes.byref(cfg), b, s, ctypes.byref(n)) == m.E_ARG
+        assert lib.minih3_attention_workspace_bytes(ctypes.byref(cfg), b, s, ctypes.byref(n)) == m.E_ARG
+        L = m._Layout(b, s, p, p, p, None, 0, None, 0, None, 0)
+        bw = (m._BlockWeights * 1)(m._BlockWeights(*[p] * 7))
+        assert lib.minih3_block_forward(ctypes.byref(cfg), ctypes.byref(L), bw, 1, p, ctypes.c_void_p(32),
+                                        ctypes.c_void_p(64), 1 << 40, 0, None, None) == m.E_ARG
+        assert lib.minih3_attention_packed(ctypes.byref(cfg), ctypes.byref(L), p, p, p, ctypes.c_void_p(32), 0.0,
+                                           ctypes.c_void_p(64), 1 << 40, 0, None) == m.E_ARG
+        assert lib.minih3_adaln_modulate(ctypes.byref(cfg), ctypes.byref(L), p, p, 0, ctypes.c_void_p(32), 0,
+                                         None) == m.E_ARG
+        assert lib.minih3_qk_norm_rope(ctypes.byref(cfg), ctypes.byref(L), p, p, p, p, p, p, 64, None) == m.E_ARG
+    for M, N, K in ((0, 256, 64), (4, 0, 64), (4, 256, 0)):
+        assert lib.minih3_linear(0, p, p, ctypes.c_void_p(32), M, N, K, None) == m.E_ARG
+        assert lib.minih3_linear_w8a8(p, p, p, p, ctypes.c_void_p(32), M, N, K, None) == m.E_ARG
+    assert lib.minih3_rotate_quantize(0, p, 0, 256, p, p, None) == m.E_ARG
+    assert lib.minih3_euler_step(None, None, None, 1, 0, 32, None, None, 8, None, None, 8, None) == m.OK
+    assert lib.minih3_euler_step(None, None, None, 1, -1, 32, None, None, 8, None, None, 8, None) == m.E_ARG
