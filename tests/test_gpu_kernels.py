@@ -2,8 +2,11 @@
 
 Each kernel is called through the C ABI (ctypes binding) on seeded inputs
 that span several tiles with a ragged tail, and compared element by element
-with the oracle at the bar stated in tests/helpers.py.
+with the oracle at the bar stated in tests/helpers.py; at the largest sizes
+(a projection operand at its 4 GiB limit, a 131k-row attention) on sampled
+rows.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -44,6 +47,31 @@ def test_linear_bf16(M, N, K):
     assert_close(got, ref, "linear")
     # element-level: bf16 rounding of an fp32-accumulated value
     assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-3)
+
+
+def test_linear_bf16_operand_at_its_4gib_limit():
+    # the A operand one row short of 4 GiB, the largest bf16 projection
+    # operand the library takes (its DMA offsets are 32-bit); one row more is
+    # refused on the host before any GPU work
+    M, N, K = (1 << 18) - 1, 256, 8192
+    print(f"linear bf16 at the operand limit M={M} K={K}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, M, 1 << 15):  # drawn in slices: no 8 GiB fp32 temporary
+        r1 = min(M, r0 + (1 << 15))
+        a[r0:r1] = torch.randn(r1 - r0, K, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.05).to(torch.bfloat16)
+    assert M * K * 2 < (1 << 32) <= (M + 1) * K * 2
+    out = m.linear(a, w)
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 255, 256, 131071, 261887, 261888, M - 1])
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    ref = f64(a[sel]) @ f64(w).T
+    got = f64(out[sel])
+    assert_close(got, ref, "linear at the operand limit")
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-3)
+    p = ctypes.c_void_p(a.data_ptr())
+    assert m.lib().minih3_linear(0, p, p, p, M + 1, N, K, None) == m.E_UNSUPPORTED
 
 
 @pytest.mark.parametrize("M,N,K", [(70, 128, 48), (5, 64, 16)])
@@ -182,6 +210,31 @@ def test_attention_sharp(S, pads):
     ref = ob.attention_doc_masked(q[0, :, :S].transpose(1, 0, 2), k[0, :, :S].transpose(1, 0, 2),
                                   v[0, :, :S].transpose(1, 0, 2), ob.doc_ids(tags), 1 / math.sqrt(128))
     assert_close(to_np64(out[0]).reshape(S, H, 128), ref, "sharp attention")
+
+
+def test_attention_long_sequence_sampled_queries():
+    # four times the clip-scale sequence, a ragged end, padding rows at the
+    # end and two inside; queries sampled at tile edges, in both documents
+    S, H = 131072 + 37, 2
+    print(f"attention long sequence S={S}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    q, k, v = (torch.randn(1, S, H, 128, device="cuda", generator=g).mul(s).to(torch.bfloat16)
+               for s in (2.0, 1.0, 1.0))
+    tags = np.zeros(S, np.int32)
+    tags[-1000:] = -1
+    tags[[5, 70000]] = -1
+    cfg = dv.config_for(synth.ModelDims(hidden=256, num_heads=H, head_dim=128, ffn_dim=256, dtype="bf16"))
+    z = np.zeros(S, np.int32)
+    lay = m.DeviceLayout(1, tags, z, np.zeros((S, 3), np.int32), z[:0], z[:0], z[:0])
+    out = m.attention_packed(cfg, lay, q, k, v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 5, 63, 64, 4095, 70000, 131071, 131072, S - 1001, S - 1000, S - 1],
+                                     rng.integers(0, S, 21)]))
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    ref = ob.attention_doc_masked(f64(q[0]), f64(k[0]), f64(v[0]), ob.doc_ids(tags), 1 / math.sqrt(128), rows=rows)
+    got = f64(out[0, rows]).reshape(len(rows), H, 128)
+    assert_close(got, ref, "attention, long sequence")
 
 
 def test_attention_f32():
