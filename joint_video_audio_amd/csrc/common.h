@@ -80,7 +80,10 @@ __device__ __forceinline__ float row_sum(float v) {
 // 1 / sqrt(mean(v^2) + eps) and the weights g, then channel pair p (2p,
 // 2p + 1) is turned by the angle whose cosine and sine are cs[p], sn[p]
 // (1 and 0 for a pair that is not rotated). The fused multiply-adds are
-// explicit so that every kernel that calls this rounds alike.
+// explicit so that every kernel that calls this rounds alike. The
+// reciprocal square root is the hardware instruction on an argument held at
+// or above the smallest normal float (it is at least eps), which gives the
+// library rsqrtf's bits without its range scaling.
 template <int CPL, int LPR>
 __device__ __forceinline__ void qk_norm_rotate(float* v, const float* g, const float* cs, const float* sn,
                                                float eps) {
@@ -88,7 +91,7 @@ __device__ __forceinline__ void qk_norm_rotate(float* v, const float* g, const f
   float sq = 0.f;
 #pragma unroll
   for (int e = 0; e < CPL; ++e) sq = __builtin_fmaf(v[e], v[e], sq);
-  const float r = rsqrtf(row_sum<LPR>(sq) * (1.f / 128) + eps);
+  const float r = __builtin_amdgcn_rsqf(fmaxf(row_sum<LPR>(sq) * (1.f / 128) + eps, 0x1p-126f));
 #pragma unroll
   for (int p = 0; p < CPL / 2; ++p) {
     const float a = v[2 * p] * r * g[2 * p], b = v[2 * p + 1] * r * g[2 * p + 1];

@@ -120,6 +120,28 @@ __device__ __forceinline__ void qkv_tile_epilogue(const uint8_t* lds, int RB, in
     const int np = ea.rope_pairs;
     const bool norms = part == 1 && ea.kmax;
     const int b0 = m0 / S;  // batch item of the tile's first row
+    // batch item and position of the lane's rows gi + 16 k, found by stepping
+    // 16 rows at a time from the tile's first row (no division per row);
+    // positions stay in [0, S) also for rows past M, which are never stored
+    int bk[16], sk[16];
+    {
+      int b = b0, sp = m0 - b0 * S + gi;
+      if (sp >= S) {
+        b += sp / S;
+        sp %= S;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        bk[k] = b;
+        sk[k] = sp;
+        sp += 16;
+        if (sp >= S) {
+          b += sp / S;
+          sp %= S;
+        }
+      }
+    }
+    const long hstride = (long)stride * 128;  // elements between the rows of two heads
     float mx[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     constexpr int U = 4;
     struct Pre {
@@ -127,21 +149,20 @@ __device__ __forceinline__ void qkv_tile_epilogue(const uint8_t* lds, int RB, in
       uint64_t mk;
     };
     auto fetch = [&](int k, Pre& p) {
-      int m = m0 + gi + 16 * k;
-      m = m < M ? m : M - 1;  // rows past M load row M - 1 (never used)
-      const int s = m % S;
+      const int s = sk[k];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int j = cl * 4 + q;
         p.t[q] = j < np ? rope[(long)s * np + j] : make_float2(1.f, 0.f);
       }
-      p.mk = norms ? ea.masks[2 * (s / 64) + 1] : 0ull;
+      p.mk = norms ? ea.masks[2 * (s >> 6) + 1] : 0ull;
     };
     auto row = [&](int k, const Pre& p) {
       const int rr = gi + 16 * k, m = m0 + rr;
       if (m >= M) return;  // uniform over the 16 lanes of a row
-      const int b = m / S, s = m - b * S;
-      const int d = (int)((p.mk >> (s % 64)) & 1ull);
+      const int b = bk[k], s = sk[k];
+      const int d = (int)((p.mk >> (s & 63)) & 1ull);
+      bf16_t* orow = out + ((long)(b * H + h0) * stride + s) * 128 + cl * 8;
       float cs[4], sn[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -161,7 +182,7 @@ __device__ __forceinline__ void qkv_tile_epilogue(const uint8_t* lds, int RB, in
         u32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-        *reinterpret_cast<u32x4*>(out + (((long)b * H + h0 + hh) * stride + s) * 128 + cl * 8) = o;
+        *reinterpret_cast<u32x4*>(orow + hh * hstride) = o;
         if (norms) {
           float n2 = 0.f;
 #pragma unroll
@@ -171,9 +192,11 @@ __device__ __forceinline__ void qkv_tile_epilogue(const uint8_t* lds, int RB, in
             n2 = __builtin_fmaf(x1, x1, n2);
           }
           n2 = row_sum<16>(n2);
-          if (b == b0)
-            mx[hh][d] = fmaxf(mx[hh][d], n2);
-          else if (cl == 0)  // rows of a second batch item in the tile: straight to memory
+          if (b == b0) {
+            const float c0 = fmaxf(mx[hh][0], n2), c1 = fmaxf(mx[hh][1], n2);
+            mx[hh][0] = d ? mx[hh][0] : c0;
+            mx[hh][1] = d ? c1 : mx[hh][1];
+          } else if (cl == 0)  // rows of a second batch item in the tile: straight to memory
             atomicMax(reinterpret_cast<int*>(ea.kmax + 2 * ((long)b * H + h0 + hh) + d),
                       __float_as_int(sqrtf(n2)));
         }
