@@ -72,8 +72,11 @@ enum {
 
 /* Model dimensions (page "MiniMaxH3Transformer3DModel", Parameters). */
 typedef struct {
-  int32_t hidden;        /* residual width D (5376); multiple of 256            */
-  int32_t num_heads;     /* H (56)                                              */
+  int32_t hidden;        /* residual width D (5376); multiple of 256, at most
+                            8192 for bf16 and 4096 for fp32 blocks            */
+  int32_t num_heads;     /* H (56); even for the block entry points (the QKV
+                            width 3*H*hd is then a multiple of 256); any for
+                            the attention and q/k entry points               */
   int32_t head_dim;      /* hd; must be 128                                      */
   int32_t ffn_dim;       /* F, inner width of each SwiGLU half (14336); multiple of 128 */
   int32_t rope_freq_dim; /* rotary frequencies per axis (16); 6*rope_freq_dim <= head_dim */

@@ -142,3 +142,23 @@ def test_empty_inputs_are_argument_errors():
     assert lib.minih3_rotate_quantize(0, p, 0, 256, p, p, None) == m.E_ARG
     assert lib.minih3_euler_step(None, None, None, 1, 0, 32, None, None, 8, None, None, 8, None) == m.OK
     assert lib.minih3_euler_step(None, None, None, 1, -1, 32, None, None, 8, None, None, 8, None) == m.E_ARG
+
+
+def test_block_dims_outside_the_kernels_are_refused():
+    # an odd head count (QKV width 3 * H * 128 not a multiple of 256), a
+    # residual width beyond the AdaLN kernels' row, a head size other than 128
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libminih3.so not built")
+    lib = m.lib()
+    base = dv.config_for(synth.workload_dims("clip32k"))
+    n = ctypes.c_size_t(0)
+    assert lib.minih3_workspace_bytes(ctypes.byref(base), 1, 64, ctypes.byref(n)) == m.OK
+    for field, value in (("num_heads", 55), ("hidden", 8448), ("head_dim", 64), ("hidden", 5000), ("ffn_dim", 100)):
+        bad = m.Config(**{f: getattr(base, f) for f, _ in m.Config._fields_})
+        setattr(bad, field, value)
+        assert lib.minih3_workspace_bytes(ctypes.byref(bad), 1, 64, ctypes.byref(n)) == m.E_UNSUPPORTED, field
+    f32 = m.Config(**{f: getattr(base, f) for f, _ in m.Config._fields_})
+    f32.act_dtype = m.F32
+    assert lib.minih3_workspace_bytes(ctypes.byref(f32), 1, 64, ctypes.byref(n)) == m.E_UNSUPPORTED  # 5376 > 4096
+    f32.hidden = 4096
+    assert lib.minih3_workspace_bytes(ctypes.byref(f32), 1, 64, ctypes.byref(n)) == m.OK
