@@ -155,6 +155,19 @@ def test_block_degenerate_layouts(segs, grid, pads):
         assert torch.equal(out, x)
 
 
+@pytest.mark.parametrize("segs,pads,batch", [
+    ([("text", 3), ("audio", 2)], 2, 3),   # 7-row items, three in one 16-row group of the q/k epilogue
+    ([("text", 1)], 0, 4),                 # one row per item
+    ([("audio", 9), ("text", 6)], 0, 2),   # 15 rows
+    ([("text", 10), ("audio", 4)], 3, 5),  # 17 rows: items straddle the epilogue's 16-row steps
+])
+def test_block_short_sequences_in_a_batch(segs, pads, batch):
+    # several batch items inside one 256-row tile, shorter than the 16 rows
+    # a lane of the QKV epilogue steps over
+    print(f"short sequences {[sg[:2] for sg in segs]} pads={pads} batch={batch}", flush=True)
+    check_block(synth.make_custom(dims_bf16(), segs, (1, 1, 1), pads, seed=6, batch=batch))
+
+
 def test_block_invariants_bit_exact():
     print("block invariants", flush=True)
     dims = dims_bf16()
